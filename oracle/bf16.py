@@ -1,0 +1,45 @@
+"""bfloat16 storage rounding for the oracle (test infrastructure only).
+
+The pages never define a low-precision format; the C++/CUDA page (section 3.4,
+mixed precision) describes fp32 master weights with low-precision activations,
+and the workload names bfloat16.  The reading used here: a value stored as bf16
+is the bf16 number nearest to the exact value, ties to even (IEEE round to
+nearest even on an 8-bit significand), NaN stays NaN, values past the largest
+finite bf16 become infinity.
+
+The rounding is applied directly to the float64 value (no intermediate float32
+rounding), which is the mathematical definition of "nearest bf16 value".
+"""
+
+import numpy as np
+
+_BF16_MAX = float(np.float64((2.0 - 2.0 ** -7) * 2.0 ** 127))
+
+
+def round_bf16(x):
+    """Return float64 array holding the nearest-even bfloat16 value of ``x``.
+
+    bf16 keeps 8 significant bits (7 stored).  A float64 keeps 53, so the
+    45 low significand bits are rounded away: add half an ulp of the kept
+    part (minus one if the kept lsb is 0, which makes ties go to even) and
+    clear the low bits.  Exponents of bf16 and float32 agree; results below
+    the normal range of bf16 (|x| < 2**-126) are rounded on the bf16 subnormal
+    grid (step 2**-133) explicitly.
+    """
+    a = np.asarray(x, dtype=np.float64)
+    out = np.array(a, dtype=np.float64, copy=True)
+    finite = np.isfinite(out)
+    tiny = finite & (np.abs(out) < 2.0 ** -126)
+    normal = finite & ~tiny
+    if np.any(normal):
+        u = out[normal].view(np.uint64).copy()
+        lsb = (u >> np.uint64(45)) & np.uint64(1)
+        u = u + np.uint64((1 << 44) - 1) + lsb
+        u = u & ~np.uint64((1 << 45) - 1)
+        r = u.view(np.float64)
+        r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+        out[normal] = r
+    if np.any(tiny):
+        step = 2.0 ** -133
+        out[tiny] = np.round(out[tiny] / step) * step  # np.round is half-to-even
+    return out

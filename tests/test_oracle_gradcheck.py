@@ -1,0 +1,249 @@
+"""Central finite differences and an independent autograd cross-check of the oracle.
+
+The define-by-run page (section 4.2) prescribes the check: compare the
+hand-derived gradient with (f(x+h) - f(x-h)) / (2h) on small networks with fixed
+seeds.  Shapes here are tiny (B=2, T=5, C=8, NH=2, hs=4, F=32, V=13, L=2) and
+everything is float64.  A second, independent check runs PyTorch's CPU float64
+autograd on the same model (a library routine; test-only).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gpt2 as og
+from tests.conftest import GOLDEN, rel_l2
+from autograd_transformer_amd import synthetic as syn
+
+H = 1e-6
+
+
+def fd_check(f, arrays, analytic, n_coords=200, seed=0, tol=1e-6):
+    """Compare analytic gradients with central differences at random coordinates."""
+    rng = np.random.default_rng(seed)
+    for name, arr in arrays.items():
+        g = analytic[name]
+        flat = arr.reshape(-1)
+        idx = rng.choice(flat.size, size=min(n_coords, flat.size), replace=False)
+        num = np.empty(idx.size)
+        for i, j in enumerate(idx):
+            old = flat[j]
+            flat[j] = old + H
+            fp = f()
+            flat[j] = old - H
+            fm = f()
+            flat[j] = old
+            num[i] = (fp - fm) / (2 * H)
+        ana = g.reshape(-1)[idx]
+        scale = max(1.0, np.max(np.abs(ana)))
+        err = np.max(np.abs(num - ana)) / scale
+        assert err < tol, f"{name}: max err {err:.3e}"
+
+
+TINY = og.GPTConfig(n_layer=2, n_embd=8, n_head=2, vocab=13, block_size=6)
+TINY_SHAPE = syn.ModelShape(2, 8, 2, 13, 6)
+
+
+def tiny_model(seed=20):
+    # perturbed biases and LayerNorm parameters so every path carries signal
+    p = syn.gpt2_params(TINY_SHAPE, seed=seed, w_std=0.5, bias_std=0.3, ln_std=0.3)
+    p = {k: v.astype(np.float64) for k, v in p.items()}
+    tok, tgt = syn.gpt2_tokens(2, 5, 13, seed=seed)
+    return p, tok, tgt
+
+
+def test_gradcheck_procedure_from_the_page():
+    """The page's own set-up: 2-d input/output, 3 hidden units, eps = 1e-5,
+    agreement within 1e-5 (here on the tiny classifier's full chain)."""
+    with open(os.path.join(GOLDEN, "gradcheck.json")) as f:
+        gc = json.load(f)
+    rng = np.random.default_rng(21)
+    n_in, hid, n_out = gc["net"]["n_in"], gc["net"]["hidden"], gc["net"]["n_out"]
+    P = dict(x=rng.standard_normal((4, n_in)), W1=rng.standard_normal((n_in, hid)),
+             b1=rng.standard_normal(hid), W2=rng.standard_normal((hid, n_out)),
+             b2=rng.standard_normal(n_out))
+    y = np.array([0, 1, 1, 0])
+    _, grads, _, _ = og.mlp_step(P["x"], P["W1"], P["b1"], P["W2"], P["b2"], y)
+
+    def f():
+        return og.mlp_step(P["x"], P["W1"], P["b1"], P["W2"], P["b2"], y)[0]
+    eps = gc["eps"]
+    for name in ("W1", "b1", "W2", "b2"):
+        flat = P[name].reshape(-1)
+        for j in range(flat.size):
+            old = flat[j]
+            flat[j] = old + eps
+            fp = f()
+            flat[j] = old - eps
+            fm = f()
+            flat[j] = old
+            assert abs((fp - fm) / (2 * eps) - grads[name].reshape(-1)[j]) < gc["tolerance"]
+
+
+def test_gradcheck_layernorm():
+    rng = np.random.default_rng(22)
+    A = dict(x=rng.standard_normal((3, 7)) * 2, g=rng.standard_normal(7), b=rng.standard_normal(7))
+    r = rng.standard_normal((3, 7))
+
+    def f():
+        return float((oracle.layernorm_fwd(A["x"], A["g"], A["b"])[0] * r).sum())
+    _, mean, rstd = oracle.layernorm_fwd(A["x"], A["g"], A["b"])
+    dx, dg, db = oracle.layernorm_bwd(A["x"], mean, rstd, A["g"], r)
+    fd_check(f, A, dict(x=dx, g=dg, b=db))
+
+
+def test_gradcheck_gelu():
+    rng = np.random.default_rng(23)
+    A = dict(x=np.concatenate([rng.standard_normal(50) * 3, [0.0, 1e-3, -1e-3]]))
+    r = rng.standard_normal(A["x"].size)
+
+    def f():
+        return float((oracle.gelu_fwd(A["x"]) * r).sum())
+    fd_check(f, A, dict(x=oracle.gelu_bwd(A["x"], r)))
+
+
+def test_gradcheck_attention():
+    rng = np.random.default_rng(24)
+    B, T, NH, hs = 2, 6, 2, 3
+    A = dict(qkv=rng.standard_normal((B, T, 3 * NH * hs)))
+    r = rng.standard_normal((B, T, NH * hs))
+
+    def f():
+        return float((oracle.attention_fwd(A["qkv"], NH)[0] * r).sum())
+    fd_check(f, A, dict(qkv=oracle.attention_bwd(A["qkv"], r, NH)))
+
+
+def test_gradcheck_lmhead_ce():
+    rng = np.random.default_rng(25)
+    A = dict(h=rng.standard_normal((6, 5)), w=rng.standard_normal((11, 5)))
+    y = rng.integers(0, 11, 6)
+
+    def f():
+        return oracle.lmhead_ce_fwdbwd(A["h"], A["w"], y)[0]
+    _, dh, dw, _ = oracle.lmhead_ce_fwdbwd(A["h"], A["w"], y)
+    fd_check(f, A, dict(h=dh, w=dw))
+
+
+def test_gradcheck_block():
+    rng = np.random.default_rng(26)
+    B, T, C, NH = 2, 5, 8, 2
+    w = syn.block_inputs(seed=26, B=B, T=T, C=C, n_head=NH, w_std=0.5, bias_std=0.3, ln_std=0.3)["w"]
+    w = {k: v.astype(np.float64) for k, v in w.items()}
+    A = dict(x=rng.standard_normal((B, T, C)), **w)
+    r = rng.standard_normal((B, T, C))
+    layer = {k: A[k] for k in og.LAYER_PARAMS}
+
+    def f():
+        return float((og.block_fwd(A["x"], layer, NH)[0] * r).sum())
+    _, cache = og.block_fwd(A["x"], layer, NH)
+    dx, gr = og.block_bwd(cache, layer, r, NH)
+    fd_check(f, A, dict(x=dx, **gr))
+
+
+def test_gradcheck_whole_model():
+    p, tok, tgt = tiny_model()
+    _, grads = og.model_fwd_bwd(p, tok, tgt, TINY)
+
+    def f():
+        return og.model_fwd_bwd(p, tok, tgt, TINY)[0]
+    fd_check(f, p, grads, n_coords=40)
+
+
+# ------------------------------------------------- PyTorch fp64 cross-check
+
+def _torch_model_loss(tp, tok, tgt, cfg):
+    import torch
+    F = torch.nn.functional
+    B, T = tok.shape
+    C, NH = cfg.n_embd, cfg.n_head
+    hs = C // NH
+    x = tp["wte"][tok] + tp["wpe"][:T][None]
+    mask = torch.triu(torch.ones(T, T, dtype=torch.bool), 1)
+    for l in range(cfg.n_layer):
+        P = lambda k: tp[f"h{l}.{k}"]  # noqa: E731
+        u = F.layer_norm(x, (C,), P("ln1_g"), P("ln1_b"), eps=cfg.ln_eps)
+        qkv = u @ P("w_qkv") + P("b_qkv")
+        q, k, v = qkv.split(C, dim=-1)
+        q = q.view(B, T, NH, hs).transpose(1, 2)
+        k = k.view(B, T, NH, hs).transpose(1, 2)
+        v = v.view(B, T, NH, hs).transpose(1, 2)
+        s = (q @ k.transpose(-1, -2)) / hs ** 0.5
+        s = s.masked_fill(mask, float("-inf"))
+        a = (torch.softmax(s, -1) @ v).transpose(1, 2).reshape(B, T, C)
+        x = x + a @ P("w_proj") + P("b_proj")
+        w2 = F.layer_norm(x, (C,), P("ln2_g"), P("ln2_b"), eps=cfg.ln_eps)
+        x = x + F.gelu(w2 @ P("w_fc") + P("b_fc"), approximate="tanh") @ P("w_fcp") + P("b_fcp")
+    f = F.layer_norm(x, (C,), tp["lnf_g"], tp["lnf_b"], eps=cfg.ln_eps)
+    z = f @ tp["wte"][:cfg.vocab].T
+    return F.cross_entropy(z.reshape(-1, cfg.vocab), tgt.reshape(-1))
+
+
+def test_model_matches_torch_autograd_fp64():
+    torch = pytest.importorskip("torch")
+    p, tok, tgt = tiny_model(seed=27)
+    loss, grads = og.model_fwd_bwd(p, tok, tgt, TINY)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    tl = _torch_model_loss(tp, torch.tensor(tok, dtype=torch.long),
+                           torch.tensor(tgt, dtype=torch.long), TINY)
+    tl.backward()
+    assert abs(loss - tl.item()) < 1e-12
+    for k in p:
+        assert rel_l2(grads[k], tp[k].grad.numpy()) < 1e-11, k
+
+
+def test_model_matches_torch_at_gpt2_width():
+    """One layer at GPT-2 width (C=768, 12 heads, F=3072), short sequence."""
+    torch = pytest.importorskip("torch")
+    cfg = og.GPTConfig(n_layer=1, n_embd=768, n_head=12, vocab=500, block_size=20)
+    shape = syn.ModelShape(1, 768, 12, 500, 20)
+    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=28, bias_std=0.02).items()}
+    tok, tgt = syn.gpt2_tokens(2, 20, 500, seed=28)
+    loss, grads = og.model_fwd_bwd(p, tok, tgt, cfg)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    tl = _torch_model_loss(tp, torch.tensor(tok, dtype=torch.long),
+                           torch.tensor(tgt, dtype=torch.long), cfg)
+    tl.backward()
+    assert abs(loss - tl.item()) < 1e-11
+    for k in p:
+        assert rel_l2(grads[k], tp[k].grad.numpy()) < 1e-10, k
+
+
+def test_train_step_matches_torch_adamw():
+    torch = pytest.importorskip("torch")
+    p, tok, tgt = tiny_model(seed=29)
+    m = {k: np.zeros_like(v) for k, v in p.items()}
+    v0 = {k: np.zeros_like(v) for k, v in p.items()}
+    _, _, newp, _, _ = og.train_step(p, m, v0, 1, tok, tgt, TINY)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    opt = torch.optim.AdamW(list(tp.values()), lr=3e-4, betas=(0.9, 0.95), eps=1e-8,
+                            weight_decay=0.1)
+    _torch_model_loss(tp, torch.tensor(tok, dtype=torch.long),
+                      torch.tensor(tgt, dtype=torch.long), TINY).backward()
+    opt.step()
+    for k in p:
+        # The key bias has an exactly-zero gradient (softmax ignores a constant
+        # added to every score of a row); its ~1e-17 rounding noise is
+        # amplified by g / (|g| + eps) at t = 1, so those entries get a looser
+        # absolute bound (lr * 1e-17 / 1e-8 * a few).
+        assert np.allclose(newp[k], tp[k].detach().numpy(), atol=1e-14, rtol=1e-12) or \
+            (k.endswith("b_qkv") and np.allclose(newp[k], tp[k].detach().numpy(), atol=3e-12)), k
+
+
+def test_mlp_step_matches_torch():
+    torch = pytest.importorskip("torch")
+    d = syn.mlp_inputs(seed=1)
+    P = {k: d[k].astype(np.float64) for k in ("W1", "b1", "W2", "b2")}
+    loss, grads, new, _ = og.mlp_step(d["x"], P["W1"], P["b1"], P["W2"], P["b2"], d["labels"])
+    tp = {k: torch.tensor(v, requires_grad=True) for k, v in P.items()}
+    x = torch.tensor(d["x"], dtype=torch.float64)
+    h = torch.nn.functional.gelu(x @ tp["W1"] + tp["b1"], approximate="tanh")
+    tl = torch.nn.functional.cross_entropy(h @ tp["W2"] + tp["b2"],
+                                           torch.tensor(d["labels"], dtype=torch.long))
+    tl.backward()
+    assert abs(loss - tl.item()) < 1e-13
+    for k in P:
+        assert np.allclose(grads[k], tp[k].grad.numpy(), atol=1e-14)
+        assert np.allclose(new[k], P[k] - 0.1 * tp[k].grad.numpy(), atol=1e-14)
