@@ -1,0 +1,105 @@
+"""ctypes declarations of the libtt C ABI (include/tt.h).
+
+Loading fails loudly when the library has not been built: there is no CPU or
+PyTorch fallback for any call.
+"""
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtt.so")
+
+vp = C.c_void_p
+i32 = C.c_int
+f32 = C.c_float
+sz = C.c_size_t
+
+
+class tt_block_cfg(C.Structure):
+    _fields_ = [("B", i32), ("T", i32), ("C", i32), ("NH", i32), ("F", i32),
+                ("mode", i32), ("ln_eps", f32)]
+
+
+_BLOCK_W = ["ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj",
+            "ln2_g", "ln2_b", "w_fc", "b_fc", "w_fcp", "b_fcp"]
+
+
+class tt_block_w(C.Structure):
+    _fields_ = [(n, vp) for n in _BLOCK_W]
+
+
+class tt_block_g(C.Structure):
+    _fields_ = [(n, vp) for n in _BLOCK_W]
+
+
+class tt_param(C.Structure):
+    _fields_ = [("w", vp), ("g", vp), ("m", vp), ("v", vp), ("w_lowp", vp),
+                ("n", sz), ("wd_mult", f32)]
+
+
+class tt_model_cfg(C.Structure):
+    _fields_ = [("L", i32), ("C", i32), ("NH", i32), ("F", i32), ("V", i32),
+                ("V_pad", i32), ("T_max", i32), ("B_max", i32), ("mode", i32),
+                ("ln_eps", f32)]
+
+
+P = C.POINTER
+SIGS = {
+    "tt_ctx_create": (i32, [i32, vp, sz, vp, P(vp)]),
+    "tt_ctx_destroy": (None, [vp]),
+    "tt_ctx_set_stream": (i32, [vp, vp]),
+    "tt_ctx_alloc": (i32, [vp, sz, sz, P(vp)]),
+    "tt_ctx_mark": (i32, [vp]),
+    "tt_ctx_reset": (i32, [vp]),
+    "tt_ctx_usage": (i32, [vp, P(sz), P(sz)]),
+    "tt_ctx_sync": (i32, [vp]),
+    "tt_strerror": (C.c_char_p, [i32]),
+    "tt_ctx_last_error": (C.c_char_p, [vp]),
+    "tt_linear_fwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]),
+    "tt_linear_bwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]),
+    "tt_layernorm_fwd": (i32, [vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
+    "tt_layernorm_bwd": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+    "tt_gelu_fwd": (i32, [vp, i32, sz, vp, vp]),
+    "tt_gelu_bwd": (i32, [vp, i32, sz, vp, vp, vp]),
+    "tt_attn_fwd": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp]),
+    "tt_attn_bwd": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+    "tt_ce_fwdbwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, f32]),
+    "tt_embed_fwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+    "tt_embed_bwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+    "tt_adamw_step": (i32, [vp, P(tt_param), i32, f32, f32, f32, f32, f32, i32]),
+    "tt_sgd_step": (i32, [vp, vp, vp, sz, f32]),
+    "tt_cast_bf16": (i32, [vp, sz, vp, vp]),
+    "tt_block_saved_create": (i32, [vp, P(tt_block_cfg), P(vp)]),
+    "tt_block_saved_destroy": (None, [vp]),
+    "tt_block_fwd": (i32, [vp, P(tt_block_cfg), P(tt_block_w), vp, vp, vp]),
+    "tt_block_bwd": (i32, [vp, P(tt_block_cfg), P(tt_block_w), vp, vp, vp, P(tt_block_g)]),
+    "tt_lmhead_ce_fwdbwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+    "tt_model_create": (i32, [vp, P(tt_model_cfg), P(vp)]),
+    "tt_model_destroy": (None, [vp]),
+    "tt_model_param_table": (i32, [vp, P(tt_param), P(i32)]),
+    "tt_model_num_params": (i32, [vp, P(sz), P(sz)]),
+    "tt_model_refresh_shadow": (i32, [vp]),
+    "tt_train_step": (i32, [vp, vp, i32, i32, vp, vp, f32, f32, f32, f32, f32, i32, vp, vp]),
+    "tt_model_fwd_bwd": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+    "tt_model_adamw": (i32, [vp, vp, f32, f32, f32, f32, f32, i32]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libtt.so once; raise if it is missing (build it first)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libtt.so not found at {LIB_PATH}: build it with "
+                "`python -m autograd_transformer_amd.build` (no fallback exists)")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

@@ -1,0 +1,644 @@
+// Host side of the C ABI: argument validation and the op schedule of the
+// block, the LM head and the whole training step.  Every step runs in the
+// HIP kernels of this library; this file only validates and enqueues.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "tt_internal.h"
+
+namespace {
+
+inline size_t esize(tt_mode m) { return m == TT_BF16 ? 2 : 4; }
+inline bool mode_ok(int m) { return m == TT_F32 || m == TT_BF16; }
+
+GemmArgs gemm_args() {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.split_k = 0;
+  return g;
+}
+
+// y[M,N] (+)= A[M,K] (k-major, lda) · B where B is W[K,N] row-major (ldb = N),
+// i.e. the forward of a linear layer.
+int linear_fwd_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X, int ldx,
+                    const void *W, const float *bias, int epi, void *out, int ldo, bool out_lowp,
+                    const float *resid, int ldr, void *aux, int ldaux) {
+  GemmArgs g = gemm_args();
+  g.A = X; g.lda = ldx; g.a_kmajor = true;
+  g.B = W; g.ldb = N; g.b_kmajor = false;
+  g.M = M; g.N = N; g.K = K;
+  g.epi = epi; g.out = out; g.ldo = ldo; g.out_bf16 = out_lowp;
+  g.bias = bias; g.resid = resid; g.ldr = ldr; g.aux = aux; g.ldx = ldaux;
+  return tt_gemm(ctx, mode, g);
+}
+
+// dX[M,K] = dY[M,N] · Wᵀ  (W [K,N]), with an epilogue.
+int linear_dx_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *dY, int ldy,
+                   const void *W, int epi, void *out, int ldo, bool out_lowp, void *aux,
+                   int ldaux) {
+  GemmArgs g = gemm_args();
+  g.A = dY; g.lda = ldy; g.a_kmajor = true;
+  g.B = W; g.ldb = N; g.b_kmajor = true;
+  g.M = M; g.N = K; g.K = N;
+  g.epi = epi; g.out = out; g.ldo = ldo; g.out_bf16 = out_lowp;
+  g.aux = aux; g.ldx = ldaux;
+  return tt_gemm(ctx, mode, g);
+}
+
+// dW[K,N] += Xᵀ · dY  (X [M,K] row-major with ldx, dY [M,N] with ldy).
+int linear_dw_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X, int ldx,
+                   const void *dY, int ldy, float *dW) {
+  GemmArgs g = gemm_args();
+  g.A = X; g.lda = ldx; g.a_kmajor = false;
+  g.B = dY; g.ldb = ldy; g.b_kmajor = false;
+  g.M = K; g.N = N; g.K = M;
+  g.epi = EPI_ACCUM; g.out = dW; g.ldo = N; g.out_bf16 = false;
+  return tt_gemm(ctx, mode, g);
+}
+
+// ------------------------------------------------------------ block pieces
+
+struct LayerBufs {
+  void *ln1; float *mean1, *rstd1;
+  void *qkv; void *att; float *lse;
+  float *x1;
+  void *ln2; float *mean2, *rstd2;
+  void *h; void *g;
+};
+
+struct BwdScratch {
+  float *dtmp;   // [N,C] f32
+  void *datt;    // [N,C] mode
+  void *dqkv;    // [N,3C] mode
+  void *dh;      // [N,F] mode
+  float *Dv;     // [B*NH*T]
+};
+
+int alloc_layer(tt_ctx *ctx, tt_mode mode, int N, int C, int F, int B, int NH, int T,
+                LayerBufs &s) {
+  const size_t es = esize(mode);
+  void *p;
+#define A_(field, bytes) TT_TRY(tt_arena_alloc(ctx, (bytes), &p)); s.field = (decltype(s.field))p;
+  A_(ln1, (size_t)N * C * es)
+  A_(mean1, (size_t)N * 4) A_(rstd1, (size_t)N * 4)
+  A_(qkv, (size_t)N * 3 * C * es)
+  A_(att, (size_t)N * C * es)
+  A_(lse, (size_t)B * NH * T * 4)
+  A_(x1, (size_t)N * C * 4)
+  A_(ln2, (size_t)N * C * es)
+  A_(mean2, (size_t)N * 4) A_(rstd2, (size_t)N * 4)
+  A_(h, (size_t)N * F * es)
+  A_(g, (size_t)N * F * es)
+#undef A_
+  return TT_OK;
+}
+
+int alloc_bwd_scratch(tt_ctx *ctx, tt_mode mode, int N, int C, int F, int B, int NH, int T,
+                      BwdScratch &s) {
+  const size_t es = esize(mode);
+  void *p;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * 4, &p)); s.dtmp = (float *)p;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * es, &p)); s.datt = p;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * 3 * C * es, &p)); s.dqkv = p;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * F * es, &p)); s.dh = p;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)B * NH * T * 4, &p)); s.Dv = (float *)p;
+  return TT_OK;
+}
+
+// Pre-LN block forward (tinytorch page §3 item 6).
+int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, float eps,
+              const tt_block_w &w, const float *x, float *y, const LayerBufs &s) {
+  const int N = B * T;
+  const bool lp = mode == TT_BF16;
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, eps, x, w.ln1_g, w.ln1_b, s.ln1, s.mean1, s.rstd1));
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, w.w_qkv, w.b_qkv, EPI_STORE, s.qkv,
+                         3 * C, lp, nullptr, 0, nullptr, 0));
+  TT_TRY(tt_attn_fwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse));
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, C, s.att, C, w.w_proj, w.b_proj, EPI_RESID, s.x1, C, false,
+                         x, C, nullptr, 0));
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, eps, s.x1, w.ln2_g, w.ln2_b, s.ln2, s.mean2, s.rstd2));
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, F, s.ln2, C, w.w_fc, w.b_fc, EPI_GELU, s.g, F, lp,
+                         nullptr, 0, s.h, F));
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, F, C, s.g, F, w.w_fcp, w.b_fcp, EPI_RESID, y, C, false,
+                         s.x1, C, nullptr, 0));
+  return TT_OK;
+}
+
+// Block backward, in place on the residual gradient R (fp32) and its GEMM
+// operand copy Rl (bf16 copy in TT_BF16, == R in TT_F32).  On entry R holds
+// dL/dy; on return it holds dL/dx.
+int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
+              const tt_block_w &w, const LayerBufs &s, const float *x, float *R, void *Rl,
+              const tt_block_g &gr, const BwdScratch &sc) {
+  const int N = B * T;
+  const bool lp = mode == TT_BF16;
+  bf16_t *Rb = lp ? (bf16_t *)Rl : nullptr;
+  // MLP down-projection: dh = (dy · W_fpᵀ) * gelu'(h); dW_fp += gᵀ dy; db_fp.
+  TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, Rl, C, w.w_fcp, EPI_GELU_BWD, sc.dh, F, lp, s.h, F));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, Rl, C, gr.w_fcp));
+  TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_fcp));
+  // MLP up-projection.
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, sc.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
+                        nullptr, 0));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, sc.dh, F, gr.w_fc));
+  TT_TRY(tt_colsum(ctx, lp, N, F, F, sc.dh, gr.b_fc));
+  // LN2 backward + residual: R = R + LN2_bwd(dtmp).
+  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R, Rb,
+                               gr.ln2_g, gr.ln2_b));
+  // Attention projection.
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, Rl, C, w.w_proj, EPI_STORE, sc.datt, C, lp, nullptr, 0));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, Rl, C, gr.w_proj));
+  TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_proj));
+  // Attention.
+  TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, sc.dqkv, sc.Dv));
+  // QKV projection.
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, 3 * C, sc.dqkv, 3 * C, w.w_qkv, EPI_STORE, sc.dtmp, C,
+                        false, nullptr, 0));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, sc.dqkv, 3 * C, gr.w_qkv));
+  TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, sc.dqkv, gr.b_qkv));
+  // LN1 backward + residual.
+  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R, Rb,
+                               gr.ln1_g, gr.ln1_b));
+  return TT_OK;
+}
+
+int check_block_cfg(tt_ctx *ctx, const tt_block_cfg *c) {
+  TT_REQUIRE(ctx, c != nullptr, "block: cfg is NULL");
+  TT_REQUIRE(ctx, mode_ok(c->mode), "block: bad mode");
+  TT_REQUIRE(ctx, c->B > 0 && c->T > 0 && c->C > 0 && c->NH > 0 && c->F > 0, "block: bad shape");
+  if (c->C % c->NH != 0 || c->C / c->NH != 64)
+    return tt_set_error(ctx, TT_EUNSUPPORTED, "block: head size must be 64 (C=%d NH=%d)", c->C, c->NH);
+  TT_REQUIRE(ctx, c->C % 8 == 0 && c->F % 8 == 0 && c->C <= 4096, "block: C, F must be multiples of 8, C <= 4096");
+  return TT_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ op level ABI
+
+extern "C" int tt_linear_fwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X,
+                             const void *W, const float *b, void *Y, int epilogue,
+                             const float *resid, void *preact) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "linear_fwd: bad mode");
+  TT_REQUIRE(ctx, M > 0 && K > 0 && N > 0, "linear_fwd: bad shape");
+  TT_REQUIRE(ctx, X && W && Y, "linear_fwd: NULL operand");
+  int epi;
+  switch (epilogue) {
+    case TT_EPI_NONE: epi = EPI_STORE; break;
+    case TT_EPI_GELU: epi = EPI_GELU; break;
+    case TT_EPI_RESIDUAL:
+      TT_REQUIRE(ctx, resid != nullptr, "linear_fwd: RESIDUAL needs resid");
+      epi = EPI_RESID;
+      break;
+    default: return tt_set_error(ctx, TT_EINVAL, "linear_fwd: bad epilogue %d", epilogue);
+  }
+  return linear_fwd_gemm(ctx, mode, M, K, N, X, K, W, b, epi, Y, N, mode == TT_BF16, resid, N,
+                         preact, N);
+}
+
+extern "C" int tt_linear_bwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X,
+                             const void *W, const void *dY, float *dX, float *dW, float *db,
+                             int accumulate_dX) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "linear_bwd: bad mode");
+  TT_REQUIRE(ctx, M > 0 && K > 0 && N > 0, "linear_bwd: bad shape");
+  TT_REQUIRE(ctx, dY != nullptr, "linear_bwd: dY is NULL");
+  TT_REQUIRE(ctx, !dX || W, "linear_bwd: dX needs W");
+  TT_REQUIRE(ctx, !dW || X, "linear_bwd: dW needs X");
+  if (dX)
+    TT_TRY(linear_dx_gemm(ctx, mode, M, K, N, dY, N, W, accumulate_dX ? EPI_STORE_ACC : EPI_STORE,
+                          dX, K, false, nullptr, 0));
+  if (dW) TT_TRY(linear_dw_gemm(ctx, mode, M, K, N, X, K, dY, N, dW));
+  if (db) TT_TRY(tt_colsum(ctx, mode == TT_BF16, M, N, N, dY, db));
+  return TT_OK;
+}
+
+extern "C" int tt_layernorm_fwd(tt_ctx *ctx, tt_mode mode, int N, int C, float eps,
+                                const float *x, const float *g, const float *b, void *y,
+                                float *mean, float *rstd) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "layernorm_fwd: bad mode");
+  TT_REQUIRE(ctx, tt_aligned16(x) && tt_aligned16(g) && tt_aligned16(b) && tt_aligned16(y),
+             "layernorm_fwd: alignment");
+  return tt_layernorm_fwd_impl(ctx, mode, N, C, eps, x, g, b, y, mean, rstd);
+}
+
+extern "C" int tt_layernorm_bwd(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                                const float *mean, const float *rstd, const float *g,
+                                const float *dy, float *dx, float *dg, float *db) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "layernorm_bwd: bad mode");
+  TT_REQUIRE(ctx, tt_aligned16(x) && tt_aligned16(dy) && tt_aligned16(dx) && tt_aligned16(g),
+             "layernorm_bwd: alignment");
+  return tt_layernorm_bwd_impl(ctx, mode, N, C, x, mean, rstd, g, dy, dx, dx, nullptr, dg, db);
+}
+
+extern "C" int tt_attn_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, int hs,
+                           const void *qkv, void *out, float *lse) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "attn_fwd: bad mode");
+  if (hs != 64) return tt_set_error(ctx, TT_EUNSUPPORTED, "attn_fwd: head size must be 64");
+  TT_REQUIRE(ctx, B > 0 && T > 0 && NH > 0, "attn_fwd: bad shape");
+  TT_REQUIRE(ctx, qkv && out && lse && tt_aligned16(qkv) && tt_aligned16(out), "attn_fwd: pointers");
+  return tt_attn_fwd_impl(ctx, mode, B, T, NH, qkv, out, lse);
+}
+
+extern "C" int tt_attn_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, int hs,
+                           const void *qkv, const void *out, const float *lse, const void *dout,
+                           void *dqkv) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "attn_bwd: bad mode");
+  if (hs != 64) return tt_set_error(ctx, TT_EUNSUPPORTED, "attn_bwd: head size must be 64");
+  TT_REQUIRE(ctx, B > 0 && T > 0 && NH > 0, "attn_bwd: bad shape");
+  TT_REQUIRE(ctx, qkv && out && lse && dout && dqkv, "attn_bwd: NULL pointer");
+  TT_REQUIRE(ctx, tt_aligned16(qkv) && tt_aligned16(out) && tt_aligned16(dout) && tt_aligned16(dqkv),
+             "attn_bwd: alignment");
+  tt_scratch_scope scope(ctx);
+  void *Dv;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)B * NH * T * 4, &Dv));
+  return tt_attn_bwd_impl(ctx, mode, B, T, NH, qkv, out, lse, dout, dqkv, (float *)Dv);
+}
+
+extern "C" int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
+                            const int32_t *targets, float *loss, float grad_scale) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "ce: bad mode");
+  TT_REQUIRE(ctx, N > 0 && V > 0 && ld >= V, "ce: bad shape");
+  tt_scratch_scope scope(ctx);
+  void *rows;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * 4, &rows));
+  return tt_ce_impl(ctx, mode, N, V, ld, logits, targets, (float *)rows, loss,
+                    grad_scale > 0.f ? grad_scale : 1.0f / (float)N);
+}
+
+// LM head + CE on an [N, ld] logits scratch buffer (ld >= V, ld % 8 == 0).
+static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld, const void *h,
+                          const void *wte, const int32_t *targets, float *loss, float *dh,
+                          float *dwte, void *logits, float *row_loss) {
+  const bool lp = mode == TT_BF16;
+  GemmArgs g = gemm_args();
+  // z = h · wteᵀ
+  g.A = h; g.lda = C; g.a_kmajor = true;
+  g.B = wte; g.ldb = C; g.b_kmajor = true;
+  g.M = N; g.N = V; g.K = C;
+  g.epi = EPI_STORE; g.out = logits; g.ldo = ld; g.out_bf16 = lp;
+  TT_TRY(tt_gemm(ctx, mode, g));
+  // loss and dz = (softmax - onehot)/N in place
+  TT_TRY(tt_ce_impl(ctx, mode, N, V, ld, logits, targets, row_loss, loss, 1.0f / (float)N));
+  // dh = dz · wte
+  g = gemm_args();
+  g.A = logits; g.lda = ld; g.a_kmajor = true;
+  g.B = wte; g.ldb = C; g.b_kmajor = false;
+  g.M = N; g.N = C; g.K = V;
+  g.epi = EPI_STORE; g.out = dh; g.ldo = C; g.out_bf16 = false;
+  TT_TRY(tt_gemm(ctx, mode, g));
+  // dwte += dzᵀ · h
+  g = gemm_args();
+  g.A = logits; g.lda = ld; g.a_kmajor = false;
+  g.B = h; g.ldb = C; g.b_kmajor = false;
+  g.M = V; g.N = C; g.K = N;
+  g.epi = EPI_ACCUM; g.out = dwte; g.ldo = C; g.out_bf16 = false;
+  return tt_gemm(ctx, mode, g);
+}
+
+extern "C" int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int V, const void *h,
+                                   const void *wte, const int32_t *targets, float *loss, float *dh,
+                                   float *dwte) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, mode_ok(mode), "lmhead_ce: bad mode");
+  TT_REQUIRE(ctx, N > 0 && C > 0 && V > 0 && C % 8 == 0, "lmhead_ce: bad shape");
+  TT_REQUIRE(ctx, h && wte && targets && loss && dh && dwte, "lmhead_ce: NULL pointer");
+  TT_REQUIRE(ctx, tt_aligned16(h) && tt_aligned16(wte), "lmhead_ce: alignment");
+  const int ld = (V + 63) / 64 * 64;
+  tt_scratch_scope scope(ctx);
+  void *logits, *rows;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * ld * esize(mode), &logits));
+  TT_TRY(tt_arena_alloc(ctx, (size_t)N * 4, &rows));
+  return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, targets, loss, dh, dwte, logits,
+                        (float *)rows);
+}
+
+// ------------------------------------------------------------ block ABI
+
+struct tt_block_saved {
+  uint32_t magic;
+  tt_block_cfg cfg;
+  LayerBufs s;
+  float *xin;  // copy of the block input (LN1's backward needs it)
+};
+
+extern "C" int tt_block_saved_create(tt_ctx *ctx, const tt_block_cfg *cfg, tt_block_saved **out) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_TRY(check_block_cfg(ctx, cfg));
+  TT_REQUIRE(ctx, out != nullptr, "block_saved_create: out is NULL");
+  tt_block_saved *sv = new tt_block_saved();
+  sv->magic = TT_SAVED_MAGIC;
+  sv->cfg = *cfg;
+  void *p = nullptr;
+  int rc = alloc_layer(ctx, cfg->mode, cfg->B * cfg->T, cfg->C, cfg->F, cfg->B, cfg->NH, cfg->T, sv->s);
+  if (rc == TT_OK) rc = tt_arena_alloc(ctx, (size_t)cfg->B * cfg->T * cfg->C * 4, &p);
+  if (rc != TT_OK) {
+    delete sv;
+    return rc;
+  }
+  sv->xin = (float *)p;
+  *out = sv;
+  return TT_OK;
+}
+
+static int check_block_w(tt_ctx *ctx, const tt_block_w *w) {
+  TT_REQUIRE(ctx, w != nullptr, "block: weights NULL");
+  TT_REQUIRE(ctx, w->ln1_g && w->ln1_b && w->w_qkv && w->b_qkv && w->w_proj && w->b_proj &&
+                      w->ln2_g && w->ln2_b && w->w_fc && w->b_fc && w->w_fcp && w->b_fcp,
+             "block: a weight pointer is NULL");
+  return TT_OK;
+}
+
+extern "C" int tt_block_fwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
+                            const float *x, float *y, tt_block_saved *saved) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_TRY(check_block_cfg(ctx, cfg));
+  TT_TRY(check_block_w(ctx, w));
+  TT_REQUIRE(ctx, x && y && saved, "block_fwd: NULL pointer");
+  if (saved->magic != TT_SAVED_MAGIC) return tt_set_error(ctx, TT_ESTALE, "block_fwd: stale saved");
+  TT_REQUIRE(ctx, saved->cfg.B == cfg->B && saved->cfg.T == cfg->T && saved->cfg.C == cfg->C &&
+                      saved->cfg.F == cfg->F && saved->cfg.mode == cfg->mode,
+             "block_fwd: saved buffers were made for another shape");
+  hipError_t e = hipMemcpyAsync(saved->xin, x, (size_t)cfg->B * cfg->T * cfg->C * 4,
+                                hipMemcpyDeviceToDevice, ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_fwd copy: %s", hipGetErrorString(e));
+  return layer_fwd(ctx, cfg->mode, cfg->B, cfg->T, cfg->C, cfg->NH, cfg->F, cfg->ln_eps, *w,
+                   saved->xin, y, saved->s);
+}
+
+extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
+                            const tt_block_saved *saved, const float *dy, float *dx,
+                            tt_block_g *g) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_TRY(check_block_cfg(ctx, cfg));
+  TT_TRY(check_block_w(ctx, w));
+  TT_REQUIRE(ctx, saved && dy && dx && g, "block_bwd: NULL pointer");
+  if (saved->magic != TT_SAVED_MAGIC) return tt_set_error(ctx, TT_ESTALE, "block_bwd: stale saved");
+  TT_REQUIRE(ctx, g->ln1_g && g->ln1_b && g->w_qkv && g->b_qkv && g->w_proj && g->b_proj &&
+                      g->ln2_g && g->ln2_b && g->w_fc && g->b_fc && g->w_fcp && g->b_fcp,
+             "block_bwd: a gradient pointer is NULL");
+  const tt_mode mode = cfg->mode;
+  const int N = cfg->B * cfg->T, C = cfg->C;
+  tt_scratch_scope scope(ctx);
+  BwdScratch sc;
+  TT_TRY(alloc_bwd_scratch(ctx, mode, N, C, cfg->F, cfg->B, cfg->NH, cfg->T, sc));
+  // R = dy (in place on dx from here on)
+  if (dx != dy) {
+    hipError_t e = hipMemcpyAsync(dx, dy, (size_t)N * C * 4, hipMemcpyDeviceToDevice, ctx->stream);
+    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_bwd copy: %s", hipGetErrorString(e));
+  }
+  void *Rl = dx;
+  if (mode == TT_BF16) {
+    TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * 2, &Rl));
+    TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl));
+  }
+  return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, Rl,
+                   *g, sc);
+}
+
+extern "C" void tt_block_saved_destroy(tt_block_saved *saved) {
+  if (!saved || saved->magic != TT_SAVED_MAGIC) return;
+  saved->magic = 0;
+  delete saved;
+}
+
+// ------------------------------------------------------------ whole model
+// Training loop of the tinytorch page (§3 item 7): forward, zero the
+// gradients, backward, Adam update — with the loss on every position and the
+// LM head tied to the token table.
+
+struct tt_model {
+  uint32_t magic;
+  tt_ctx *ctx;
+  tt_model_cfg cfg;
+  size_t n_slots = 0, n_params = 0;
+  std::vector<size_t> off, numel;
+  float *w = nullptr, *g = nullptr, *m = nullptr, *v = nullptr;
+  bf16_t *lowp = nullptr;
+  std::vector<LayerBufs> layers;
+  std::vector<float *> xs;
+  void *lnf = nullptr;
+  float *meanf = nullptr, *rstdf = nullptr;
+  void *logits = nullptr;
+  int ld = 0;
+  float *row_loss = nullptr;
+  float *R = nullptr;
+  void *Rl = nullptr;
+  BwdScratch sc;
+};
+
+namespace {
+
+enum { P_WTE = 0, P_WPE = 1, P_LAYER0 = 2 };
+constexpr int PER_LAYER = 12;
+inline int p_lnf_g(const tt_model *md) { return P_LAYER0 + PER_LAYER * md->cfg.L; }
+
+int check_model(tt_model *md) {
+  if (!md) return TT_EINVAL;
+  if (md->magic != TT_MODEL_MAGIC) return TT_ESTALE;
+  return TT_OK;
+}
+
+const void *mat(const tt_model *md, int idx) {
+  if (md->cfg.mode == TT_BF16) return md->lowp + md->off[idx];
+  return md->w + md->off[idx];
+}
+
+void layer_views(const tt_model *md, int l, tt_block_w &w, tt_block_g &gr) {
+  const int b = P_LAYER0 + PER_LAYER * l;
+  auto W = [&](int i) { return (const float *)(md->w + md->off[b + i]); };
+  auto G = [&](int i) { return md->g + md->off[b + i]; };
+  w.ln1_g = W(0); w.ln1_b = W(1); w.w_qkv = mat(md, b + 2); w.b_qkv = W(3);
+  w.w_proj = mat(md, b + 4); w.b_proj = W(5); w.ln2_g = W(6); w.ln2_b = W(7);
+  w.w_fc = mat(md, b + 8); w.b_fc = W(9); w.w_fcp = mat(md, b + 10); w.b_fcp = W(11);
+  gr.ln1_g = G(0); gr.ln1_b = G(1); gr.w_qkv = G(2); gr.b_qkv = G(3);
+  gr.w_proj = G(4); gr.b_proj = G(5); gr.ln2_g = G(6); gr.ln2_b = G(7);
+  gr.w_fc = G(8); gr.b_fc = G(9); gr.w_fcp = G(10); gr.b_fcp = G(11);
+}
+
+}  // namespace
+
+extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **out) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, cfg && out, "model_create: NULL argument");
+  *out = nullptr;
+  const tt_model_cfg c = *cfg;
+  TT_REQUIRE(ctx, mode_ok(c.mode), "model_create: bad mode");
+  TT_REQUIRE(ctx, c.L > 0 && c.C > 0 && c.NH > 0 && c.F > 0 && c.V > 0 && c.V_pad >= c.V &&
+                      c.T_max > 0 && c.B_max > 0,
+             "model_create: bad shape");
+  if (c.C / c.NH != 64 || c.C % c.NH)
+    return tt_set_error(ctx, TT_EUNSUPPORTED, "model_create: head size must be 64");
+  TT_REQUIRE(ctx, c.C % 8 == 0 && c.F % 8 == 0 && c.C <= 4096, "model_create: C, F multiples of 8");
+  tt_model *md = new tt_model();
+  md->magic = TT_MODEL_MAGIC;
+  md->ctx = ctx;
+  md->cfg = c;
+  auto add = [&](size_t n) {
+    md->off.push_back(md->n_slots);
+    md->numel.push_back(n);
+    md->n_params += n;
+    md->n_slots += (n + 63) / 64 * 64;  // 256-byte aligned tensors
+  };
+  const size_t C = c.C, F = c.F;
+  add((size_t)c.V_pad * C);
+  add((size_t)c.T_max * C);
+  for (int l = 0; l < c.L; ++l) {
+    add(C); add(C); add(C * 3 * C); add(3 * C); add(C * C); add(C);
+    add(C); add(C); add(C * F); add(F); add(F * C); add(C);
+  }
+  add(C); add(C);
+  const size_t save = ctx->offset;
+  int rc = TT_OK;
+  void *p;
+  auto alloc = [&](size_t bytes) -> void * {
+    if (rc != TT_OK) return nullptr;
+    rc = tt_arena_alloc(ctx, bytes, &p);
+    return rc == TT_OK ? p : nullptr;
+  };
+  md->w = (float *)alloc(md->n_slots * 4);
+  md->g = (float *)alloc(md->n_slots * 4);
+  md->m = (float *)alloc(md->n_slots * 4);
+  md->v = (float *)alloc(md->n_slots * 4);
+  if (c.mode == TT_BF16) md->lowp = (bf16_t *)alloc(md->n_slots * 2);
+  const int N = c.B_max * c.T_max;
+  const size_t es = esize(c.mode);
+  md->layers.resize(c.L);
+  for (int l = 0; l < c.L && rc == TT_OK; ++l)
+    rc = alloc_layer(ctx, c.mode, N, c.C, c.F, c.B_max, c.NH, c.T_max, md->layers[l]);
+  for (int l = 0; l <= c.L; ++l) md->xs.push_back((float *)alloc((size_t)N * C * 4));
+  md->lnf = alloc((size_t)N * C * es);
+  md->meanf = (float *)alloc((size_t)N * 4);
+  md->rstdf = (float *)alloc((size_t)N * 4);
+  md->ld = (c.V + 63) / 64 * 64;
+  md->logits = alloc((size_t)N * md->ld * es);
+  md->row_loss = (float *)alloc((size_t)N * 4);
+  md->R = (float *)alloc((size_t)N * C * 4);
+  md->Rl = c.mode == TT_BF16 ? alloc((size_t)N * C * 2) : (void *)md->R;
+  if (rc == TT_OK) rc = alloc_bwd_scratch(ctx, c.mode, N, c.C, c.F, c.B_max, c.NH, c.T_max, md->sc);
+  for (float *buf : {md->w, md->g, md->m, md->v})
+    if (rc == TT_OK) rc = tt_fill_f32(ctx, buf, md->n_slots, 0.f);
+  if (rc == TT_OK && md->lowp) rc = tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp);
+  if (rc != TT_OK) {
+    ctx->offset = save;
+    md->magic = 0;
+    delete md;
+    return rc;
+  }
+  *out = md;
+  return TT_OK;
+}
+
+extern "C" void tt_model_destroy(tt_model *model) {
+  if (!model || model->magic != TT_MODEL_MAGIC) return;
+  model->magic = 0;
+  delete model;
+}
+
+extern "C" int tt_model_param_table(tt_model *md, tt_param *params, int *count) {
+  TT_TRY(check_model(md));
+  if (!count) return TT_EINVAL;
+  const int n = (int)md->off.size();
+  if (params) {
+    if (*count < n) return TT_EINVAL;
+    for (int i = 0; i < n; ++i) {
+      params[i].w = md->w + md->off[i];
+      params[i].g = md->g + md->off[i];
+      params[i].m = md->m + md->off[i];
+      params[i].v = md->v + md->off[i];
+      params[i].w_lowp = md->lowp ? (void *)(md->lowp + md->off[i]) : nullptr;
+      params[i].n = md->numel[i];
+      params[i].wd_mult = 1.0f;
+    }
+  }
+  *count = n;
+  return TT_OK;
+}
+
+extern "C" int tt_model_num_params(const tt_model *md, size_t *n_slots, size_t *n_params) {
+  if (!md) return TT_EINVAL;
+  if (md->magic != TT_MODEL_MAGIC) return TT_ESTALE;
+  if (n_slots) *n_slots = md->n_slots;
+  if (n_params) *n_params = md->n_params;
+  return TT_OK;
+}
+
+extern "C" int tt_model_refresh_shadow(tt_model *md) {
+  TT_TRY(check_model(md));
+  tt_ctx *ctx = md->ctx;
+  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp));
+  TT_TRY(tt_fill_f32(ctx, md->m, md->n_slots, 0.f));
+  return tt_fill_f32(ctx, md->v, md->n_slots, 0.f);
+}
+
+extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const int32_t *tok,
+                                const int32_t *targets, float *loss) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "fwd_bwd: bad model handle");
+  TT_REQUIRE(ctx, md->ctx == ctx, "fwd_bwd: model belongs to another context");
+  const tt_model_cfg &c = md->cfg;
+  TT_REQUIRE(ctx, B > 0 && T > 0 && B <= c.B_max && T <= c.T_max, "fwd_bwd: B, T exceed capacity");
+  TT_REQUIRE(ctx, tok && targets && loss, "fwd_bwd: NULL pointer");
+  const tt_mode mode = c.mode;
+  const int N = B * T, C = c.C;
+  const bool lp = mode == TT_BF16;
+
+  TT_TRY(tt_fill_f32(ctx, md->g, md->n_slots, 0.f));
+  TT_TRY(tt_embed_fwd(ctx, B, T, C, c.V, tok, md->w + md->off[P_WTE], md->w + md->off[P_WPE],
+                      md->xs[0]));
+  tt_block_w w;
+  tt_block_g gr;
+  for (int l = 0; l < c.L; ++l) {
+    layer_views(md, l, w, gr);
+    TT_TRY(layer_fwd(ctx, mode, B, T, C, c.NH, c.F, c.ln_eps, w, md->xs[l], md->xs[l + 1],
+                     md->layers[l]));
+  }
+  const int lf = p_lnf_g(md);
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, c.ln_eps, md->xs[c.L], md->w + md->off[lf],
+                               md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
+  TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), targets, loss,
+                        md->sc.dtmp, md->g + md->off[P_WTE], md->logits, md->row_loss));
+  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
+                               md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
+                               lp ? (bf16_t *)md->Rl : nullptr, md->g + md->off[lf],
+                               md->g + md->off[lf + 1]));
+  for (int l = c.L - 1; l >= 0; --l) {
+    layer_views(md, l, w, gr);
+    TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, md->Rl, gr,
+                     md->sc));
+  }
+  return tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
+                      md->g + md->off[P_WPE]);
+}
+
+extern "C" int tt_model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, float beta2,
+                              float eps, float wd, int t) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "adamw: bad model handle");
+  TT_REQUIRE(ctx, t >= 1, "adamw: t is 1-based");
+  return tt_adamw_flat(ctx, md->w, md->g, md->m, md->v, md->lowp, md->n_slots, lr, beta1, beta2,
+                       eps, wd, t);
+}
+
+extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int32_t *tok,
+                             const int32_t *targets, float lr, float beta1, float beta2, float eps,
+                             float wd, int t, float *loss, int32_t *nonfinite) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, t >= 1, "train_step: t is 1-based");
+  TT_TRY(tt_model_fwd_bwd(ctx, md, B, T, tok, targets, loss));
+  if (nonfinite) {
+    TT_TRY(tt_fill_f32(ctx, (float *)nonfinite, 1, 0.f));
+    TT_TRY(tt_check_finite(ctx, loss, 1, nonfinite));
+  }
+  return tt_model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t);
+}

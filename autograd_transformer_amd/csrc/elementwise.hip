@@ -1,0 +1,274 @@
+// Elementwise / gather / scatter kernels: embeddings, AdamW, SGD, GELU,
+// fills and casts.  All bandwidth-bound: 16-byte vector accesses, grid-stride.
+#include "tt_internal.h"
+
+namespace {
+
+inline int grid_for(size_t n, int per_thread = 4) {
+  size_t blocks = (n + (size_t)256 * per_thread - 1) / ((size_t)256 * per_thread);
+  if (blocks > 65535u * 16u) blocks = 65535u * 16u;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+// Token + position embedding (tinytorch page §3 item 6):
+//   x0[b,t,:] = wte[tok[b,t],:] + wpe[t,:].
+// One wave per token row; out-of-range ids poison the row with NaN and raise
+// the context's range flag instead of reading outside the table.
+__global__ void __launch_bounds__(256) embed_fwd_kernel(int BT, int T, int C, int V,
+                                                        const int32_t *__restrict__ tok,
+                                                        const float *__restrict__ wte,
+                                                        const float *__restrict__ wpe,
+                                                        float *__restrict__ x0, int32_t *flags) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= BT) return;
+  const int t = row % T;
+  const int id = tok[row];
+  const bool ok = id >= 0 && id < V;
+  if (!ok && lane == 0) atomicOr(flags, 1);
+  const float4 *w = (const float4 *)(wte + (size_t)(ok ? id : 0) * C);
+  const float4 *p = (const float4 *)(wpe + (size_t)t * C);
+  float4 *o = (float4 *)(x0 + (size_t)row * C);
+  for (int c = lane; c < C / 4; c += 64) {
+    float4 a = w[c], b = p[c];
+    o[c] = ok ? make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w)
+              : make_float4(NAN, NAN, NAN, NAN);
+  }
+}
+
+// dwte[tok] += dx0 rows (float atomics: ids repeat, order is not fixed);
+// dwpe[t] += sum over the batch (one thread per (t, c), deterministic).
+__global__ void __launch_bounds__(256) embed_bwd_tok_kernel(int BT, int C, int V,
+                                                            const int32_t *__restrict__ tok,
+                                                            const float *__restrict__ dx0,
+                                                            float *__restrict__ dwte) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= BT) return;
+  const int id = tok[row];
+  if (id < 0 || id >= V) return;
+  const float *src = dx0 + (size_t)row * C;
+  float *dst = dwte + (size_t)id * C;
+  for (int c = lane; c < C; c += 64) unsafeAtomicAdd(&dst[c], src[c]);
+}
+
+__global__ void __launch_bounds__(256) embed_bwd_pos_kernel(int B, int T, int C,
+                                                            const float *__restrict__ dx0,
+                                                            float *__restrict__ dwpe) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * C) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) s += dx0[(size_t)b * T * C + i];
+  dwpe[i] += s;
+}
+
+// AdamW on a flat range (tinytorch page §3 item 7; Forge page "核心组件清单").
+// bc1 = 1 - beta1^t, bc2 = 1 - beta2^t computed on the host.
+__device__ __forceinline__ void adamw_one(float &w, float g, float &m, float &v, float lr,
+                                          float b1, float b2, float eps, float wd, float rbc1,
+                                          float rbc2) {
+  m = b1 * m + (1.0f - b1) * g;
+  v = b2 * v + (1.0f - b2) * g * g;
+  const float mh = m * rbc1, vh = v * rbc2;
+  w = w - lr * (mh / (sqrtf(vh) + eps) + wd * w);
+}
+
+__global__ void __launch_bounds__(256) adamw_kernel(size_t n, float *__restrict__ w,
+                                                    const float *__restrict__ g,
+                                                    float *__restrict__ m, float *__restrict__ v,
+                                                    bf16_t *__restrict__ wl, float lr, float b1,
+                                                    float b2, float eps, float wd, float rbc1,
+                                                    float rbc2) {
+  const size_t n4 = n / 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 W = ((float4 *)w)[i], G = ((const float4 *)g)[i];
+    float4 Mv = ((float4 *)m)[i], Vv = ((float4 *)v)[i];
+    adamw_one(W.x, G.x, Mv.x, Vv.x, lr, b1, b2, eps, wd, rbc1, rbc2);
+    adamw_one(W.y, G.y, Mv.y, Vv.y, lr, b1, b2, eps, wd, rbc1, rbc2);
+    adamw_one(W.z, G.z, Mv.z, Vv.z, lr, b1, b2, eps, wd, rbc1, rbc2);
+    adamw_one(W.w, G.w, Mv.w, Vv.w, lr, b1, b2, eps, wd, rbc1, rbc2);
+    ((float4 *)w)[i] = W;
+    ((float4 *)m)[i] = Mv;
+    ((float4 *)v)[i] = Vv;
+    if (wl) ((uint2 *)wl)[i] = make_uint2(pack_bf2(W.x, W.y), pack_bf2(W.z, W.w));
+  }
+  // tail
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    float W = w[i], Mv = m[i], Vv = v[i];
+    adamw_one(W, g[i], Mv, Vv, lr, b1, b2, eps, wd, rbc1, rbc2);
+    w[i] = W; m[i] = Mv; v[i] = Vv;
+    if (wl) wl[i] = f2bf(W);
+  }
+}
+
+__global__ void __launch_bounds__(256) sgd_kernel(size_t n, float *__restrict__ w,
+                                                  const float *__restrict__ g, float lr) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) w[i] -= lr * g[i];
+}
+
+__global__ void __launch_bounds__(256) fill_kernel(size_t n, float *__restrict__ p, float val) {
+  const size_t n4 = n / 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
+    ((float4 *)p)[i] = make_float4(val, val, val, val);
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = val;
+}
+
+__global__ void __launch_bounds__(256) cast_kernel(size_t n, const float *__restrict__ s,
+                                                   bf16_t *__restrict__ d) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) d[i] = f2bf(s[i]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) gelu_fwd_kernel(size_t n, const T *__restrict__ x,
+                                                       T *__restrict__ y) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    Elem<T>::store(y, i, gelu_f(Elem<T>::load(x, i)));
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) gelu_bwd_kernel(size_t n, const T *__restrict__ x,
+                                                       const T *__restrict__ dy,
+                                                       T *__restrict__ dx) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    Elem<T>::store(dx, i, Elem<T>::load(dy, i) * gelu_grad_f(Elem<T>::load(x, i)));
+}
+
+__global__ void __launch_bounds__(256) finite_kernel(size_t n, const float *__restrict__ x,
+                                                     int32_t *__restrict__ flag) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    bad |= !isfinite(x[i]);
+  if (bad) atomicOr(flag, 1);
+}
+
+}  // namespace
+
+int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v) {
+  if (n == 0) return TT_OK;
+  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, p, v);
+  return tt_check_launch(ctx, "fill");
+}
+
+int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst) {
+  if (n == 0) return TT_OK;
+  hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src, dst);
+  return tt_check_launch(ctx, "cast");
+}
+
+int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,
+                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t) {
+  if (n == 0) return TT_OK;
+  const float rbc1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)t)));
+  const float rbc2 = (float)(1.0 / (1.0 - pow((double)beta2, (double)t)));
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, w, g, m, v,
+                     w_lowp, lr, beta1, beta2, eps, wd, rbc1, rbc2);
+  return tt_check_launch(ctx, "adamw");
+}
+
+int tt_check_finite(tt_ctx *ctx, const float *x, size_t n, int32_t *flag) {
+  hipLaunchKernelGGL(finite_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, x, flag);
+  return tt_check_launch(ctx, "finite");
+}
+
+extern "C" int tt_embed_fwd(tt_ctx *ctx, int B, int T, int C, int V, const int32_t *tok,
+                            const float *wte, const float *wpe, float *x0) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, B >= 0 && T >= 0 && C > 0 && C % 4 == 0 && V > 0, "embed_fwd: bad shape");
+  TT_REQUIRE(ctx, tok && wte && wpe && x0, "embed_fwd: NULL pointer");
+  TT_REQUIRE(ctx, tt_aligned16(wte) && tt_aligned16(wpe) && tt_aligned16(x0), "embed_fwd: alignment");
+  const int BT = B * T;
+  if (BT == 0) return TT_OK;
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3((BT + 3) / 4), dim3(256), 0, ctx->stream, BT, T, C, V,
+                     tok, wte, wpe, x0, ctx->dev_flags);
+  return tt_check_launch(ctx, "embed_fwd");
+}
+
+extern "C" int tt_embed_bwd(tt_ctx *ctx, int B, int T, int C, int V, const int32_t *tok,
+                            const float *dx0, float *dwte, float *dwpe) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, B >= 0 && T >= 0 && C > 0 && V > 0, "embed_bwd: bad shape");
+  TT_REQUIRE(ctx, tok && dx0, "embed_bwd: NULL pointer");
+  const int BT = B * T;
+  if (BT == 0) return TT_OK;
+  if (dwte) {
+    hipLaunchKernelGGL(embed_bwd_tok_kernel, dim3((BT + 3) / 4), dim3(256), 0, ctx->stream, BT, C, V,
+                       tok, dx0, dwte);
+    TT_TRY(tt_check_launch(ctx, "embed_bwd_tok"));
+  }
+  if (dwpe) {
+    size_t n = (size_t)T * C;
+    hipLaunchKernelGGL(embed_bwd_pos_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       ctx->stream, B, T, C, dx0, dwpe);
+    TT_TRY(tt_check_launch(ctx, "embed_bwd_pos"));
+  }
+  return TT_OK;
+}
+
+extern "C" int tt_adamw_step(tt_ctx *ctx, const tt_param *params, int count, float lr,
+                             float beta1, float beta2, float eps, float wd, int t) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, params != nullptr && count >= 0, "adamw: bad table");
+  TT_REQUIRE(ctx, t >= 1, "adamw: t is 1-based");
+  for (int i = 0; i < count; ++i) {
+    const tt_param &p = params[i];
+    TT_REQUIRE(ctx, p.w && p.g && p.m && p.v, "adamw: NULL tensor %d", i);
+    TT_REQUIRE(ctx, tt_aligned16(p.w) && tt_aligned16(p.g) && tt_aligned16(p.m) &&
+                        tt_aligned16(p.v) && (!p.w_lowp || (((uintptr_t)p.w_lowp) & 7) == 0),
+               "adamw: tensor %d misaligned", i);
+  }
+  for (int i = 0; i < count; ++i) {
+    const tt_param &p = params[i];
+    TT_TRY(tt_adamw_flat(ctx, p.w, p.g, p.m, p.v, (bf16_t *)p.w_lowp, p.n, lr, beta1, beta2, eps,
+                         wd * p.wd_mult, t));
+  }
+  return TT_OK;
+}
+
+extern "C" int tt_sgd_step(tt_ctx *ctx, float *w, const float *g, size_t n, float lr) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, w && g, "sgd: NULL pointer");
+  if (n == 0) return TT_OK;
+  hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n, w, g, lr);
+  return tt_check_launch(ctx, "sgd");
+}
+
+extern "C" int tt_cast_bf16(tt_ctx *ctx, size_t n, const float *src, void *dst) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, src && dst, "cast: NULL pointer");
+  return tt_cast_f32_bf16(ctx, n, src, (bf16_t *)dst);
+}
+
+extern "C" int tt_gelu_fwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, void *y) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, x && y, "gelu_fwd: NULL pointer");
+  if (n == 0) return TT_OK;
+  if (mode == TT_BF16)
+    hipLaunchKernelGGL(gelu_fwd_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const bf16_t *)x, (bf16_t *)y);
+  else
+    hipLaunchKernelGGL(gelu_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const float *)x, (float *)y);
+  return tt_check_launch(ctx, "gelu_fwd");
+}
+
+extern "C" int tt_gelu_bwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, const void *dy,
+                           void *dx) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, x && dy && dx, "gelu_bwd: NULL pointer");
+  if (n == 0) return TT_OK;
+  if (mode == TT_BF16)
+    hipLaunchKernelGGL(gelu_bwd_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const bf16_t *)x, (const bf16_t *)dy, (bf16_t *)dx);
+  else
+    hipLaunchKernelGGL(gelu_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const float *)x, (const float *)dy, (float *)dx);
+  return tt_check_launch(ctx, "gelu_bwd");
+}

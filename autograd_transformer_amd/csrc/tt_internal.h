@@ -1,0 +1,174 @@
+// Internal definitions shared by the libtt HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "tt.h"
+
+// ---------------------------------------------------------------------------
+// Context
+// ---------------------------------------------------------------------------
+
+#define TT_CTX_MAGIC 0x54544358u    // "TTCX"
+#define TT_MODEL_MAGIC 0x54544d44u  // "TTMD"
+#define TT_SAVED_MAGIC 0x54545342u  // "TTSB"
+
+struct tt_ctx {
+  uint32_t magic;
+  int device;
+  hipStream_t stream;
+  char *arena;
+  size_t capacity;
+  size_t offset;
+  size_t mark;
+  bool owns_arena;
+  int32_t *dev_flags;  // [0]: range error seen in a kernel (token/target id)
+  std::string last_error;
+};
+
+// Validate a context handle (magic word catches freed or foreign pointers,
+// the debug guard idea of the microcrad page's Value.magic).
+int tt_check_ctx(const tt_ctx *ctx);
+int tt_set_error(tt_ctx *ctx, int status, const char *fmt, ...);
+// Report the result of the last kernel launch(es) on this thread.
+int tt_check_launch(tt_ctx *ctx, const char *what);
+// Arena scratch that lives until the matching tt_scratch_release.
+struct tt_scratch_scope {
+  tt_ctx *ctx;
+  size_t saved;
+  explicit tt_scratch_scope(tt_ctx *c) : ctx(c), saved(c->offset) {}
+  ~tt_scratch_scope() { ctx->offset = saved; }
+};
+int tt_arena_alloc(tt_ctx *ctx, size_t bytes, void **p);
+
+#define TT_REQUIRE(ctx, cond, ...)                                 \
+  do {                                                             \
+    if (!(cond)) return tt_set_error((ctx), TT_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+#define TT_TRY(expr)          \
+  do {                        \
+    int _rc = (expr);         \
+    if (_rc != TT_OK) return _rc; \
+  } while (0)
+
+static inline bool tt_aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+typedef uint16_t bf16_t;  // bf16 storage
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// float -> bf16, round to nearest even, NaN kept quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// Pack two floats into one dword of two bf16 (lo = a).
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t *p, size_t i) { return bf2f(p[i]); }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) { p[i] = f2bf(v); }
+};
+
+// Wave64 reductions (butterfly over all 64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))).
+// tanh(u) = 1 - 2/(exp(2u)+1) evaluated with the hardware exp; saturates
+// correctly for |u| large (exp -> inf gives 1, exp -> 0 gives -1).
+#define TT_GELU_K 0.7978845608028654f
+#define TT_GELU_A 0.044715f
+__device__ __forceinline__ float tt_tanh(float u) {
+  float e = __expf(2.0f * u);
+  return 1.0f - 2.0f / (e + 1.0f);
+}
+__device__ __forceinline__ float gelu_f(float x) {
+  float u = TT_GELU_K * (x + TT_GELU_A * x * x * x);
+  return 0.5f * x * (1.0f + tt_tanh(u));
+}
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  float u = TT_GELU_K * (x + TT_GELU_A * x * x * x);
+  float t = tt_tanh(u);
+  float du = TT_GELU_K * (1.0f + 3.0f * TT_GELU_A * x * x);
+  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * du;
+}
+
+// ---------------------------------------------------------------------------
+// Internal launchers (defined in the .hip files)
+// ---------------------------------------------------------------------------
+
+// Epilogue kinds of the GEMM kernel.
+enum GemmEpi {
+  EPI_STORE = 0,       // out = acc + bias                  (OutT)
+  EPI_RESID = 1,       // out(f32) = resid + acc + bias
+  EPI_GELU = 2,        // aux = bf(acc + bias) ; out = gelu(acc + bias)
+  EPI_GELU_BWD = 3,    // out = acc * gelu'(aux)            (aux = stored preact)
+  EPI_ACCUM = 4,       // out(f32) += acc  (atomic when split-K > 1)
+  EPI_STORE_ACC = 5    // out(f32) += acc  (non-atomic, split-K must be 1)
+};
+
+// C[m,n] = sum_k A(m,k) B(k,n), row/col strides described by the k-major flags:
+//   a_kmajor: A(m,k) = A[m*lda + k]   else A[k*lda + m]
+//   b_kmajor: B(k,n) = B[n*ldb + k]   else B[k*ldb + n]
+struct GemmArgs {
+  const void *A; int lda; bool a_kmajor;
+  const void *B; int ldb; bool b_kmajor;
+  int M, N, K;
+  int epi;
+  void *out; int ldo; bool out_bf16;
+  const float *bias;           // [N] nullable
+  const float *resid; int ldr; // EPI_RESID
+  void *aux; int ldx;          // EPI_GELU (written preact) / EPI_GELU_BWD (read preact)
+  int split_k;                 // >= 1 (EPI_ACCUM only)
+  int n_valid;                 // columns >= n_valid of C are not stored (ragged pad); 0 = N
+};
+int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
+
+int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, const float *x,
+                          const float *g, const float *b, void *y, float *mean, float *rstd);
+// dx_out = dres + LN_bwd(dy); also writes a bf16 copy when dx_bf16 != NULL.
+int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                          const float *mean, const float *rstd, const float *g, const float *dy,
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db);
+int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out);
+int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v);
+int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst);
+int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
+                     void *out, float *lse);
+int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
+                     const void *out, const float *lse, const void *dout, void *dqkv,
+                     float *scratch_D);
+// In-place CE over logits; per_row_loss [N] scratch; loss = mean.
+int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
+               const int32_t *targets, float *per_row_loss, float *loss, float grad_scale);
+int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,
+                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t);
+int tt_check_finite(tt_ctx *ctx, const float *x, size_t n, int32_t *flag);

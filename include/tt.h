@@ -1,0 +1,301 @@
+/*
+ * tt.h — C ABI of libtt, an MI355X (gfx950) GPT-2 training step.
+ *
+ * Sources (page titles abbreviated):
+ *   tinytorch page  "不用PyTorch，一个头文件就能训练GPT-2：Arena内存池+自动微分的C++实现"
+ *   Forge page      "17岁少年用C++从零构建深度学习框架Forge，精确复现GPT-2"
+ *   C++/CUDA page   "从零手写C++深度学习框架：Tensor设计、Autograd与CUDA优化实战"
+ *   define-by-run   "为什么我要从零写一个深度学习框架" (NumPy autograd tutorial)
+ *   microcrad page  "microcrad" (micrograd in C)
+ *
+ * General conventions
+ *   - Every pointer argument is a DEVICE pointer unless marked [host].
+ *   - All arrays are dense row-major.  A linear layer is y = x·W + b with W of
+ *     shape [in, out] (tinytorch page, §3 item 3: C[M,N] = A[M,K]·B[K,N]).
+ *   - Every call only validates arguments on the host and enqueues kernels on
+ *     the context's HIP stream; it returns before the GPU work finishes.
+ *     Nothing aborts: every call returns a tt_status (0 on success, negative
+ *     on failure — the convention of microcrad's value_backward).  On a
+ *     validation failure nothing is enqueued.  Asynchronous device faults and
+ *     in-kernel range errors (a token id or target outside [0, V)) surface at
+ *     tt_ctx_sync().
+ *   - Gradient outputs marked "+=" ACCUMULATE into what the caller passes, the
+ *     rule the tinytorch page states for tensors with several consumers
+ *     (§3 item 3) and the define-by-run page illustrates with 2 + 3 = 5
+ *     (§3.2).  The caller zeroes them (microcrad "反向传播" section;
+ *     tinytorch §3 item 7, ZeroGrad before Backward).  tt_train_step zeroes
+ *     its own gradient buffer.
+ *   - Precision modes.  TT_F32: every tensor float32 and float32 arithmetic.
+ *     TT_BF16: GEMM and attention operands bf16 with float32 accumulation;
+ *     master weights, gradients, optimizer moments, the residual stream,
+ *     LayerNorm statistics and the loss stay float32 (C++/CUDA page §3.4:
+ *     fp32 master weights with low-precision compute).  A "mode tensor" below
+ *     is float32 in TT_F32 and bf16 (uint16 storage, round to nearest even)
+ *     in TT_BF16.
+ *   - Alignment: device pointers must be 16-byte aligned; row lengths need not
+ *     be tile multiples (ragged edges are handled).
+ *   - One context per stream; a context is not thread-safe.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TT_OK = 0,
+  TT_EINVAL = -1,       /* bad argument: NULL, shape, alignment, mode           */
+  TT_ENOMEM = -2,       /* arena exhausted, or device allocation failed          */
+  TT_EHIP = -3,         /* HIP runtime error (text in tt_ctx_last_error)         */
+  TT_ESTALE = -4,       /* handle whose magic word does not match (freed/foreign)*/
+  TT_ENONFINITE = -5,   /* a non-finite value was detected                       */
+  TT_EUNSUPPORTED = -6, /* shape outside what the kernels support (e.g. hs!=64)  */
+  TT_ERANGE = -7        /* a token id or target was outside [0, V) (device check)*/
+} tt_status;
+
+typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_mode;
+
+typedef struct tt_ctx tt_ctx;
+typedef struct tt_model tt_model;
+
+/* ------------------------------------------------------------------------ */
+/* Context and HBM arena.                                                    */
+/* The tinytorch page (§3 item 1) carves every tensor out of one pre-allocated */
+/* block by bumping an offset and frees all intermediates at once by resetting */
+/* it.  Here the block lives in HBM: one hipMalloc (or caller-owned memory),   */
+/* bumped with 256-byte alignment; tt_ctx_mark() fixes what stays and          */
+/* tt_ctx_reset() returns the offset to the mark.                             */
+/* ------------------------------------------------------------------------ */
+
+/* device: HIP device ordinal.  hip_stream: hipStream_t to enqueue on (NULL =
+ * the null stream).  arena_bytes: arena size.  arena_base: nullable; when
+ * given, caller-owned device memory of arena_bytes bytes (e.g. a torch
+ * buffer) that must outlive the context; when NULL the context hipMallocs the
+ * arena and frees it in tt_ctx_destroy.  *out [host] receives the handle.
+ * Errors: TT_EINVAL, TT_ENOMEM, TT_EHIP. */
+int tt_ctx_create(int device, void *hip_stream, size_t arena_bytes, void *arena_base,
+                  tt_ctx **out);
+/* NULL-safe (microcrad: releasing NULL is a no-op).  Frees only what the
+ * context allocated.  Waits for the stream first. */
+void tt_ctx_destroy(tt_ctx *ctx);
+/* Change the stream later calls enqueue on. */
+int tt_ctx_set_stream(tt_ctx *ctx, void *hip_stream);
+/* Bump-allocate bytes (align: power of two, at least 256 is used).  *dptr
+ * [host] receives a device pointer valid until the next tt_ctx_reset() below
+ * it or tt_ctx_destroy().  TT_ENOMEM when the arena is exhausted. */
+int tt_ctx_alloc(tt_ctx *ctx, size_t bytes, size_t align, void **dptr);
+/* Make everything allocated so far persistent. */
+int tt_ctx_mark(tt_ctx *ctx);
+/* Return the offset to the last mark (tinytorch §3 item 1, Reset()). */
+int tt_ctx_reset(tt_ctx *ctx);
+/* Bytes in use / capacity ([host] outputs, either may be NULL). */
+int tt_ctx_usage(const tt_ctx *ctx, size_t *used, size_t *capacity);
+/* Wait for the stream; report asynchronous HIP errors (TT_EHIP) and in-kernel
+ * range errors (TT_ERANGE, then cleared). */
+int tt_ctx_sync(tt_ctx *ctx);
+const char *tt_strerror(int status);
+const char *tt_ctx_last_error(const tt_ctx *ctx);
+
+/* ------------------------------------------------------------------------ */
+/* Op level.                                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef enum {
+  TT_EPI_NONE = 0,     /* Y = X·W + b                                   (Y mode)   */
+  TT_EPI_GELU = 1,     /* P = X·W + b stored in preact; Y = GELU_tanh(P)  (mode)    */
+  TT_EPI_RESIDUAL = 2  /* Y = resid + X·W + b                           (Y float32)*/
+} tt_epilogue;
+
+/* Linear forward — tinytorch page §3 item 3 (MatMulForward), §3 item 4 (GELU,
+ * tanh form), §4 (residual connection x + f(x)).
+ * X [M,K] mode tensor, W [K,N] mode tensor, b [N] float32 (nullable).
+ * Y [M,N]: mode tensor for NONE/GELU, float32 for RESIDUAL.  resid [M,N]
+ * float32 (RESIDUAL only; may equal Y).  preact [M,N] mode tensor (GELU only,
+ * nullable: then not stored).  M, K, N >= 1. */
+int tt_linear_fwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X,
+                  const void *W, const float *b, void *Y, int epilogue, const float *resid,
+                  void *preact);
+
+/* Linear backward — tinytorch page §3 item 3 (MatMulBackward: dA += dC·Bᵀ,
+ * dB += Aᵀ·dC); define-by-run page §3.2 (same shapes).
+ * X [M,K], W [K,N], dY [M,N]: mode tensors.  dX [M,K] float32, nullable:
+ * written (accumulate_dX = 0) or += (accumulate_dX != 0).  dW [K,N] float32
+ * +=, nullable.  db [N] float32 +=, nullable (column sums of dY). */
+int tt_linear_bwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X,
+                  const void *W, const void *dY, float *dX, float *dW, float *db,
+                  int accumulate_dX);
+
+/* LayerNorm forward — tinytorch page §4 (subtract the mean, divide by the
+ * standard deviation, scale, shift); Forge page "最硬的一关" (epsilon placement
+ * and variance method matter).  Biased variance, eps inside the square root:
+ *   y = (x - mean) * rstd * g + b,  rstd = 1/sqrt(mean((x-mean)^2) + eps).
+ * x [N,C] float32; g, b [C] float32; y [N,C] mode tensor; mean, rstd [N]
+ * float32 (nullable).  1 <= C <= 4096, C % 4 == 0. */
+int tt_layernorm_fwd(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, const float *x,
+                     const float *g, const float *b, void *y, float *mean, float *rstd);
+
+/* LayerNorm backward (chain rule of the above).  dy [N,C] float32.
+ * dx [N,C] float32 +=.  dg, db [C] float32 +=.  Same C limits. */
+int tt_layernorm_bwd(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                     const float *mean, const float *rstd, const float *g, const float *dy,
+                     float *dx, float *dg, float *db);
+
+/* GELU, tanh form (tinytorch page §3 item 4), elementwise on n values of a
+ * mode tensor.  Backward uses the analytic derivative of the tanh form
+ * (the page's printed backward is not that derivative): dx = dy * gelu'(x),
+ * dx written. */
+int tt_gelu_fwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, void *y);
+int tt_gelu_bwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, const void *dy, void *dx);
+
+/* Causal multi-head self-attention — tinytorch page §4 (causal mask, stable
+ * softmax); Forge page "最硬的一关" (scale 1/sqrt(d_k), -inf above the
+ * diagonal).  qkv [B,T,3C] mode tensor with q | k | v column blocks, head h
+ * owning columns h*hs .. h*hs+hs-1 of each; out [B,T,C] mode tensor; lse
+ * [B,NH,T] float32 = log of each row's softmax denominator (of the scaled
+ * scores).  hs must be 64; T >= 1 (ragged T handled). */
+int tt_attn_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, int hs, const void *qkv,
+                void *out, float *lse);
+/* Backward: dout [B,T,C] mode tensor -> dqkv [B,T,3C] mode tensor (written).
+ * Uses out and lse from the forward.  Scratch comes from the arena. */
+int tt_attn_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, int hs, const void *qkv,
+                const void *out, const float *lse, const void *dout, void *dqkv);
+
+/* Fused softmax + cross-entropy, forward and backward in place — tinytorch
+ * page §3 item 5 (dlogits = probs - onehot), Forge page "核心组件清单"
+ * (cross-entropy fused with log-softmax) and "瓶颈分析是否合理" (one fused
+ * pass instead of three).  logits [N, ld] mode tensor, the first V columns
+ * used; on return it holds dz = (softmax(z) - onehot(y)) * grad_scale in the
+ * first V columns and 0 in columns V..ld-1.  targets [N] int32 in [0,V).
+ * loss: one float32 receiving mean_n(logsumexp(z_n) - z_n[y_n]) (written).
+ * grad_scale <= 0 means 1/N. */
+int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
+                 const int32_t *targets, float *loss, float grad_scale);
+
+/* Token + position embedding — tinytorch page §3 item 6.
+ * tok [B,T] int32 in [0,V); wte [V,C], wpe [>=T,C], x0 [B,T,C] float32.
+ * x0[b,t] = wte[tok[b,t]] + wpe[t].  Ids outside [0,V) give a NaN row and
+ * TT_ERANGE at the next tt_ctx_sync. */
+int tt_embed_fwd(tt_ctx *ctx, int B, int T, int C, int V, const int32_t *tok,
+                 const float *wte, const float *wpe, float *x0);
+/* dwte [V,C] += scatter of dx0 rows by token id; dwpe [>=T,C] += sum over b. */
+int tt_embed_bwd(tt_ctx *ctx, int B, int T, int C, int V, const int32_t *tok,
+                 const float *dx0, float *dwte, float *dwpe);
+
+/* Optimisers.  AdamW — tinytorch page §3 item 7 (m, v, bias correction with
+ * t = step + 1) and Forge page "核心组件清单" (decoupled weight decay):
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   w -= lr * (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd * wd_mult * w).
+ * w_lowp (nullable) receives a bf16 copy of the new w.  t is 1-based. */
+typedef struct {
+  float *w;
+  const float *g;
+  float *m;
+  float *v;
+  void *w_lowp;
+  size_t n;
+  float wd_mult;
+} tt_param;
+int tt_adamw_step(tt_ctx *ctx, const tt_param *params /* [host] */, int count, float lr,
+                  float beta1, float beta2, float eps, float wd, int t);
+/* SGD — tinytorch page §8 step 5: w -= lr * g. */
+int tt_sgd_step(tt_ctx *ctx, float *w, const float *g, size_t n, float lr);
+/* float32 -> bf16 (round to nearest even) copy of n values. */
+int tt_cast_bf16(tt_ctx *ctx, size_t n, const float *src, void *dst);
+
+/* ------------------------------------------------------------------------ */
+/* Composite calls.                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* One pre-LN transformer block — tinytorch page §3 item 6:
+ *   x1 = x + attn(LN1(x)) ; y = x1 + MLP(LN2(x1)), MLP = fc -> GELU -> fcproj.
+ * F is the MLP width (4C for GPT-2); hs = C/NH must be 64. */
+typedef struct {
+  int B, T, C, NH, F;
+  tt_mode mode;
+  float ln_eps;
+} tt_block_cfg;
+/* Weight matrices in the mode dtype ([in,out]); biases and LN params float32. */
+typedef struct {
+  const float *ln1_g, *ln1_b;
+  const void *w_qkv; const float *b_qkv;   /* [C,3C], [3C] */
+  const void *w_proj; const float *b_proj; /* [C,C],  [C]  */
+  const float *ln2_g, *ln2_b;
+  const void *w_fc; const float *b_fc;     /* [C,F],  [F]  */
+  const void *w_fcp; const float *b_fcp;   /* [F,C],  [C]  */
+} tt_block_w;
+/* Gradients, all float32, accumulated (+=). */
+typedef struct {
+  float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_proj, *b_proj;
+  float *ln2_g, *ln2_b, *w_fc, *b_fc, *w_fcp, *b_fcp;
+} tt_block_g;
+/* Activations the backward needs, carved from the arena (opaque). */
+typedef struct tt_block_saved tt_block_saved;
+int tt_block_saved_create(tt_ctx *ctx, const tt_block_cfg *cfg, tt_block_saved **out);
+/* NULL-safe; the device memory returns with the arena. */
+void tt_block_saved_destroy(tt_block_saved *saved);
+/* x, y [B,T,C] float32. */
+int tt_block_fwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w, const float *x,
+                 float *y, tt_block_saved *saved);
+/* dy [B,T,C] float32 -> dx [B,T,C] float32 (written); grads +=.  Scratch
+ * from the arena. */
+int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
+                 const tt_block_saved *saved, const float *dy, float *dx, tt_block_g *g);
+
+/* Tied LM head + mean cross-entropy, forward and backward (tinytorch page §3
+ * items 5-6; Forge page "瓶颈分析是否合理").  h [N,C] mode tensor, wte [V,C]
+ * mode tensor, targets [N] int32.  loss: one float32 (written, the mean).
+ * dh [N,C] float32 (written).  dwte [V,C] float32 (+=).  The [N,V] logits
+ * live in arena scratch (mode dtype) and are overwritten by their gradient. */
+int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int V, const void *h,
+                        const void *wte, const int32_t *targets, float *loss, float *dh,
+                        float *dwte);
+
+/* Whole GPT-2 model: parameters, gradients, AdamW moments and (TT_BF16) a
+ * bf16 shadow of the parameters, all in one arena region; activations for a
+ * batch of up to B_max x T_max tokens.  The token table has V_pad >= V rows
+ * (rows V..V_pad-1 stay zero) and is tied to the LM head. */
+typedef struct {
+  int L, C, NH, F, V, V_pad, T_max, B_max;
+  tt_mode mode;
+  float ln_eps;
+} tt_model_cfg;
+int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **out);
+void tt_model_destroy(tt_model *model); /* NULL-safe; memory returns with the arena */
+/* Parameter table: count [host] receives the number of tensors; when params
+ * [host] is non-NULL it must hold *count entries and receives, in order,
+ * wte [V_pad,C], wpe [T_max,C], per layer ln1_g, ln1_b, w_qkv, b_qkv, w_proj,
+ * b_proj, ln2_g, ln2_b, w_fc, b_fc, w_fcp, b_fcp, then lnf_g, lnf_b — with
+ * device pointers to the master weight (w), gradient (g), moments (m, v) and
+ * shadow (w_lowp, NULL in TT_F32).  Callers write initial weights through w
+ * and then call tt_model_refresh_shadow. */
+int tt_model_param_table(tt_model *model, tt_param *params, int *count);
+/* Total float32 parameter slots (including alignment padding). */
+int tt_model_num_params(const tt_model *model, size_t *n_slots, size_t *n_params);
+/* Recompute the bf16 shadow from the master weights and zero m, v. */
+int tt_model_refresh_shadow(tt_model *model);
+/* One training step (tinytorch page §3 item 7: forward, zero grads, backward,
+ * Adam update), loss on every position with next-token targets, mean over the
+ * B*T positions.  tok, targets [B,T] int32.  loss: one float32 (written).
+ * nonfinite: nullable int32 flag set to 1 if the loss is not finite (AdamW
+ * still runs; callers that want to skip it use tt_model_fwd_bwd + their own
+ * check).  t: 1-based AdamW step.  B <= B_max, T <= T_max. */
+int tt_train_step(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *tok,
+                  const int32_t *targets, float lr, float beta1, float beta2, float eps,
+                  float wd, int t, float *loss, int32_t *nonfinite);
+/* Forward + backward only (gradients written to the model's gradient
+ * buffer, zeroed first), no optimizer step. */
+int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *tok,
+                     const int32_t *targets, float *loss);
+/* AdamW over every model parameter in one launch (weight decay on all). */
+int tt_model_adamw(tt_ctx *ctx, tt_model *model, float lr, float beta1, float beta2,
+                   float eps, float wd, int t);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_H */
