@@ -53,6 +53,7 @@ struct GemmParams {
   void *aux; int ldx;
   int n_valid;
   int tiles_m, tiles_n;
+  int vec_out;   // output/aux/resid rows allow 4-wide vector access
 };
 
 // Tile shape: BM x BN block, BK deep, WM x WN waves.
@@ -87,17 +88,36 @@ struct TileLoader {
     return KMAJOR ? p[(size_t)r * ld + k] : p[(size_t)k * ld + r];
   }
 
+  // Pack VEC elements (element i read by f(i), zero when !ok(i)) into a uint4
+  // without an addressable temporary (keeps everything in registers).
+  template <typename F>
+  __device__ __forceinline__ static uint4 gather_vec(F f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (sizeof(T) == 2) {
+        uint32_t lo = f(2 * q), hi = f(2 * q + 1);
+        w[q] = lo | (hi << 16);
+      } else {
+        w[q] = f(q);
+      }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ __forceinline__ static uint32_t bits(T v) {
+    if constexpr (sizeof(T) == 2) return (uint32_t)v;
+    else return __float_as_uint(v);
+  }
+
   __device__ __forceinline__ static uint4 load_vec_kmajor(const T *p, int ld, int r, int k, int R,
                                                           int K) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < R) {
+      const T *row = p + (size_t)r * ld;
       if (k + VEC <= K) {
-        v = *(const uint4 *)(p + (size_t)r * ld + k);
+        v = *(const uint4 *)(row + k);
       } else if (k < K) {
-        T tmp[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) tmp[i] = (k + i < K) ? p[(size_t)r * ld + k + i] : T(0);
-        v = *(uint4 *)tmp;
+        v = gather_vec([&](int i) { return (k + i < K) ? bits(row[k + i]) : 0u; });
       }
     }
     return v;
@@ -106,13 +126,11 @@ struct TileLoader {
                                                           int K) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (k < K) {
+      const T *row = p + (size_t)k * ld;
       if (r + VEC <= R) {
-        v = *(const uint4 *)(p + (size_t)k * ld + r);
+        v = *(const uint4 *)(row + r);
       } else if (r < R) {
-        T tmp[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) tmp[i] = (r + i < R) ? p[(size_t)k * ld + r + i] : T(0);
-        v = *(uint4 *)tmp;
+        v = gather_vec([&](int i) { return (r + i < R) ? bits(row[r + i]) : 0u; });
       }
     }
     return v;
@@ -224,6 +242,87 @@ __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int 
     ((float *)out)[(size_t)m * ldo + n] = v;
 }
 
+// Epilogue for 4 consecutive columns n..n+3 of row m (only the first `cnt`
+// of them exist when the tile sticks out of the matrix).  Vector accesses
+// need 16-byte (f32) / 8-byte (bf16) aligned rows, which the host checks
+// (p.vec_out); otherwise elements are handled one by one.
+__device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
+  const bool full = cnt >= 4 && p.vec_out;
+  float a[4] = {v.x, v.y, v.z, v.w};
+  const int lim = cnt < 4 ? cnt : 4;
+  switch (p.epi) {
+    case EPI_STORE:
+    case EPI_GELU: {
+      if (p.epi == EPI_GELU) {
+        if (p.aux) {
+          if (full && p.out_bf16)
+            *(uint2 *)((bf16_t *)p.aux + (size_t)m * p.ldx + n) =
+                make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+          else
+            for (int q = 0; q < lim; ++q) store_out(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = gelu_f(a[q]);
+      }
+      if (full) {
+        if (p.out_bf16)
+          *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
+              make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+        else
+          *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) = make_float4(a[0], a[1], a[2], a[3]);
+      } else {
+        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+      }
+      break;
+    }
+    case EPI_RESID: {
+      const float *rp = p.resid + (size_t)m * p.ldr + n;
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      if (full) {
+        float4 r = *(const float4 *)rp;
+        *(float4 *)op = make_float4(r.x + a[0], r.y + a[1], r.z + a[2], r.w + a[3]);
+      } else {
+        for (int q = 0; q < lim; ++q) op[q] = rp[q] + a[q];
+      }
+      break;
+    }
+    case EPI_GELU_BWD: {
+      float h[4];
+      if (p.out_bf16) {
+        const bf16_t *hp = (const bf16_t *)p.aux + (size_t)m * p.ldx + n;
+        if (full) {
+          uint2 u = *(const uint2 *)hp;
+          h[0] = __uint_as_float(u.x << 16); h[1] = __uint_as_float(u.x & 0xffff0000u);
+          h[2] = __uint_as_float(u.y << 16); h[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          for (int q = 0; q < 4; ++q) h[q] = q < lim ? bf2f(hp[q]) : 0.f;
+        }
+      } else {
+        const float *hp = (const float *)p.aux + (size_t)m * p.ldx + n;
+        for (int q = 0; q < 4; ++q) h[q] = q < lim ? hp[q] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] *= gelu_grad_f(h[q]);
+      if (full && p.out_bf16)
+        *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
+            make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+      else
+        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+      break;
+    }
+    case EPI_ACCUM: {
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      for (int q = 0; q < lim; ++q) unsafeAtomicAdd(op + q, a[q]);
+      break;
+    }
+    case EPI_STORE_ACC: {
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      for (int q = 0; q < lim; ++q) op[q] += a[q];
+      break;
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool A_KM, bool B_KM, bool VECLD>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(GemmParams p) {
@@ -302,45 +401,41 @@ gemm_kernel(GemmParams p) {
   }
 
   // ---------------------------------------------------------------- epilogue
+  // Stage the fp32 C tile through LDS (the operand buffers are free now), then
+  // apply the epilogue cooperatively: each thread owns 4 consecutive columns,
+  // so bias / residual / aux reads and the output writes are row-coalesced.
+  constexpr int LDC = BN + 4;
+  static_assert(BM * LDC * 4 <= (int)sizeof(smem), "C tile does not fit in LDS");
+  float *Cs = (float *)smem;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Cs[(wm * TL::WTM + i * 16 + lg * 4 + r) * LDC + wn * TL::WTN + j * 16 + lr] = acc[i][j][r];
+  __syncthreads();
+  constexpr int TPR = BN / 4;            // threads per row
+  constexpr int RPP = NT / TPR;          // rows per pass
+  const int cc = (tid % TPR) * 4;
+  const int n = n0 + cc;
   const int nv = p.n_valid;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TL::WTN + j * 16 + lr;
-      if (n >= nv) continue;
-      const float bias = (p.bias && blockIdx.z == 0) ? p.bias[n] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * TL::WTM + i * 16 + lg * 4 + r;
-        if (m >= p.M) continue;
-        float v = acc[i][j][r] + bias;
-        switch (p.epi) {
-          case EPI_STORE:
-            store_out(p.out, p.ldo, p.out_bf16, m, n, v);
-            break;
-          case EPI_RESID:
-            ((float *)p.out)[(size_t)m * p.ldo + n] = p.resid[(size_t)m * p.ldr + n] + v;
-            break;
-          case EPI_GELU:
-            if (p.aux) store_out(p.aux, p.ldx, p.out_bf16, m, n, v);
-            store_out(p.out, p.ldo, p.out_bf16, m, n, gelu_f(v));
-            break;
-          case EPI_GELU_BWD: {
-            float h = p.out_bf16 ? bf2f(((const bf16_t *)p.aux)[(size_t)m * p.ldx + n])
-                                 : ((const float *)p.aux)[(size_t)m * p.ldx + n];
-            store_out(p.out, p.ldo, p.out_bf16, m, n, v * gelu_grad_f(h));
-            break;
-          }
-          case EPI_ACCUM:
-            unsafeAtomicAdd(&((float *)p.out)[(size_t)m * p.ldo + n], v);
-            break;
-          case EPI_STORE_ACC:
-            ((float *)p.out)[(size_t)m * p.ldo + n] += v;
-            break;
-        }
-      }
+  float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.bias && blockIdx.z == 0) {
+    if (n + 3 < nv) {
+      bias = *(const float4 *)(p.bias + n);
+    } else {
+      if (n < nv) bias.x = p.bias[n];
+      if (n + 1 < nv) bias.y = p.bias[n + 1];
+      if (n + 2 < nv) bias.z = p.bias[n + 2];
     }
+  }
+  for (int rr = tid / TPR; rr < BM; rr += RPP) {
+    const int m = m0 + rr;
+    if (m >= p.M || n >= nv) continue;
+    float4 v = *(const float4 *)(Cs + rr * LDC + cc);
+    v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
+    epilogue4(p, m, n, v, nv - n);
   }
 }
 
@@ -352,6 +447,15 @@ int launch_gemm(tt_ctx *ctx, const GemmArgs &g, int split) {
   p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
   p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
   p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
+  {
+    const int oes = g.out_bf16 ? 2 : 4;   // bytes per output element (aux has the same)
+    bool ok = ((uintptr_t)g.out % (4 * oes) == 0) && (g.ldo % 4 == 0);
+    if (g.aux) ok = ok && ((uintptr_t)g.aux % (4 * oes) == 0) && (g.ldx % 4 == 0);
+    if (g.resid) ok = ok && ((uintptr_t)g.resid % 16 == 0) && (g.ldr % 4 == 0);
+    if (g.epi == EPI_RESID || g.epi == EPI_ACCUM || g.epi == EPI_STORE_ACC)
+      ok = ok && ((uintptr_t)g.out % 16 == 0);
+    p.vec_out = ok ? 1 : 0;
+  }
   p.tiles_m = (g.M + BM - 1) / BM;
   p.tiles_n = (g.N + BN - 1) / BN;
   int kb = (g.K + BK - 1) / BK;

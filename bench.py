@@ -1,0 +1,171 @@
+"""Benchmark: one GPT-2 training step (forward, backward, AdamW) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
+
+Workload (default): GPT-2 124M — 12 layers, d=768, 12 heads, vocab 50257
+(token table padded to 50304 rows), context 1024, batch 8; synthetic seeded
+token ids and weights; bf16 MFMA compute with fp32 master weights; AdamW
+lr 3e-4, betas (0.9, 0.95), wd 0.1.  Inputs and weights are resident in HBM
+before the timed region.  Prints ONE JSON line on stdout (progress on stderr).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec, GPT-2 124M fwd+bwd+AdamW step at 1 GPU; MFMA util %"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+WORKLOADS = {
+    "gpt2-124m": dict(L=12, C=768, NH=12, V=50257, V_pad=50304, T=1024, B=8),
+    "gpt2-350m": dict(L=24, C=1024, NH=16, V=50257, V_pad=50304, T=1024, B=16),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_flops(L, C, V, T, B, F=None, **_):
+    """Algorithmic FLOPs of one training step (forward + backward = 3x forward;
+    causal attention counts only the j <= i triangle)."""
+    F = 4 * C if F is None else F
+    N = B * T
+    linear = 2.0 * N * (4 * C * C + 2 * C * F)        # qkv, proj, fc, fcproj
+    attn = 2.0 * B * C * T * (T + 1)                   # QK^T and PV, causal
+    head = 2.0 * N * C * V
+    return 3.0 * (L * (linear + attn) + head)
+
+
+def cpu_baseline(w, seconds_budget=20.0):
+    """Time the CPU oracle (float64 NumPy, as it stands) on a bounded sample of
+    the same workload: one training step of the same model on one sequence of
+    a reduced length, scaled to tokens/s."""
+    import numpy as np
+    import oracle  # noqa: F401  (test infrastructure: the baseline leg only)
+    from oracle import gpt2 as og
+    from autograd_transformer_amd import synthetic as syn
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
+    shape = syn.ModelShape(w["L"], w["C"], w["NH"], w["V"], w["T"])
+    cfg = og.GPTConfig(n_layer=w["L"], n_embd=w["C"], n_head=w["NH"], vocab=w["V"],
+                       block_size=w["T"])
+    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=3).items()}
+    zeros = {k: np.zeros_like(v) for k, v in p.items()}
+    T = 128
+    tok, tgt = syn.gpt2_tokens(1, T, w["V"], seed=3)
+    t0 = time.perf_counter()
+    og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full {w['L']}-layer training step (fwd+bwd+AdamW, bf16 storage "
+                      f"rounding, float64 NumPy) on 1 sequence of {T} tokens; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the data-parallel sharding is described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+
+    w = WORKLOADS[args.workload]
+    L, C, NH, V, V_pad, T, B = (w[k] for k in ("L", "C", "NH", "V", "V_pad", "T", "B"))
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] {args.workload}: generating synthetic weights ...")
+    shape = syn.ModelShape(L, C, NH, V, T)
+    params = syn.gpt2_params(shape, seed=3)
+    tok, tgt = syn.gpt2_tokens(B, T, V, seed=3)
+    arena = 64 << 30 if L > 12 else 24 << 30
+    ctx = tt.Context(arena_bytes=arena, stream=stream)
+    model = tt.Model(ctx, L=L, C=C, NH=NH, V=V, T_max=T, B_max=B, mode="bf16", V_pad=V_pad)
+    model.load(params)
+    del params
+    tok_d = torch.from_numpy(tok).cuda()
+    tgt_d = torch.from_numpy(tgt).cuda()
+    loss = torch.zeros(1, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.95, 1e-8, 0.1
+
+    def step(t):
+        tt.tt_train_step(ctx, model, B, T, tok_d, tgt_d, lr, b1, b2, eps, wd, t, loss, flag)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    t = 1
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    ctx.sync()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(t)
+        t += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ctx.sync()
+    ms = e0.elapsed_time(e1) / args.steps
+    last_loss = float(loss.item())
+    if not math.isfinite(last_loss) or int(flag.item()) != 0:
+        log(f"[bench] WARNING: non-finite loss {last_loss}")
+    tokens = B * T
+    flops = step_flops(**w)
+    value = tokens / (ms / 1e3)
+    tflops = flops / (ms / 1e3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step  {value:,.0f} tokens/s  {tflops:.1f} TFLOP/s "
+        f"(wall {wall:.2f}s)  loss {last_loss:.4f}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded uniform token ids, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload} train step (fwd+bwd+AdamW), bf16 MFMA / fp32 master",
+                   "global_batch": B, "seq_len": T, "layers": L, "d_model": C, "heads": NH,
+                   "vocab": V, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "loss": round(last_loss, 5),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    model.close()
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,22 +24,23 @@ def round_bf16(x):
     part (minus one if the kept lsb is 0, which makes ties go to even) and
     clear the low bits.  Exponents of bf16 and float32 agree; results below
     the normal range of bf16 (|x| < 2**-126) are rounded on the bf16 subnormal
-    grid (step 2**-133) explicitly.
+    grid (step 2**-133) explicitly.  Non-finite inputs pass through.
     """
     a = np.asarray(x, dtype=np.float64)
-    out = np.array(a, dtype=np.float64, copy=True)
-    finite = np.isfinite(out)
-    tiny = finite & (np.abs(out) < 2.0 ** -126)
-    normal = finite & ~tiny
-    if np.any(normal):
-        u = out[normal].view(np.uint64).copy()
-        lsb = (u >> np.uint64(45)) & np.uint64(1)
-        u = u + np.uint64((1 << 44) - 1) + lsb
-        u = u & ~np.uint64((1 << 45) - 1)
-        r = u.view(np.float64)
-        r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
-        out[normal] = r
-    if np.any(tiny):
-        step = 2.0 ** -133
-        out[tiny] = np.round(out[tiny] / step) * step  # np.round is half-to-even
-    return out
+    u = np.ascontiguousarray(a).view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    u = u + np.uint64((1 << 44) - 1) + lsb
+    u = u & ~np.uint64((1 << 45) - 1)
+    r = u.view(np.float64).reshape(a.shape)
+    with np.errstate(invalid="ignore", over="ignore"):
+        big = np.abs(r) > _BF16_MAX
+        if big.any():
+            r[big] = np.copysign(np.inf, a[big])
+        tiny = np.abs(a) < 2.0 ** -126
+        if tiny.any():
+            step = 2.0 ** -133
+            r[tiny] = np.round(a[tiny] / step) * step   # np.round: half to even
+        bad = ~np.isfinite(a)
+        if bad.any():
+            r[bad] = a[bad]
+    return r

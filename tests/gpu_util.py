@@ -59,3 +59,39 @@ def tol(mode):
 
 def sync():
     torch_mod().cuda.synchronize()
+
+
+def split_key_bias(name, got, ref, C):
+    """The key third of a qkv bias has an exactly zero gradient: adding a
+    constant to every key adds q·b_k to a whole score row, which the softmax
+    ignores.  Returns (rest_got, rest_ref, key_got) so the rest is compared by
+    rel-L2 and the key part by a noise bound."""
+    if not name.endswith("b_qkv"):
+        return got, ref, None
+    import numpy as _np
+    rest = _np.r_[0:C, 2 * C:3 * C]
+    return got[rest], ref[rest], got[C:2 * C]
+
+
+KEY_BIAS_NOISE = {"f32": 1e-3, "bf16": 5e-2}
+
+
+def check_post_adamw(w_gpu, w0, g_ref, w_ref, lr, wd, bar, grad_rms):
+    """Post-AdamW weights after the first step (t = 1), where
+    w1 = w0 (1 - lr wd) - lr g / (|g| + eps): the step jumps by 2 lr when a
+    gradient's sign changes, so entries whose oracle gradient is within the
+    gradient tolerance of zero (|g| <= 0.1 rms) have no unique expected value.
+    Those are checked against AdamW's step bound |w1 - w0 (1 - lr wd)| <= lr;
+    the resolved entries by rel-L2.  Returns the rel-L2."""
+    import numpy as _np
+    w_gpu, w0, g_ref, w_ref = (_np.asarray(a, _np.float64).ravel() for a in (w_gpu, w0, g_ref, w_ref))
+    resolved = _np.abs(g_ref) > 0.1 * grad_rms
+    step = _np.abs(w_gpu - w0 * (1 - lr * wd))
+    assert _np.all(step[~resolved] <= lr * 1.001 + 1e-7 * _np.abs(w0[~resolved])), "step bound"
+    if not resolved.any():
+        return 0.0
+    d = _np.linalg.norm(w_gpu[resolved] - w_ref[resolved])
+    n = _np.linalg.norm(w_ref[resolved])
+    err = d / n if n > 0 else d
+    assert err <= bar, err
+    return err

@@ -1,0 +1,119 @@
+"""Composite parity: one pre-LN GPT-2 block (tt_block_fwd / tt_block_bwd) and the
+tiny classifier step, against the float64 oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gpt2 as og
+import autograd_transformer_amd as tt
+from autograd_transformer_amd import synthetic as syn
+from tests.conftest import rel_l2
+from tests.gpu_util import dev, host, empty, zeros, lowp, tol, sync
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = tt.Context(arena_bytes=8 << 30)
+    yield c
+    c.close()
+
+
+def run_block(ctx, d, mode):
+    B, T, C, NH, F = d["B"], d["T"], d["C"], d["n_head"], d["F"]
+    w = d["w"]
+    wd = {k: dev(v, lowp(mode) if k.startswith("w_") else "f32") for k, v in w.items()}
+    saved = tt.BlockSaved(ctx, B, T, C, NH, F, mode)
+    y = empty((B, T, C))
+    tt.tt_block_fwd(ctx, saved, wd, dev(d["x"]), y)
+    dx = empty((B, T, C))
+    grads = {k: zeros(v.shape) for k, v in w.items()}
+    tt.tt_block_bwd(ctx, saved, wd, dev(d["dy"]), dx, grads)
+    sync()
+    out = host(y), host(dx), {k: host(v) for k, v in grads.items()}
+    saved.close()
+    return out
+
+
+def check_block(ctx, d, mode, bar=None):
+    bar = tol(mode) if bar is None else bar
+    w64 = {k: v.astype(np.float64) for k, v in d["w"].items()}
+    y_ref, cache = og.block_fwd(d["x"], w64, d["n_head"], mode)
+    dx_ref, g_ref = og.block_bwd(cache, w64, d["dy"], d["n_head"], mode)
+    y, dx, g = run_block(ctx, d, mode)
+    errs = {"y": rel_l2(y, y_ref), "dx": rel_l2(dx, dx_ref)}
+    errs.update({k: rel_l2(g[k], g_ref[k]) for k in g_ref})
+    bad = {k: e for k, e in errs.items() if not e <= bar}
+    assert not bad, f"rel-L2 above {bar}: {bad}"
+    return errs
+
+
+def test_block_gpt2_width_fp32():
+    """Single GPT-2 block, fp32: B=4, T=256, C=768, 12 heads, MLP 3072."""
+    c = tt.Context(arena_bytes=8 << 30)
+    errs = check_block(c, syn.block_inputs(seed=2), "f32")
+    print({k: f"{v:.1e}" for k, v in errs.items()})
+    c.close()
+
+
+def test_block_gpt2_width_bf16(ctx):
+    errs = check_block(ctx, syn.block_inputs(seed=2), "bf16")
+    print({k: f"{v:.1e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_block_ragged_perturbed(ctx, mode):
+    """Ragged T, two heads, perturbed biases and LayerNorm parameters."""
+    d = syn.block_inputs(seed=21, B=3, T=77, C=128, n_head=2, bias_std=0.1, ln_std=0.2, w_std=0.05)
+    check_block(ctx, d, mode)
+
+
+def test_block_zero_weights_is_identity(ctx):
+    d = syn.block_inputs(seed=22, B=2, T=64, C=128, n_head=2)
+    for k in d["w"]:
+        d["w"][k] = np.zeros_like(d["w"][k])
+    d["w"]["ln1_g"][:] = 1.0
+    d["w"]["ln2_g"][:] = 1.0
+    y, dx, _ = run_block(ctx, d, "f32")
+    assert np.array_equal(y, d["x"].astype(np.float64))
+    assert np.array_equal(dx, d["dy"].astype(np.float64))
+
+
+def test_block_rejects_other_head_sizes(ctx):
+    with pytest.raises(tt.TTError) as e:
+        tt.BlockSaved(ctx, 1, 8, 96, 2, 384, "f32")
+    assert e.value.status == -6
+
+
+# -------------------------------------------------------------- tiny MLP
+
+def test_tiny_mlp_sgd_step(ctx):
+    """Linear(3->32) -> tanh-GELU -> Linear(32->4) -> softmax -> mean CE,
+    backward, one SGD step with lr 0.1, all through the op-level ABI."""
+    d = syn.mlp_inputs(seed=1)
+    n, nin, hid, ncls = 64, 3, 32, 4
+    P = {k: dev(d[k]) for k in ("W1", "b1", "W2", "b2")}
+    x = dev(d["x"])
+    hpre, h = empty((n, hid)), empty((n, hid))
+    tt.tt_linear_fwd(ctx, "f32", n, nin, hid, x, P["W1"], P["b1"], h, tt.TT_EPI_GELU, None, hpre)
+    z = empty((n, ncls))
+    tt.tt_linear_fwd(ctx, "f32", n, hid, ncls, h, P["W2"], P["b2"], z)
+    loss = empty((1,))
+    tt.tt_ce_fwdbwd(ctx, "f32", n, ncls, ncls, z, dev(d["labels"], "i32"), loss)
+    G = {k: zeros(v.shape) for k, v in P.items()}
+    dh = empty((n, hid))
+    tt.tt_linear_bwd(ctx, "f32", n, hid, ncls, h, P["W2"], z, dh, G["W2"], G["b2"])
+    dhpre = empty((n, hid))
+    tt.tt_gelu_bwd(ctx, "f32", n * hid, hpre, dh, dhpre)
+    tt.tt_linear_bwd(ctx, "f32", n, nin, hid, x, P["W1"], dhpre, None, G["W1"], G["b1"])
+    for k in P:
+        tt.tt_sgd_step(ctx, P[k], G[k], 0.1)
+    sync()
+    W = {k: d[k].astype(np.float64) for k in ("W1", "b1", "W2", "b2")}
+    l_ref, g_ref, new_ref, _ = og.mlp_step(d["x"], W["W1"], W["b1"], W["W2"], W["b2"], d["labels"])
+    assert abs(host(loss)[0] - l_ref) / l_ref <= 1e-5
+    for k in P:
+        assert rel_l2(host(G[k]), g_ref[k]) <= 1e-5, k
+        assert rel_l2(host(P[k]), new_ref[k]) <= 1e-5, k

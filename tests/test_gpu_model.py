@@ -1,0 +1,229 @@
+"""Whole-model parity: tt_model_fwd_bwd / tt_train_step against the oracle.
+
+* small models (every path exercised, perturbed biases and LayerNorm
+  parameters): loss, every gradient and every post-AdamW weight, fp32 and
+  bf16 modes;
+* the full-size GPT-2 124M step (12 layers, C=768, V=50257, T=1024) in bf16:
+  one sequence against sampled values the oracle wrote (tests/golden), and
+  at B=8 — the configuration the benchmark times — through the batch
+  property: the B=8 loss and gradients equal the mean over the eight
+  sequences run one at a time.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gpt2 as og
+import autograd_transformer_amd as tt
+from autograd_transformer_amd import synthetic as syn
+from tests.conftest import GOLDEN, rel_l2
+from tests.gpu_util import (dev, host, empty, zeros, tol, sync, split_key_bias, KEY_BIAS_NOISE,
+                            check_post_adamw)
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1)
+
+
+def make_model(ctx, shape, B, T, mode, params, V_pad=None):
+    m = tt.Model(ctx, L=shape.n_layer, C=shape.n_embd, NH=shape.n_head, V=shape.vocab,
+                 T_max=shape.block_size, B_max=B, mode=mode, V_pad=V_pad)
+    m.load(params)
+    return m
+
+
+def grads_of(model):
+    return {k: host(model.tensor(k, "g")) for k in model.names}
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_small_model_train_step(mode):
+    shape = syn.ModelShape(n_layer=2, n_embd=128, n_head=2, vocab=97, block_size=80)
+    cfg = og.GPTConfig(n_layer=2, n_embd=128, n_head=2, vocab=97, block_size=80)
+    B, T = 3, 77
+    params = syn.gpt2_params(shape, seed=31, w_std=0.05, bias_std=0.05, ln_std=0.1)
+    tok, tgt = syn.gpt2_tokens(B, T, 97, seed=31)
+    ctx = tt.Context(arena_bytes=1 << 30)
+    model = make_model(ctx, shape, B, T, mode, params, V_pad=128)
+    loss = empty((1,))
+    tok_d, tgt_d = dev(tok, "i32"), dev(tgt, "i32")
+    tt.tt_model_fwd_bwd(ctx, model, B, T, tok_d, tgt_d, loss)
+    sync()
+    g = grads_of(model)
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    l_ref, g_ref = og.model_fwd_bwd(p64, tok, tgt, cfg, mode)
+    assert abs(host(loss)[0] - l_ref) / l_ref <= tol(mode)
+    errs, kb = {}, {}
+    for k in g_ref:
+        got = g[k][: g_ref[k].shape[0]] if k == "wte" else g[k]
+        rest, rest_ref, key = split_key_bias(k, got, g_ref[k], 128)
+        errs[k] = rel_l2(rest, rest_ref)
+        if key is not None:
+            kb[k] = np.linalg.norm(key) / np.linalg.norm(rest_ref)
+    assert np.all(g["wte"][97:] == 0)           # padding rows get no gradient
+    bad = {k: e for k, e in errs.items() if not e <= tol(mode)}
+    assert not bad, bad
+    assert max(kb.values()) <= KEY_BIAS_NOISE[mode], kb
+    # AdamW on the model's gradient buffer, t = 1
+    tt.tt_model_adamw(ctx, model, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"], 1)
+    sync()
+    for k in g_ref:
+        w_ref, _, _ = oracle.adamw_update(p64[k], g_ref[k], 0, 0, t=1, **{
+            "lr": HP["lr"], "beta1": HP["beta1"], "beta2": HP["beta2"], "eps": HP["eps"],
+            "wd": HP["wd"]})
+        got = host(model.tensor(k, "w"))
+        got = got[:97] if k == "wte" else got
+        rms = np.linalg.norm(g_ref[k]) / np.sqrt(g_ref[k].size)
+        gk = g_ref[k].copy()
+        if k.endswith("b_qkv"):
+            gk[128:256] = 0.0      # exact value of the key-bias gradient
+        check_post_adamw(got, p64[k], gk, w_ref, HP["lr"], HP["wd"], tol(mode), rms)
+    if mode == "bf16":
+        wl = host(model.tensor("h0.w_fc", "w_lowp"))
+        assert np.array_equal(wl, oracle.round_bf16(host(model.tensor("h0.w_fc", "w"))))
+    model.close()
+    ctx.close()
+
+
+def test_train_step_matches_fwd_bwd_then_adamw():
+    shape = syn.ModelShape(n_layer=1, n_embd=64, n_head=1, vocab=50, block_size=32)
+    params = syn.gpt2_params(shape, seed=32)
+    tok, tgt = syn.gpt2_tokens(2, 32, 50, seed=32)
+    ctx = tt.Context(arena_bytes=1 << 29)
+    m1 = make_model(ctx, shape, 2, 32, "bf16", params, V_pad=64)
+    m2 = make_model(ctx, shape, 2, 32, "bf16", params, V_pad=64)
+    l1, l2 = empty((1,)), empty((1,))
+    flag = zeros((1,), "i32")
+    tok_d, tgt_d = dev(tok, "i32"), dev(tgt, "i32")
+    tt.tt_train_step(ctx, m1, 2, 32, tok_d, tgt_d, 3e-4, 0.9, 0.95, 1e-8, 0.1, 1, l1, flag)
+    tt.tt_model_fwd_bwd(ctx, m2, 2, 32, tok_d, tgt_d, l2)
+    tt.tt_model_adamw(ctx, m2, 3e-4, 0.9, 0.95, 1e-8, 0.1, 1)
+    sync()
+    assert host(l1)[0] == host(l2)[0]
+    assert host(flag)[0] == 0
+    for k in m1.names:
+        assert rel_l2(host(m1.tensor(k)), host(m2.tensor(k))) <= 1e-6, k
+    m1.close(); m2.close(); ctx.close()
+
+
+def test_nonfinite_flag_and_target_range():
+    shape = syn.ModelShape(n_layer=1, n_embd=64, n_head=1, vocab=50, block_size=16)
+    params = syn.gpt2_params(shape, seed=33)
+    params["h0.b_fc"][3] = np.nan
+    ctx = tt.Context(arena_bytes=1 << 29)
+    m = make_model(ctx, shape, 1, 16, "f32", params)
+    tok, tgt = syn.gpt2_tokens(1, 16, 50, seed=33)
+    loss, flag = empty((1,)), zeros((1,), "i32")
+    tt.tt_train_step(ctx, m, 1, 16, dev(tok, "i32"), dev(tgt, "i32"), 3e-4, 0.9, 0.95, 1e-8,
+                     0.1, 1, loss, flag)
+    ctx.sync()
+    assert host(flag)[0] == 1 and not np.isfinite(host(loss)[0])
+    bad = tgt.copy()
+    bad[0, 3] = 50
+    tt.tt_model_fwd_bwd(ctx, m, 1, 16, dev(tok, "i32"), dev(bad, "i32"), loss)
+    with pytest.raises(tt.TTError) as e:
+        ctx.sync()
+    assert e.value.status == -7
+    m.close(); ctx.close()
+
+
+def test_model_rejects_bad_configs():
+    ctx = tt.Context(arena_bytes=1 << 26)
+    with pytest.raises(tt.TTError) as e:       # arena too small
+        tt.Model(ctx, L=12, C=768, NH=12, V=50257, T_max=1024, B_max=8, mode="bf16")
+    assert e.value.status == -2
+    with pytest.raises(tt.TTError) as e:       # head size 48
+        tt.Model(ctx, L=1, C=96, NH=2, V=10, T_max=8, B_max=1, mode="f32")
+    assert e.value.status == -6
+    ctx.close()
+
+
+# ------------------------------------------------------------ full size
+
+@pytest.fixture(scope="module")
+def gpt2_124m():
+    params = syn.gpt2_params(syn.GPT2_124M, seed=3)
+    ctx = tt.Context(arena_bytes=24 << 30)
+    model = make_model(ctx, syn.GPT2_124M, 8, 1024, "bf16", params, V_pad=50304)
+    yield ctx, model, params
+    model.close()
+    ctx.close()
+
+
+def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
+    ctx, model, _ = gpt2_124m
+    with open(os.path.join(GOLDEN, "gpt2_124m_step_b1_t1024_bf16.json")) as f:
+        ref = json.load(f)
+    tok, tgt = syn.gpt2_tokens(1, 1024, seed=3)
+    loss = empty((1,))
+    tt.tt_model_fwd_bwd(ctx, model, 1, 1024, dev(tok, "i32"), dev(tgt, "i32"), loss)
+    sync()
+    assert abs(host(loss)[0] - ref["loss"]) / ref["loss"] <= 2e-2
+    g_all, norm_err, samp_err = {}, {}, {}
+    C = 768
+    for name, r in ref["tensors"].items():
+        g = host(model.tensor(name, "g")).reshape(-1)
+        g_all[name] = g
+        idx = np.array(r["idx"])
+        if name.endswith("b_qkv"):
+            # exclude the key third (exact gradient 0, see split_key_bias)
+            keep = (idx < C) | (idx >= 2 * C)
+            rest = np.r_[0:C, 2 * C:3 * C]
+            norm_err[name] = abs(np.linalg.norm(g[rest]) - r["grad_norm"]) / r["grad_norm"]
+            samp_err[name] = rel_l2(g[idx[keep]], np.array(r["grad"])[keep])
+            assert np.linalg.norm(g[C:2 * C]) <= KEY_BIAS_NOISE["bf16"] * r["grad_norm"]
+            continue
+        norm_err[name] = abs(np.linalg.norm(g) - r["grad_norm"]) / max(r["grad_norm"], 1e-30)
+        samp_err[name] = rel_l2(g[idx], r["grad"])
+    bad = {k: (norm_err[k], samp_err[k]) for k in ref["tensors"]
+           if not (norm_err[k] <= 2e-2 and samp_err[k] <= 2e-2)}
+    assert not bad, bad
+    tt.tt_model_adamw(ctx, model, ref["workload"]["lr"], ref["workload"]["beta1"],
+                      ref["workload"]["beta2"], ref["workload"]["eps"], ref["workload"]["wd"], 1)
+    sync()
+    w_err = {}
+    lr, wd = ref["workload"]["lr"], ref["workload"]["wd"]
+    params = syn.gpt2_params(syn.GPT2_124M, seed=3)
+    for name, r in ref["tensors"].items():
+        idx = np.array(r["idx"])
+        w = host(model.tensor(name, "w")).reshape(-1)[idx]
+        w0 = params[name].reshape(-1)[idx]
+        g = np.array(r["grad"])
+        if name.endswith("b_qkv"):
+            g[(idx >= C) & (idx < 2 * C)] = 0.0   # exact key-bias gradient
+        rms = r["grad_norm"] / np.sqrt(params[name].size)
+        w_err[name] = check_post_adamw(w, w0, g, r["w_new"], lr, wd, 2e-2, rms)
+    print(f"loss {host(loss)[0]:.6f} vs {ref['loss']:.6f}; max grad-norm err "
+          f"{max(norm_err.values()):.2e}; max sampled-grad err {max(samp_err.values()):.2e}")
+
+
+def test_gpt2_124m_batch_of_8_is_mean_of_sequences(gpt2_124m):
+    """At B=8, T=1024 (the benchmarked step) the loss and every gradient are the
+    mean of the eight single-sequence results — a property of the mean loss
+    that holds at any size."""
+    ctx, model, params = gpt2_124m
+    model.load(params)
+    tok, tgt = syn.gpt2_tokens(8, 1024, seed=41)
+    loss = empty((1,))
+    tt.tt_model_fwd_bwd(ctx, model, 8, 1024, dev(tok, "i32"), dev(tgt, "i32"), loss)
+    sync()
+    l8 = host(loss)[0]
+    g8 = {k: host(model.tensor(k, "g")) for k in model.names}
+    acc = {k: np.zeros_like(v) for k, v in g8.items()}
+    lsum = 0.0
+    for b in range(8):
+        tt.tt_model_fwd_bwd(ctx, model, 1, 1024, dev(tok[b:b + 1], "i32"),
+                            dev(tgt[b:b + 1], "i32"), loss)
+        sync()
+        lsum += host(loss)[0]
+        for k in acc:
+            acc[k] += host(model.tensor(k, "g"))
+    assert abs(l8 - lsum / 8) / l8 <= 1e-5
+    errs = {k: rel_l2(g8[k], acc[k] / 8) for k in acc}
+    bad = {k: e for k, e in errs.items() if not e <= 1e-3}
+    assert not bad, bad
+    assert abs(l8 - (np.log(50257) + 0.02 ** 2 * 768 / 2)) < 0.1
