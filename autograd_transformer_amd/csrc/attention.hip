@@ -525,12 +525,15 @@ int attn_bwd_t(tt_ctx *ctx, int B, int T_, int NH, const void *qkv, const void *
 
 int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv, void *out,
                      float *lse) {
+  if (mode == TT_BF16 && tt_attn_bf16_ok(B, T, NH)) return tt_attn_fwd_bf16(ctx, B, T, NH, qkv, out, lse);
   if (mode == TT_BF16) return attn_fwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse);
   return attn_fwd_t<float>(ctx, B, T, NH, qkv, out, lse);
 }
 
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      const void *out, const float *lse, const void *dout, void *dqkv, float *Dv) {
+  if (mode == TT_BF16 && tt_attn_bf16_ok(B, T, NH))
+    return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
   if (mode == TT_BF16) return attn_bwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
   return attn_bwd_t<float>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
 }

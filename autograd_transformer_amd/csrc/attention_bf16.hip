@@ -1,0 +1,454 @@
+// Causal attention in bf16 on gfx950: forward, dK/dV and dQ kernels.
+//
+// Same mathematics and the same transposed-product layout trick as the
+// generic kernels (attention.hip); what differs is the data movement:
+//  * 64-token tiles of K/V (forward, dQ) or Q/dO (dK/dV) stay in LDS in their
+//    natural [token][head dim] layout, double-buffered: the next tile is
+//    fetched into registers with buffer loads (rows past T get an
+//    out-of-range offset and read zero, no branches) while the current one
+//    is used, so one barrier per tile suffices;
+//  * a product that reduces over the token index reads its A operand
+//    "transposed" with ds_read_b64_tr_b16 (lane s of a 16-lane group points
+//    at 4 elements of token row t0 + s/4, columns c0 + 4(s%4); lane j then
+//    holds column c0 + j of rows t0 .. t0+3), in the permuted slot order of
+//    the accumulator it is multiplied with (rows 4g..4g+3 and 16+4g..+3);
+//  * probabilities and dS are packed to bf16 with v_cvt_pk_bf16_f32.
+#include "tt_internal.h"
+
+namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+constexpr int HS = 64;
+constexpr int LDT = HS + 8;            // LDS row: 144 bytes
+constexpr uint32_t OOB = 0x7ffffff0u;  // buffer offset past every tensor (host checks sizes)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float SL2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) folded into exp2
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ bf16x8_t as_frag(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ bf16x8_t pack8(f32x4_t a, f32x4_t b) {
+  return as_frag(make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]),
+                            pack_bf2(b[2], b[3])));
+}
+
+// k-major fragment: token row rb + lane%16, head dims kk + 8*(lane/16) .. +7.
+__device__ __forceinline__ bf16x8_t row_frag(const bf16_t *tile, int rb, int kk, int lr, int lg) {
+  return *(const bf16x8_t *)(tile + (rb + lr) * LDT + kk + 8 * lg);
+}
+
+// Transposed fragment: column (head dim) cb + lane%16, slots 0..3 = token rows
+// rbase + 4g + i, slots 4..7 = rows rbase + 16 + 4g + i (g = lane/16).
+__device__ __forceinline__ bf16x8_t tr_frag(const bf16_t *tile, int rbase, int cb, int lr, int lg) {
+  const bf16_t *p0 = tile + (rbase + 4 * lg + (lr >> 2)) * LDT + cb + 4 * (lr & 3);
+  v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p0);
+  v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p0 + 16 * LDT));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 64 x 64 tile (token rows t0.., head columns col..col+63 of a [.., ld]
+// tensor), 2 vectors per thread of a 256-thread block.
+struct TileRegs {
+  uint4 v[2];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, size_t row0, int t0, int T, int ld,
+                                       int col, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + i * 256, row = u >> 3, ch = u & 7;
+      const int t = t0 + row;
+      v[i] = bload(r, t < T ? (uint32_t)(((row0 + t) * ld + col + ch * 8) * 2) : OOB);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t *tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + i * 256;
+      *(uint4 *)(tile + (u >> 3) * LDT + (u & 7) * 8) = v[i];
+    }
+  }
+};
+
+// ------------------------------------------------------------------ forward
+// 4 waves x 32 queries; K/V tiles of 64 keys; Sᵀ = K Qᵀ, Oᵀ += Vᵀ Pᵀ.
+__global__ void __launch_bounds__(256, 2)
+attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out,
+                     float *__restrict__ lse, int nqb, uint32_t qkv_bytes) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][64 * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int qb = nqb - 1 - (blockIdx.x % nqb);   // heavy query blocks first
+  const int bh = blockIdx.x / nqb, b = bh / NH, h = bh % NH;
+  const int C = NH * HS, ld = 3 * C;
+  const size_t row0 = (size_t)b * T;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(qkv, qkv_bytes);
+
+  const int q0 = qb * 128 + wave * 32;
+  bf16x8_t qf[2][2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int t = q0 + qs * 16 + lr;
+      qf[qs][st] = as_frag(bload(rs, t < T ? (uint32_t)(((row0 + t) * ld + h * HS + st * 32 + lg * 8) * 2) : OOB));
+    }
+  f32x4_t o[4][2];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) o[d][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+
+  const int kend = min(T, qb * 128 + 128);
+  const int nkb = (kend + 63) / 64;
+  TileRegs kr, vr;
+  kr.load(rs, row0, 0, T, ld, C + h * HS, tid);
+  vr.load(rs, row0, 0, T, ld, 2 * C + h * HS, tid);
+  kr.store(Ks[0], tid);
+  vr.store(Vs[0], tid);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const int k0 = kb * 64;
+    if (kb + 1 < nkb) {
+      kr.load(rs, row0, k0 + 64, T, ld, C + h * HS, tid);
+      vr.load(rs, row0, k0 + 64, T, ld, 2 * C + h * HS, tid);
+    }
+    if (k0 <= q0 + 31 && q0 < T) {
+      const bf16_t *ks = Ks[cur], *vs = Vs[cur];
+      f32x4_t s[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t k_0 = row_frag(ks, j * 16, 0, lr, lg), k_1 = row_frag(ks, j * 16, 32, lr, lg);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          s[j][qs] = mfma(k_1, qf[qs][1], mfma(k_0, qf[qs][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      }
+      const bool diag = k0 + 64 > q0;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int q = q0 + qs * 16 + lr;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + j * 16 + lg * 4 + r;
+            float v = s[j][qs][r];
+            if (diag && (key > q || key >= T)) v = -INFINITY;
+            s[j][qs][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrow[qs], mx * SL2);
+        const float alpha = exp2f(mrow[qs] - mnew);
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = exp2f(fmaf(s[j][qs][r], SL2, -mnew));
+            s[j][qs][r] = p;
+            ps += p;
+          }
+        lrow[qs] = lrow[qs] * alpha + ps;
+        mrow[qs] = mnew;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[d][qs][r] *= alpha;
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) pb[qs] = pack8(s[2 * t2][qs], s[2 * t2 + 1][qs]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8_t va = tr_frag(vs, t2 * 32, d * 16, lr, lg);
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) o[d][qs] = mfma(va, pb[qs], o[d][qs]);
+        }
+      }
+    }
+    if (kb + 1 < nkb) {
+      kr.store(Ks[cur ^ 1], tid);
+      vr.store(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    float l = lrow[qs];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int q = q0 + qs * 16 + lr;
+    if (q >= T) continue;
+    const float inv = 1.0f / l;
+    bf16_t *orow = out + (row0 + q) * C + h * HS;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      *(uint2 *)(orow + d * 16 + lg * 4) =
+          make_uint2(pack_bf2(o[d][qs][0] * inv, o[d][qs][1] * inv),
+                     pack_bf2(o[d][qs][2] * inv, o[d][qs][3] * inv));
+    if (lg == 0) lse[((size_t)b * NH + h) * T + q] = (mrow[qs] + log2f(l)) / LOG2E;
+  }
+}
+
+// ---------------------------------------------------------------- dK / dV
+// Workgroup: 64 keys (4 waves x 16) walking 64-query blocks from the
+// diagonal.  Rows = queries: S = Q Kᵀ, dP = dO Vᵀ, P = exp(S/8 - lse),
+// dS = P (dP - Dv); dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (reductions over queries).
+__global__ void __launch_bounds__(256, 2)
+attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
+                      const float *__restrict__ lse, const float *__restrict__ Dv,
+                      bf16_t *__restrict__ dqkv, int nkb, uint32_t qkv_bytes, uint32_t do_bytes) {
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][64 * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t Os[2][64 * LDT];
+  __shared__ float ls[2][64], ds[2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int kb = blockIdx.x % nkb;
+  const int bh = blockIdx.x / nkb, b = bh / NH, h = bh % NH;
+  const int C = NH * HS, ld = 3 * C;
+  const size_t row0 = (size_t)b * T;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes);
+  const float *lseg = lse + ((size_t)b * NH + h) * T;
+  const float *Dg = Dv + ((size_t)b * NH + h) * T;
+
+  const int key = kb * 64 + wave * 16 + lr;   // this lane's key column
+  bf16x8_t kf[2], vf[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const bool ok = key < T;
+    kf[st] = as_frag(bload(rq, ok ? (uint32_t)(((row0 + key) * ld + C + h * HS + st * 32 + lg * 8) * 2) : OOB));
+    vf[st] = as_frag(bload(rq, ok ? (uint32_t)(((row0 + key) * ld + 2 * C + h * HS + st * 32 + lg * 8) * 2) : OOB));
+  }
+  f32x4_t dk[4], dv[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    dk[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dv[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nqb = (T + 63) / 64;
+  TileRegs qr, orr;
+  float lv = 0.f, dvv = 0.f;
+  auto fetch = [&](int q0) {
+    qr.load(rq, row0, q0, T, ld, h * HS, tid);
+    orr.load(ro, row0, q0, T, C, h * HS, tid);
+    if (tid < 64) {
+      const int q = q0 + tid;
+      lv = q < T ? lseg[q] * LOG2E : INFINITY;
+      dvv = q < T ? Dg[q] : 0.f;
+    }
+  };
+  auto put = [&](int buf) {
+    qr.store(Qs[buf], tid);
+    orr.store(Os[buf], tid);
+    if (tid < 64) {
+      ls[buf][tid] = lv;
+      ds[buf][tid] = dvv;
+    }
+  };
+  fetch(kb * 64);
+  put(0);
+  __syncthreads();
+  for (int qb = kb; qb < nqb; ++qb) {
+    const int cur = (qb - kb) & 1;
+    const int q0 = qb * 64;
+    if (qb + 1 < nqb) fetch(q0 + 64);
+    const bf16_t *qs_t = Qs[cur], *os_t = Os[cur];
+    f32x4_t p[4], dsv[4];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      const bf16x8_t a0 = row_frag(qs_t, qs * 16, 0, lr, lg), a1 = row_frag(qs_t, qs * 16, 32, lr, lg);
+      const bf16x8_t o0 = row_frag(os_t, qs * 16, 0, lr, lg), o1 = row_frag(os_t, qs * 16, 32, lr, lg);
+      const f32x4_t sacc = mfma(a1, kf[1], mfma(a0, kf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      const f32x4_t dpacc = mfma(o1, vf[1], mfma(o0, vf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ql = qs * 16 + lg * 4 + r;
+        const int q = q0 + ql;
+        const float pv = (key > q || key >= T) ? 0.f : exp2f(fmaf(sacc[r], SL2, -ls[cur][ql]));
+        p[qs][r] = pv;
+        dsv[qs][r] = pv * (dpacc[r] - ds[cur][ql]);
+      }
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const bf16x8_t pb = pack8(p[2 * t2], p[2 * t2 + 1]);
+      const bf16x8_t sb = pack8(dsv[2 * t2], dsv[2 * t2 + 1]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        dv[d] = mfma(tr_frag(os_t, t2 * 32, d * 16, lr, lg), pb, dv[d]);
+        dk[d] = mfma(tr_frag(qs_t, t2 * 32, d * 16, lr, lg), sb, dk[d]);
+      }
+    }
+    if (qb + 1 < nqb) put(cur ^ 1);
+    __syncthreads();
+  }
+  if (key >= T) return;
+  bf16_t *drow = dqkv + (row0 + key) * ld + h * HS;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int dd = d * 16 + lg * 4;
+    *(uint2 *)(drow + C + dd) = make_uint2(pack_bf2(dk[d][0] * 0.125f, dk[d][1] * 0.125f),
+                                           pack_bf2(dk[d][2] * 0.125f, dk[d][3] * 0.125f));
+    *(uint2 *)(drow + 2 * C + dd) =
+        make_uint2(pack_bf2(dv[d][0], dv[d][1]), pack_bf2(dv[d][2], dv[d][3]));
+  }
+}
+
+// -------------------------------------------------------------------- dQ
+// Workgroup: 64 queries (4 waves x 16) walking key blocks up to the diagonal.
+// Rows = keys: Sᵀ = K Qᵀ, dPᵀ = V dOᵀ, dSᵀ = Pᵀ (dPᵀ - Dv); dQᵀ += Kᵀ dSᵀ.
+__global__ void __launch_bounds__(256, 2)
+attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
+                    const float *__restrict__ lse, const float *__restrict__ Dv,
+                    bf16_t *__restrict__ dqkv, int nqb, uint32_t qkv_bytes, uint32_t do_bytes) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][64 * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int qb = nqb - 1 - (blockIdx.x % nqb);
+  const int bh = blockIdx.x / nqb, b = bh / NH, h = bh % NH;
+  const int C = NH * HS, ld = 3 * C;
+  const size_t row0 = (size_t)b * T;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes);
+
+  const int q = qb * 64 + wave * 16 + lr;   // this lane's query column
+  bf16x8_t qf[2], of[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const bool ok = q < T;
+    qf[st] = as_frag(bload(rq, ok ? (uint32_t)(((row0 + q) * ld + h * HS + st * 32 + lg * 8) * 2) : OOB));
+    of[st] = as_frag(bload(ro, ok ? (uint32_t)(((row0 + q) * C + h * HS + st * 32 + lg * 8) * 2) : OOB));
+  }
+  const float lq = q < T ? lse[((size_t)b * NH + h) * T + q] * LOG2E : 0.f;
+  const float Dq = q < T ? Dv[((size_t)b * NH + h) * T + q] : 0.f;
+  f32x4_t dq[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dq[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int kend = min(T, qb * 64 + 64);
+  const int nkb = (kend + 63) / 64;
+  const int qw0 = qb * 64 + wave * 16;
+  TileRegs kr, vr;
+  kr.load(rq, row0, 0, T, ld, C + h * HS, tid);
+  vr.load(rq, row0, 0, T, ld, 2 * C + h * HS, tid);
+  kr.store(Ks[0], tid);
+  vr.store(Vs[0], tid);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const int k0 = kb * 64;
+    if (kb + 1 < nkb) {
+      kr.load(rq, row0, k0 + 64, T, ld, C + h * HS, tid);
+      vr.load(rq, row0, k0 + 64, T, ld, 2 * C + h * HS, tid);
+    }
+    if (k0 <= qw0 + 15) {
+      const bf16_t *ks = Ks[cur], *vs = Vs[cur];
+      f32x4_t dsv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t sacc = mfma(row_frag(ks, j * 16, 32, lr, lg), qf[1],
+                                  mfma(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t dpacc = mfma(row_frag(vs, j * 16, 32, lr, lg), of[1],
+                                   mfma(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + j * 16 + lg * 4 + r;
+          const float pv = (key > q || key >= T || q >= T) ? 0.f : exp2f(fmaf(sacc[r], SL2, -lq));
+          dsv[j][r] = pv * (dpacc[r] - Dq);
+        }
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8_t sb = pack8(dsv[2 * t2], dsv[2 * t2 + 1]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) dq[d] = mfma(tr_frag(ks, t2 * 32, d * 16, lr, lg), sb, dq[d]);
+      }
+    }
+    if (kb + 1 < nkb) {
+      kr.store(Ks[cur ^ 1], tid);
+      vr.store(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  if (q >= T) return;
+  bf16_t *drow = dqkv + (row0 + q) * ld + h * HS;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    *(uint2 *)(drow + d * 16 + lg * 4) =
+        make_uint2(pack_bf2(dq[d][0] * 0.125f, dq[d][1] * 0.125f),
+                   pack_bf2(dq[d][2] * 0.125f, dq[d][3] * 0.125f));
+}
+
+// Dv[b,h,t] = sum_d dO[t, h*64+d] * O[t, h*64+d]: one wave per (token, 4
+// heads), 16 lanes per head, 4 elements per lane.
+__global__ void __launch_bounds__(256) attn_dot_bf16_kernel(int BT, int T, int NH,
+                                                            const bf16_t *__restrict__ o,
+                                                            const bf16_t *__restrict__ dO,
+                                                            float *__restrict__ Dv) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int seg = gid >> 4;           // (token, head) pair
+  const int l16 = threadIdx.x & 15;
+  const bool ok = seg < BT * NH;
+  float s = 0.f;
+  const int row = ok ? seg / NH : 0, h = ok ? seg % NH : 0;
+  if (ok) {
+    const size_t off = (size_t)row * NH * HS + h * HS + l16 * 4;
+    const uint2 a = *(const uint2 *)(o + off), c = *(const uint2 *)(dO + off);
+    s = bf2f(a.x & 0xffffu) * bf2f(c.x & 0xffffu) + bf2f(a.x >> 16) * bf2f(c.x >> 16) +
+        bf2f(a.y & 0xffffu) * bf2f(c.y & 0xffffu) + bf2f(a.y >> 16) * bf2f(c.y >> 16);
+  }
+#pragma unroll
+  for (int w = 8; w > 0; w >>= 1) s += __shfl_xor(s, w, 64);
+  if (ok && l16 == 0) Dv[((size_t)(row / T) * NH + h) * T + row % T] = s;
+}
+
+}  // namespace
+
+bool tt_attn_bf16_ok(int B, int T, int NH) {
+  const size_t qkv = (size_t)B * T * 3 * NH * HS * 2;
+  return qkv < OOB;
+}
+
+int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse) {
+  const int nqb = (T + 127) / 128;
+  const uint32_t qb = (uint32_t)((size_t)B * T * 3 * NH * HS * 2);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(B * NH * nqb), dim3(256), 0, ctx->stream, T, NH,
+                     (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
+  return tt_check_launch(ctx, "attn_fwd_bf16");
+}
+
+int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
+                     const float *lse, const void *dout, void *dqkv, float *Dv) {
+  const int BT = B * T;
+  const uint32_t qb = (uint32_t)((size_t)BT * 3 * NH * HS * 2);
+  const uint32_t ob = (uint32_t)((size_t)BT * NH * HS * 2);
+  hipLaunchKernelGGL(attn_dot_bf16_kernel, dim3((BT * NH * 16 + 255) / 256), dim3(256), 0,
+                     ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
+  TT_TRY(tt_check_launch(ctx, "attn_dot_bf16"));
+  const int nb = (T + 63) / 64;
+  hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
+                     (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
+  TT_TRY(tt_check_launch(ctx, "attn_dkdv_bf16"));
+  hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
+                     (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
+  return tt_check_launch(ctx, "attn_dq_bf16");
+}

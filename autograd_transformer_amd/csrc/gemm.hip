@@ -17,9 +17,11 @@
 // MFMA fragment layout used (16x16 blocks, wave64): lane l holds row l%16 of
 // A and column l%16 of B for the k slots of lane group l/16; the accumulator
 // holds D[4*(l/16)+r][l%16], r = 0..3.
-#include "tt_internal.h"
+#include "gemm_common.h"
 
 namespace {
+
+using namespace tt_gemm_detail;
 
 template <typename T> struct MfmaTraits;
 template <> struct MfmaTraits<bf16_t> {
@@ -39,21 +41,6 @@ template <> struct MfmaTraits<float> {
   __device__ __forceinline__ static f32x4_t mfma(frag_t a, frag_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-};
-
-struct GemmParams {
-  const void *A; int lda;
-  const void *B; int ldb;
-  int M, N, K;
-  int k_chunk;   // K range per split (multiple of BK)
-  int epi;
-  void *out; int ldo; int out_bf16;
-  const float *bias;
-  const float *resid; int ldr;
-  void *aux; int ldx;
-  int n_valid;
-  int tiles_m, tiles_n;
-  int vec_out;   // output/aux/resid rows allow 4-wide vector access
 };
 
 // Tile shape: BM x BN block, BK deep, WM x WN waves.
@@ -235,94 +222,6 @@ struct TileLoader {
   }
 };
 
-__device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
-  if (out_bf16)
-    ((bf16_t *)out)[(size_t)m * ldo + n] = f2bf(v);
-  else
-    ((float *)out)[(size_t)m * ldo + n] = v;
-}
-
-// Epilogue for 4 consecutive columns n..n+3 of row m (only the first `cnt`
-// of them exist when the tile sticks out of the matrix).  Vector accesses
-// need 16-byte (f32) / 8-byte (bf16) aligned rows, which the host checks
-// (p.vec_out); otherwise elements are handled one by one.
-__device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
-  const bool full = cnt >= 4 && p.vec_out;
-  float a[4] = {v.x, v.y, v.z, v.w};
-  const int lim = cnt < 4 ? cnt : 4;
-  switch (p.epi) {
-    case EPI_STORE:
-    case EPI_GELU: {
-      if (p.epi == EPI_GELU) {
-        if (p.aux) {
-          if (full && p.out_bf16)
-            *(uint2 *)((bf16_t *)p.aux + (size_t)m * p.ldx + n) =
-                make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
-          else
-            for (int q = 0; q < lim; ++q) store_out(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = gelu_f(a[q]);
-      }
-      if (full) {
-        if (p.out_bf16)
-          *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-              make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
-        else
-          *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) = make_float4(a[0], a[1], a[2], a[3]);
-      } else {
-        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
-      }
-      break;
-    }
-    case EPI_RESID: {
-      const float *rp = p.resid + (size_t)m * p.ldr + n;
-      float *op = (float *)p.out + (size_t)m * p.ldo + n;
-      if (full) {
-        float4 r = *(const float4 *)rp;
-        *(float4 *)op = make_float4(r.x + a[0], r.y + a[1], r.z + a[2], r.w + a[3]);
-      } else {
-        for (int q = 0; q < lim; ++q) op[q] = rp[q] + a[q];
-      }
-      break;
-    }
-    case EPI_GELU_BWD: {
-      float h[4];
-      if (p.out_bf16) {
-        const bf16_t *hp = (const bf16_t *)p.aux + (size_t)m * p.ldx + n;
-        if (full) {
-          uint2 u = *(const uint2 *)hp;
-          h[0] = __uint_as_float(u.x << 16); h[1] = __uint_as_float(u.x & 0xffff0000u);
-          h[2] = __uint_as_float(u.y << 16); h[3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-          for (int q = 0; q < 4; ++q) h[q] = q < lim ? bf2f(hp[q]) : 0.f;
-        }
-      } else {
-        const float *hp = (const float *)p.aux + (size_t)m * p.ldx + n;
-        for (int q = 0; q < 4; ++q) h[q] = q < lim ? hp[q] : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a[q] *= gelu_grad_f(h[q]);
-      if (full && p.out_bf16)
-        *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-            make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
-      else
-        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
-      break;
-    }
-    case EPI_ACCUM: {
-      float *op = (float *)p.out + (size_t)m * p.ldo + n;
-      for (int q = 0; q < lim; ++q) unsafeAtomicAdd(op + q, a[q]);
-      break;
-    }
-    case EPI_STORE_ACC: {
-      float *op = (float *)p.out + (size_t)m * p.ldo + n;
-      for (int q = 0; q < lim; ++q) op[q] += a[q];
-      break;
-    }
-  }
-}
-
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool A_KM, bool B_KM, bool VECLD>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(GemmParams p) {
@@ -447,15 +346,7 @@ int launch_gemm(tt_ctx *ctx, const GemmArgs &g, int split) {
   p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
   p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
   p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
-  {
-    const int oes = g.out_bf16 ? 2 : 4;   // bytes per output element (aux has the same)
-    bool ok = ((uintptr_t)g.out % (4 * oes) == 0) && (g.ldo % 4 == 0);
-    if (g.aux) ok = ok && ((uintptr_t)g.aux % (4 * oes) == 0) && (g.ldx % 4 == 0);
-    if (g.resid) ok = ok && ((uintptr_t)g.resid % 16 == 0) && (g.ldr % 4 == 0);
-    if (g.epi == EPI_RESID || g.epi == EPI_ACCUM || g.epi == EPI_STORE_ACC)
-      ok = ok && ((uintptr_t)g.out % 16 == 0);
-    p.vec_out = ok ? 1 : 0;
-  }
+  p.vec_out = gemm_vec_out(g) ? 1 : 0;
   p.tiles_m = (g.M + BM - 1) / BM;
   p.tiles_n = (g.N + BN - 1) / BN;
   int kb = (g.K + BK - 1) / BK;
@@ -499,6 +390,7 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
     while (tiles * split < 512 && split * 2 <= kb / 4) split *= 2;
     if (g.split_k > 0) split = g.split_k;
   }
+  if (mode == TT_BF16 && vec && tt_gemm_bf16_ok(g)) return tt_gemm_bf16(ctx, g);
   if (mode == TT_BF16) return dispatch_layout<bf16_t, 128, 128, 64, 2, 2>(ctx, g, split, vec);
   return dispatch_layout<float, 128, 128, 32, 2, 2>(ctx, g, split, vec);
 }

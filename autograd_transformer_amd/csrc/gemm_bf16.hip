@@ -1,0 +1,344 @@
+// bf16 MFMA GEMM for gfx950 (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// C[m,n] = sum_k A(m,k) B(k,n): the linear layer's forward and its two
+// backward products (tinytorch page, §3 item 3).  Both operands are copied to
+// LDS in their natural global layout with 16-byte loads, double-buffered.
+// An MFMA lane needs 8 consecutive k values of one row of A / column of B:
+//  * if the operand is k-contiguous ("k-major") the fragment is one 16-byte
+//    LDS read;
+//  * otherwise (the weight-gradient products reduce over the token index,
+//    which is the row index of both operands) the fragment is assembled with
+//    two ds_read_b64_tr_b16: within each 16-lane group, lane s points at 4
+//    consecutive elements of row k0 + s/4, columns c0 + 4(s%4) .. +3, and
+//    lane j then receives column c0 + j of rows k0 .. k0+3.
+// Tile BM x BN x 64 per workgroup, WM x WN waves each owning a
+// (BM/WM) x (BN/WN) block of 16x16 accumulator tiles.
+#include <algorithm>
+
+#include "gemm_common.h"
+
+namespace {
+
+using namespace tt_gemm_detail;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+constexpr int BK = 64;
+constexpr int KPAD = 8;    // k-major rows: 72 elements (144 B) apart
+constexpr int RPAD = 16;   // row-major rows: ROWS + 16 elements (shift of 32 B per row)
+constexpr uint32_t OOB = 0x7ffffff0u;  // buffer offset past every operand (host: extent < 2 GB)
+
+template <int ROWS, bool KM>
+struct Operand {
+  static constexpr int LD = KM ? (BK + KPAD) : (ROWS + RPAD);
+  static constexpr int ELEMS = KM ? ROWS * LD : BK * LD;
+  static constexpr int UNITS = ROWS * BK / 8;     // 16-byte vectors per tile
+
+  // Global -> registers with buffer loads: the hardware returns zeros for
+  // offsets at or past num_records, so an out-of-range vector is given the
+  // offset OOB and no branch is needed.  Unit u covers 8 consecutive elements
+  // along the contiguous dimension; consecutive lanes take consecutive units.
+  // Rows past the matrix (m >= M, n >= N) only feed outputs that are not
+  // stored; k >= K must read zero in at least one operand, which the host
+  // guarantees (K % 8 == 0, or a row-major operand whose k rows are masked).
+  template <int NT>
+  __device__ __forceinline__ static void load(uint4 *reg, __amdgpu_buffer_rsrc_t rs, int ld, int r0,
+                                              int k0, int R, int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < UNITS / NT; ++i) {
+      const int u = tid + i * NT;
+      uint32_t off;
+      if constexpr (KM) {
+        const int r = r0 + u / (BK / 8), k = k0 + (u % (BK / 8)) * 8;
+        off = (r < R && k < K) ? (uint32_t)(((size_t)r * ld + k) * 2) : OOB;
+      } else {
+        const int k = k0 + u / (ROWS / 8), r = r0 + (u % (ROWS / 8)) * 8;
+        off = (k < K && r < R) ? (uint32_t)(((size_t)k * ld + r) * 2) : OOB;
+      }
+      reg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  }
+
+  template <int NT>
+  __device__ __forceinline__ static void store(bf16_t *s, const uint4 *reg, int tid) {
+#pragma unroll
+    for (int i = 0; i < UNITS / NT; ++i) {
+      const int u = tid + i * NT;
+      if constexpr (KM) {
+        const int r = u / (BK / 8), k = (u % (BK / 8)) * 8;
+        *(uint4 *)(s + r * LD + k) = reg[i];
+      } else {
+        const int k = u / (ROWS / 8), r = (u % (ROWS / 8)) * 8;
+        *(uint4 *)(s + k * LD + r) = reg[i];
+      }
+    }
+  }
+
+  // MFMA fragment: rows rb .. rb+15 (lane%16), k = kk + 8*(lane/16) .. +7.
+  __device__ __forceinline__ static bf16x8_t frag(const bf16_t *s, int rb, int kk, int lr, int lg) {
+    if constexpr (KM) {
+      return *(const bf16x8_t *)(s + (rb + lr) * LD + kk + 8 * lg);
+    } else {
+      const int kr = kk + 8 * lg + (lr >> 2);
+      const int c = rb + 4 * (lr & 3);
+      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(s + kr * LD + c));
+      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(s + (kr + 4) * LD + c));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      v8s r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, r);
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN, bool A_KM, bool B_KM>
+struct Cfg {
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  using OA = Operand<BM, A_KM>;
+  using OB = Operand<BN, B_KM>;
+  static constexpr int STAGE = OA::ELEMS + OB::ELEMS;            // bf16 elements
+  static constexpr int OPER_BYTES = 2 * STAGE * 2;
+  static constexpr int LDC = BN + 4;
+  static constexpr int EPI_BYTES = WTM * LDC * 4;                 // one wave-row of C, fp32
+  static constexpr int SMEM = OPER_BYTES > EPI_BYTES ? OPER_BYTES : EPI_BYTES;
+  static_assert(OA::UNITS % NT == 0 && OB::UNITS % NT == 0, "tile not divisible by threads");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+};
+
+// Occupancy target: two waves per SIMD (two 4-wave or one 8-wave workgroup
+// per CU), which caps registers at 256 per lane.
+template <int BM, int BN, int WM, int WN, bool A_KM, bool B_KM>
+__global__ void __launch_bounds__(64 * WM * WN, (WM * WN == 4) ? 2 : 1)
+gemm_bf16_kernel(GemmParams p) {
+  using C = Cfg<BM, BN, WM, WN, A_KM, B_KM>;
+  using OA = typename C::OA;
+  using OB = typename C::OB;
+  constexpr int NT = C::NT, FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
+  bf16_t *smem = (bf16_t *)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lg = lane >> 4;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+  // Two register sets: the loads for stage it+2 are issued while stage it is
+  // computed from LDS and stage it+1 waits in the other set.
+  uint4 ra0[OA::UNITS / NT], rb0[OB::UNITS / NT], ra1[OA::UNITS / NT], rb1[OB::UNITS / NT];
+  bf16_t *As[2] = {smem, smem + C::STAGE};
+  bf16_t *Bs[2] = {smem + OA::ELEMS, smem + C::STAGE + OA::ELEMS};
+
+  auto compute = [&](const bf16_t *as, const bf16_t *bs) {
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t fb[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  if (nk > 0) {
+    OA::template load<NT>(ra0, rsa, p.lda, m0, kbeg, p.M, kend, tid);
+    OB::template load<NT>(rb0, rsb, p.ldb, n0, kbeg, p.N, kend, tid);
+    if (nk > 1) {
+      OA::template load<NT>(ra1, rsa, p.lda, m0, kbeg + BK, p.M, kend, tid);
+      OB::template load<NT>(rb1, rsb, p.ldb, n0, kbeg + BK, p.N, kend, tid);
+    }
+    OA::template store<NT>(As[0], ra0, tid);
+    OB::template store<NT>(Bs[0], rb0, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nk; it += 2) {
+    // even stage: compute buffer 0, set 0 is free -> stage it+2, store set 1 (stage it+1)
+    if (it + 2 < nk) {
+      OA::template load<NT>(ra0, rsa, p.lda, m0, kbeg + (it + 2) * BK, p.M, kend, tid);
+      OB::template load<NT>(rb0, rsb, p.ldb, n0, kbeg + (it + 2) * BK, p.N, kend, tid);
+    }
+    compute(As[0], Bs[0]);
+    if (it + 1 < nk) {
+      OA::template store<NT>(As[1], ra1, tid);
+      OB::template store<NT>(Bs[1], rb1, tid);
+    }
+    __syncthreads();
+    if (it + 1 >= nk) break;
+    // odd stage: compute buffer 1, set 1 is free -> stage it+3, store set 0 (stage it+2)
+    if (it + 3 < nk) {
+      OA::template load<NT>(ra1, rsa, p.lda, m0, kbeg + (it + 3) * BK, p.M, kend, tid);
+      OB::template load<NT>(rb1, rsb, p.ldb, n0, kbeg + (it + 3) * BK, p.N, kend, tid);
+    }
+    compute(As[1], Bs[1]);
+    if (it + 2 < nk) {
+      OA::template store<NT>(As[0], ra0, tid);
+      OB::template store<NT>(Bs[0], rb0, tid);
+    }
+    __syncthreads();
+  }
+
+  // Split-K partial sums go to their own slice of a workspace.
+  if (p.out_zstride) p.out = (float *)p.out + blockIdx.z * p.out_zstride;
+  // Epilogue, one wave-row of the tile at a time through LDS (fp32), then
+  // row-coalesced 4-wide stores by all threads.
+  float *Cs = (float *)smem_raw;
+  constexpr int TPR = BN / 4, RPP = NT / TPR;
+  const int cc = (tid % TPR) * 4;
+  const int n = n0 + cc;
+  const int nv = p.n_valid;
+  float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.bias && blockIdx.z == 0) {
+    if (n + 3 < nv) {
+      bias = *(const float4 *)(p.bias + n);
+    } else {
+      if (n < nv) bias.x = p.bias[n];
+      if (n + 1 < nv) bias.y = p.bias[n + 1];
+      if (n + 2 < nv) bias.z = p.bias[n + 2];
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < WM; ++pass) {
+    if (pass > 0) __syncthreads();
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
+    }
+    __syncthreads();
+    for (int rr = tid / TPR; rr < C::WTM; rr += RPP) {
+      const int m = m0 + pass * C::WTM + rr;
+      if (m >= p.M || n >= nv) continue;
+      float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
+      v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
+      epilogue4(p, m, n, v, nv - n);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
+  GemmParams p;
+  p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
+  p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
+  p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
+  p.vec_out = gemm_vec_out(g) ? 1 : 0;
+  p.out_zstride = 0;
+  p.a_bytes = (uint32_t)gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda);
+  p.b_bytes = (uint32_t)gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb);
+  p.tiles_m = (g.M + BM - 1) / BM;
+  p.tiles_n = (g.N + BN - 1) / BN;
+  const int kb = (g.K + BK - 1) / BK;
+  const int per = (kb + split - 1) / split;
+  p.k_chunk = per * BK;
+  split = (kb + per - 1) / per;
+  p.out_zstride = out_zstride;
+  dim3 grid(p.tiles_m * p.tiles_n, 1, split);
+#define TT_L(AK, BKM)                                                                          \
+  if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                 \
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM>), grid, dim3(64 * WM * WN), 0, \
+                       ctx->stream, p);                                                        \
+    return tt_check_launch(ctx, "gemm_bf16");                                                  \
+  }
+  TT_L(true, true) TT_L(true, false) TT_L(false, true) TT_L(false, false)
+#undef TT_L
+  return TT_EINVAL;
+}
+
+
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ out, int ldo,
+                                                             const float *__restrict__ ws, int M,
+                                                             int N, int split) {
+  const size_t mn = (size_t)M * N;
+  const size_t n4 = mn / 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  if (N % 4 == 0 && ldo % 4 == 0) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+      float4 s = ((const float4 *)ws)[i];
+      for (int z = 1; z < split; ++z) {
+        float4 t = ((const float4 *)(ws + z * mn))[i];
+        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+      }
+      const size_t e = i * 4;
+      const int m = (int)(e / N), n = (int)(e % N);
+      float4 *o = (float4 *)(out + (size_t)m * ldo + n);
+      float4 c = *o;
+      *o = make_float4(c.x + s.x, c.y + s.y, c.z + s.z, c.w + s.w);
+    }
+  } else {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += stride) {
+      float s = ws[i];
+      for (int z = 1; z < split; ++z) s += ws[z * mn + i];
+      out[(i / N) * ldo + i % N] += s;
+    }
+  }
+}
+
+}  // namespace
+
+// Host guard: the buffer-load path needs every operand extent below the OOB
+// offset, and a zero in one operand for k >= K (see Operand::load).
+bool tt_gemm_bf16_ok(const GemmArgs &g) {
+  if (gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda) >= OOB) return false;
+  if (gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb) >= OOB) return false;
+  return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
+}
+
+// Tile: 256 x 128 with 8 waves (two per SIMD).
+// Weight gradients (EPI_ACCUM, output += product) never use atomics: one
+// split accumulates with a plain read-modify-write (a workgroup owns its
+// output tile); several splits write fp32 partials to arena scratch, then
+// one coalesced pass adds them into the output.
+int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
+  const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
+  if (g.epi != EPI_ACCUM) return launch<256, 128, 4, 2>(ctx, g, 1);
+  const int kb = (g.K + BK - 1) / BK;
+  int split = 1;
+  while (tiles * split < 256 && split * 2 <= kb / 8) split *= 2;
+  if (g.split_k > 0) split = g.split_k;
+  GemmArgs h = g;
+  if (split == 1) {
+    h.epi = EPI_STORE_ACC;
+    return launch<256, 128, 4, 2>(ctx, h, 1);
+  }
+  tt_scratch_scope scope(ctx);
+  void *ws;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)split * g.M * g.N * 4, &ws));
+  h.epi = EPI_STORE;
+  h.out = ws;
+  h.ldo = g.N;
+  h.out_bf16 = false;
+  h.bias = nullptr;
+  TT_TRY((launch<256, 128, 4, 2>(ctx, h, split, (size_t)g.M * g.N)));
+  const size_t work = (size_t)g.M * g.N / 4;
+  const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, ctx->stream, (float *)g.out,
+                     g.ldo, (const float *)ws, g.M, g.N, split);
+  return tt_check_launch(ctx, "splitk_reduce");
+}

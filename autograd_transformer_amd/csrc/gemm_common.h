@@ -1,0 +1,147 @@
+// Shared pieces of the GEMM kernels: launch parameters and the epilogue.
+#pragma once
+
+#include "tt_internal.h"
+
+namespace tt_gemm_detail {
+
+struct GemmParams {
+  const void *A; int lda;
+  const void *B; int ldb;
+  int M, N, K;
+  int k_chunk;   // K range per split (multiple of BK)
+  int epi;
+  void *out; int ldo; int out_bf16;
+  const float *bias;
+  const float *resid; int ldr;
+  void *aux; int ldx;
+  int n_valid;
+  int tiles_m, tiles_n;
+  int vec_out;   // output/aux/resid rows allow 4-wide vector access
+  uint32_t a_bytes, b_bytes;  // operand extents for buffer range checks
+  size_t out_zstride;         // split-K partials: output offset per blockIdx.z (elements)
+};
+
+__device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
+  if (out_bf16)
+    ((bf16_t *)out)[(size_t)m * ldo + n] = f2bf(v);
+  else
+    ((float *)out)[(size_t)m * ldo + n] = v;
+}
+
+// Epilogue for 4 consecutive columns n..n+3 of row m (only the first `cnt`
+// of them exist when the tile sticks out of the matrix).  Vector accesses
+// need 16-byte (f32) / 8-byte (bf16) aligned rows, which the host checks
+// (p.vec_out); otherwise elements are handled one by one.
+__device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
+  const bool full = cnt >= 4 && p.vec_out;
+  float a[4] = {v.x, v.y, v.z, v.w};
+  const int lim = cnt < 4 ? cnt : 4;
+  switch (p.epi) {
+    case EPI_STORE:
+    case EPI_GELU: {
+      if (p.epi == EPI_GELU) {
+        if (p.aux) {
+          if (full && p.out_bf16)
+            *(uint2 *)((bf16_t *)p.aux + (size_t)m * p.ldx + n) =
+                make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+          else
+            for (int q = 0; q < lim; ++q) store_out(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = gelu_f(a[q]);
+      }
+      if (full) {
+        if (p.out_bf16)
+          *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
+              make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+        else
+          *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) = make_float4(a[0], a[1], a[2], a[3]);
+      } else {
+        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+      }
+      break;
+    }
+    case EPI_RESID: {
+      const float *rp = p.resid + (size_t)m * p.ldr + n;
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      if (full) {
+        float4 r = *(const float4 *)rp;
+        *(float4 *)op = make_float4(r.x + a[0], r.y + a[1], r.z + a[2], r.w + a[3]);
+      } else {
+        for (int q = 0; q < lim; ++q) op[q] = rp[q] + a[q];
+      }
+      break;
+    }
+    case EPI_GELU_BWD: {
+      float h[4];
+      if (p.out_bf16) {
+        const bf16_t *hp = (const bf16_t *)p.aux + (size_t)m * p.ldx + n;
+        if (full) {
+          uint2 u = *(const uint2 *)hp;
+          h[0] = __uint_as_float(u.x << 16); h[1] = __uint_as_float(u.x & 0xffff0000u);
+          h[2] = __uint_as_float(u.y << 16); h[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          for (int q = 0; q < 4; ++q) h[q] = q < lim ? bf2f(hp[q]) : 0.f;
+        }
+      } else {
+        const float *hp = (const float *)p.aux + (size_t)m * p.ldx + n;
+        for (int q = 0; q < 4; ++q) h[q] = q < lim ? hp[q] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] *= gelu_grad_f(h[q]);
+      if (full && p.out_bf16)
+        *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
+            make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+      else
+        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+      break;
+    }
+    case EPI_ACCUM: {
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      for (int q = 0; q < lim; ++q) unsafeAtomicAdd(op + q, a[q]);
+      break;
+    }
+    case EPI_STORE_ACC: {
+      float *op = (float *)p.out + (size_t)m * p.ldo + n;
+      for (int q = 0; q < lim; ++q) op[q] += a[q];
+      break;
+    }
+  }
+}
+
+
+// Block id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
+// the 8 XCDs (each with its own L2), so first give every XCD a contiguous
+// range of tiles, then walk that range in groups of GM tile-rows so that
+// neighbouring workgroups share both A rows and B columns in L2.
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, int &tm,
+                                            int &tn) {
+  constexpr int XCDS = 8, GM = 8;
+  if (nwg % XCDS == 0) bid = (bid % XCDS) * (nwg / XCDS) + bid / XCDS;
+  const int per_group = GM * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in = bid % per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// Host: may the epilogue use 4-wide vector accesses on out / aux / resid?
+inline bool gemm_vec_out(const GemmArgs &g) {
+  const int oes = g.out_bf16 ? 2 : 4;   // bytes per output element (aux has the same)
+  bool ok = ((uintptr_t)g.out % (4 * oes) == 0) && (g.ldo % 4 == 0);
+  if (g.aux) ok = ok && ((uintptr_t)g.aux % (4 * oes) == 0) && (g.ldx % 4 == 0);
+  if (g.resid) ok = ok && ((uintptr_t)g.resid % 16 == 0) && (g.ldr % 4 == 0);
+  if (g.epi == EPI_RESID || g.epi == EPI_ACCUM || g.epi == EPI_STORE_ACC)
+    ok = ok && ((uintptr_t)g.out % 16 == 0);
+  return ok;
+}
+
+// Bytes spanned by an operand: rows x reduction, k-major or row-major.
+inline size_t gemm_extent_bytes(bool kmajor, int rows, int K, int ld) {
+  return kmajor ? ((size_t)(rows - 1) * ld + K) * 2 : ((size_t)(K - 1) * ld + rows) * 2;
+}
+
+}  // namespace tt_gemm_detail

@@ -66,18 +66,16 @@ typedef uint16_t bf16_t;  // bf16 storage
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
-// float -> bf16, round to nearest even, NaN kept quiet NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32), NaN stays NaN.
+typedef float tt_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 tt_b2 __attribute__((ext_vector_type(2)));
 // Pack two floats into one dword of two bf16 (lo = a).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  tt_f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, tt_b2));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack_bf2(f, 0.f) & 0xffffu); }
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -151,6 +149,9 @@ struct GemmArgs {
   int n_valid;                 // columns >= n_valid of C are not stored (ragged pad); 0 = N
 };
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
+// bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
+int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g);
+bool tt_gemm_bf16_ok(const GemmArgs &g);
 
 int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, const float *x,
                           const float *g, const float *b, void *y, float *mean, float *rstd);
@@ -166,6 +167,12 @@ int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      const void *out, const float *lse, const void *dout, void *dqkv,
                      float *scratch_D);
+// bf16 attention kernels (buffer loads, LDS transpose reads); *_ok says
+// whether the tensors fit their 32-bit buffer offsets.
+bool tt_attn_bf16_ok(int B, int T, int NH);
+int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse);
+int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
+                     const float *lse, const void *dout, void *dqkv, float *Dv);
 // In-place CE over logits; per_row_loss [N] scratch; loss = mean.
 int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
                const int32_t *targets, float *per_row_loss, float *loss, float grad_scale);
