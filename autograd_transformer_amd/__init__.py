@@ -95,6 +95,20 @@ class Context:
     def reset(self):
         return self.check(lib().tt_ctx_reset(self.handle))
 
+    def profile(self, enable):
+        """Start (clearing earlier records) or stop per-kernel event timing."""
+        return self.check(lib().tt_ctx_profile(self.handle, 1 if enable else 0))
+
+    def profile_report(self):
+        """Per-kernel totals since profile(True): list of dicts with name,
+        calls, ms, flops, bytes (algorithmic work of those launches)."""
+        n = _C.c_int(0)
+        self.check(lib().tt_ctx_profile_report(self.handle, None, _C.byref(n)))
+        arr = (_L.tt_prof_entry * max(n.value, 1))()
+        self.check(lib().tt_ctx_profile_report(self.handle, arr, _C.byref(n)))
+        return [dict(name=e.name.decode(), calls=e.calls, ms=e.ms, flops=e.flops, bytes=e.bytes)
+                for e in arr[: n.value]]
+
     def usage(self):
         u, c = _C.c_size_t(), _C.c_size_t()
         self.check(lib().tt_ctx_usage(self.handle, _C.byref(u), _C.byref(c)))

@@ -38,6 +38,11 @@ class tt_param(C.Structure):
                 ("n", sz), ("wd_mult", f32)]
 
 
+class tt_prof_entry(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("calls", i32), ("ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
 class tt_model_cfg(C.Structure):
     _fields_ = [("L", i32), ("C", i32), ("NH", i32), ("F", i32), ("V", i32),
                 ("V_pad", i32), ("T_max", i32), ("B_max", i32), ("mode", i32),
@@ -56,6 +61,8 @@ SIGS = {
     "tt_ctx_sync": (i32, [vp]),
     "tt_strerror": (C.c_char_p, [i32]),
     "tt_ctx_last_error": (C.c_char_p, [vp]),
+    "tt_ctx_profile": (i32, [vp, i32]),
+    "tt_ctx_profile_report": (i32, [vp, P(tt_prof_entry), P(i32)]),
     "tt_linear_fwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]),
     "tt_linear_bwd": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]),
     "tt_layernorm_fwd": (i32, [vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp]),

@@ -431,6 +431,8 @@ bool tt_attn_bf16_ok(int B, int T, int NH) {
 int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse) {
   const int nqb = (T + 127) / 128;
   const uint32_t qb = (uint32_t)((size_t)B * T * 3 * NH * HS * 2);
+  const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
+  tt_prof_scope prof(ctx, "attn_fwd_bf16_kernel", 2.0 * pass, 0.0);
   hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(B * NH * nqb), dim3(256), 0, ctx->stream, T, NH,
                      (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
   return tt_check_launch(ctx, "attn_fwd_bf16");
@@ -441,13 +443,22 @@ int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const v
   const int BT = B * T;
   const uint32_t qb = (uint32_t)((size_t)BT * 3 * NH * HS * 2);
   const uint32_t ob = (uint32_t)((size_t)BT * NH * HS * 2);
-  hipLaunchKernelGGL(attn_dot_bf16_kernel, dim3((BT * NH * 16 + 255) / 256), dim3(256), 0,
-                     ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
+  const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
+  {
+    tt_prof_scope prof(ctx, "attn_dot_bf16_kernel", 0.0, 2.0 * ob + 4.0 * BT * NH);
+    hipLaunchKernelGGL(attn_dot_bf16_kernel, dim3((BT * NH * 16 + 255) / 256), dim3(256), 0,
+                       ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
+  }
   TT_TRY(tt_check_launch(ctx, "attn_dot_bf16"));
   const int nb = (T + 63) / 64;
+  {
+  // algorithmic backward: dP, dV, dK here, dQ in the next kernel (4 products)
+  tt_prof_scope prof(ctx, "attn_dkdv_bf16_kernel", 3.0 * pass, 0.0);
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
                      (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
+  }
   TT_TRY(tt_check_launch(ctx, "attn_dkdv_bf16"));
+  tt_prof_scope prof(ctx, "attn_dq_bf16_kernel", pass, 0.0);
   hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
                      (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
   return tt_check_launch(ctx, "attn_dq_bf16");

@@ -7,6 +7,7 @@
 // buffer) and carving is 256-byte aligned.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "tt_internal.h"
 
@@ -104,6 +105,7 @@ extern "C" void tt_ctx_destroy(tt_ctx *ctx) {
   if (!ctx || ctx->magic != TT_CTX_MAGIC) return;
   (void)hipSetDevice(ctx->device);
   (void)hipStreamSynchronize(ctx->stream);
+  for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   if (ctx->owns_arena && ctx->arena) (void)hipFree(ctx->arena);
   if (ctx->dev_flags) (void)hipFree(ctx->dev_flags);
   ctx->magic = 0;
@@ -158,6 +160,66 @@ extern "C" int tt_ctx_sync(tt_ctx *ctx) {
     (void)hipMemset(ctx->dev_flags, 0, 16);
     return tt_set_error(ctx, TT_ERANGE, "a token id or target was outside [0, V)");
   }
+  return TT_OK;
+}
+
+static hipEvent_t prof_event(tt_ctx *ctx) {
+  if (ctx->ev_used == ctx->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    ctx->ev_pool.push_back(e);
+  }
+  return ctx->ev_pool[ctx->ev_used++];
+}
+
+tt_prof_scope::tt_prof_scope(tt_ctx *c, const char *name, double flops, double bytes) : ctx(c) {
+  if (!ctx->profiling) return;
+  tt_prof_rec r{name, flops, bytes, prof_event(ctx), prof_event(ctx)};
+  if (!r.e0 || !r.e1) return;
+  (void)hipEventRecord(r.e0, ctx->stream);
+  idx = (long)ctx->prof.size();
+  ctx->prof.push_back(r);
+}
+
+tt_prof_scope::~tt_prof_scope() {
+  if (idx >= 0) (void)hipEventRecord(ctx->prof[idx].e1, ctx->stream);
+}
+
+extern "C" int tt_ctx_profile(tt_ctx *ctx, int enable) {
+  TT_TRY(tt_check_ctx(ctx));
+  if (enable) {
+    ctx->prof.clear();
+    ctx->ev_used = 0;
+  }
+  ctx->profiling = enable != 0;
+  return TT_OK;
+}
+
+extern "C" int tt_ctx_profile_report(tt_ctx *ctx, tt_prof_entry *out, int *count) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, count != nullptr, "profile_report: count is NULL");
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "profile_report: %s", hipGetErrorString(e));
+  std::vector<tt_prof_entry> agg;
+  for (const tt_prof_rec &r : ctx->prof) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) {
+      (void)hipGetLastError();
+      continue;
+    }
+    size_t i = 0;
+    while (i < agg.size() && strcmp(agg[i].name, r.name) != 0) ++i;
+    if (i == agg.size()) agg.push_back(tt_prof_entry{r.name, 0, 0.0, 0.0, 0.0});
+    agg[i].calls += 1;
+    agg[i].ms += ms;
+    agg[i].flops += r.flops;
+    agg[i].bytes += r.bytes;
+  }
+  if (out) {
+    const int n = (int)agg.size() < *count ? (int)agg.size() : *count;
+    for (int i = 0; i < n; ++i) out[i] = agg[i];
+  }
+  *count = (int)agg.size();
   return TT_OK;
 }
 

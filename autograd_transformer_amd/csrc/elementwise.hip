@@ -153,12 +153,14 @@ __global__ void __launch_bounds__(256) finite_kernel(size_t n, const float *__re
 
 int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v) {
   if (n == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "fill_kernel", 0.0, 4.0 * n);
   hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, p, v);
   return tt_check_launch(ctx, "fill");
 }
 
 int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst) {
   if (n == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "cast_kernel", 0.0, 6.0 * n);
   hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src, dst);
   return tt_check_launch(ctx, "cast");
 }
@@ -168,6 +170,8 @@ int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf1
   if (n == 0) return TT_OK;
   const float rbc1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)t)));
   const float rbc2 = (float)(1.0 / (1.0 - pow((double)beta2, (double)t)));
+  // w, g, m, v read; w, m, v written; optional bf16 copy: 28 (30) bytes per parameter
+  tt_prof_scope prof(ctx, "adamw_kernel", 0.0, (28.0 + (w_lowp ? 2.0 : 0.0)) * n);
   hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, w, g, m, v,
                      w_lowp, lr, beta1, beta2, eps, wd, rbc1, rbc2);
   return tt_check_launch(ctx, "adamw");
@@ -186,6 +190,7 @@ extern "C" int tt_embed_fwd(tt_ctx *ctx, int B, int T, int C, int V, const int32
   TT_REQUIRE(ctx, tt_aligned16(wte) && tt_aligned16(wpe) && tt_aligned16(x0), "embed_fwd: alignment");
   const int BT = B * T;
   if (BT == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "embed_fwd_kernel", 0.0, 12.0 * BT * (double)C + 4.0 * BT);
   hipLaunchKernelGGL(embed_fwd_kernel, dim3((BT + 3) / 4), dim3(256), 0, ctx->stream, BT, T, C, V,
                      tok, wte, wpe, x0, ctx->dev_flags);
   return tt_check_launch(ctx, "embed_fwd");
@@ -199,12 +204,14 @@ extern "C" int tt_embed_bwd(tt_ctx *ctx, int B, int T, int C, int V, const int32
   const int BT = B * T;
   if (BT == 0) return TT_OK;
   if (dwte) {
+    tt_prof_scope prof(ctx, "embed_bwd_tok_kernel", 0.0, 12.0 * BT * (double)C + 4.0 * BT);
     hipLaunchKernelGGL(embed_bwd_tok_kernel, dim3((BT + 3) / 4), dim3(256), 0, ctx->stream, BT, C, V,
                        tok, dx0, dwte);
     TT_TRY(tt_check_launch(ctx, "embed_bwd_tok"));
   }
   if (dwpe) {
     size_t n = (size_t)T * C;
+    tt_prof_scope prof(ctx, "embed_bwd_pos_kernel", 0.0, 4.0 * BT * (double)C + 8.0 * n);
     hipLaunchKernelGGL(embed_bwd_pos_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        ctx->stream, B, T, C, dx0, dwpe);
     TT_TRY(tt_check_launch(ctx, "embed_bwd_pos"));

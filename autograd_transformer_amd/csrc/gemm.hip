@@ -354,6 +354,8 @@ int launch_gemm(tt_ctx *ctx, const GemmArgs &g, int split) {
   p.k_chunk = per * BK;
   split = (kb + per - 1) / per;
   dim3 grid(p.tiles_m * p.tiles_n, 1, split);
+  tt_prof_scope prof(ctx, sizeof(T) == 2 ? "gemm_kernel<bf16>" : "gemm_kernel<f32>",
+                     2.0 * g.M * g.N * g.K, 0.0);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, A_KM, B_KM, VECLD>), grid,
                      dim3(64 * WM * WN), 0, ctx->stream, p);
   return tt_check_launch(ctx, "gemm");

@@ -13,6 +13,8 @@
 //    lane j then receives column c0 + j of rows k0 .. k0+3.
 // Tile BM x BN x 64 per workgroup, WM x WN waves each owning a
 // (BM/WM) x (BN/WN) block of 16x16 accumulator tiles.
+#include <stdio.h>
+
 #include <algorithm>
 
 #include "gemm_common.h"
@@ -260,6 +262,12 @@ int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   split = (kb + per - 1) / per;
   p.out_zstride = out_zstride;
   dim3 grid(p.tiles_m * p.tiles_n, 1, split);
+  static char names[4][80];
+  const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0);
+  if (!names[li][0])
+    snprintf(names[li], sizeof names[li], "gemm_bf16_kernel<%d, %d, %d, %d, %s, %s>", BM, BN, WM, WN,
+             g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
+  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, 0.0);
 #define TT_L(AK, BKM)                                                                          \
   if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                 \
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM>), grid, dim3(64 * WM * WN), 0, \
@@ -338,6 +346,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   TT_TRY((launch<256, 128, 4, 2>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
+  tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0, (split + 2.0) * g.M * g.N * 4.0);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, ctx->stream, (float *)g.out,
                      g.ldo, (const float *)ws, g.M, g.N, split);
   return tt_check_launch(ctx, "splitk_reduce");

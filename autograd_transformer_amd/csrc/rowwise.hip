@@ -310,6 +310,8 @@ int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, co
   if (N == 0) return TT_OK;
   dim3 grid((N + 3) / 4);
   const int nv = (C / 4 + 63) / 64;
+  tt_prof_scope prof(ctx, "layernorm_fwd_kernel", 0.0,
+                     (double)N * C * (4.0 + (mode == TT_BF16 ? 2.0 : 4.0)) + 8.0 * C + 8.0 * N);
 #define TT_LNF(NV)                                                                              \
   if (nv <= NV) {                                                                               \
     if (mode == TT_BF16)                                                                        \
@@ -334,6 +336,9 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
   if (N == 0) return TT_OK;
   dim3 grid((N + LNB_ROWS - 1) / LNB_ROWS);
   const int nv = (C / 4 + 63) / 64;
+  tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
+                     (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
+                         16.0 * C + 8.0 * N);
 #define TT_LNB(NV)                                                                              \
   if (nv <= NV) {                                                                               \
     hipLaunchKernelGGL((layernorm_bwd_kernel<NV>), grid, dim3(256), 0, ctx->stream, N, C, x, mean, \
@@ -352,6 +357,7 @@ int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src,
   while (colblocks * rowsplit < 1024 && rowsplit * 64 < M) rowsplit *= 2;
   int rpb = (M + rowsplit - 1) / rowsplit;
   dim3 grid(colblocks, (M + rpb - 1) / rpb);
+  tt_prof_scope prof(ctx, "colsum_kernel", 0.0, (double)M * N * (src_bf16 ? 2.0 : 4.0) + 4.0 * N);
   if (src_bf16)
     hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(256), 0, ctx->stream, M, N, ld, rpb, src, out);
   else
@@ -363,6 +369,8 @@ int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
                const int32_t *targets, float *per_row_loss, float *loss, float grad_scale) {
   TT_REQUIRE(ctx, N > 0 && V > 0 && ld >= V, "ce: bad shape N=%d V=%d ld=%d", N, V, ld);
   TT_REQUIRE(ctx, logits && targets && per_row_loss && loss, "ce: NULL pointer");
+  {
+  tt_prof_scope prof(ctx, "ce_kernel", 0.0, 2.0 * N * (double)ld * (mode == TT_BF16 ? 2.0 : 4.0) + 8.0 * N);
   if (mode == TT_BF16) {
     TT_REQUIRE(ctx, ld % 8 == 0 && tt_aligned16(logits), "ce(bf16): ld %% 8 and 16-byte alignment required");
     hipLaunchKernelGGL(ce_kernel<true>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
@@ -371,7 +379,9 @@ int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
     hipLaunchKernelGGL(ce_kernel<false>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
                        targets, per_row_loss, grad_scale, ctx->dev_flags);
   }
+  }
   TT_TRY(tt_check_launch(ctx, "ce"));
+  tt_prof_scope prof(ctx, "mean_kernel", 0.0, 4.0 * N);
   hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, ctx->stream, N, per_row_loss, loss);
   return tt_check_launch(ctx, "ce_mean");
 }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <vector>
 
 #include "tt.h"
 
@@ -16,6 +17,15 @@
 #define TT_CTX_MAGIC 0x54544358u    // "TTCX"
 #define TT_MODEL_MAGIC 0x54544d44u  // "TTMD"
 #define TT_SAVED_MAGIC 0x54545342u  // "TTSB"
+
+// One timed kernel launch (profiling mode): HIP events on the context's
+// stream around the launch, tagged with the kernel name and its algorithmic
+// work (FLOPs for contractions, HBM bytes for bandwidth-bound kernels).
+struct tt_prof_rec {
+  const char *name;
+  double flops, bytes;
+  hipEvent_t e0, e1;
+};
 
 struct tt_ctx {
   uint32_t magic;
@@ -28,6 +38,18 @@ struct tt_ctx {
   bool owns_arena;
   int32_t *dev_flags;  // [0]: range error seen in a kernel (token/target id)
   std::string last_error;
+  bool profiling = false;
+  std::vector<tt_prof_rec> prof;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+};
+
+// Bracket one kernel launch with profiling events (no-op unless enabled).
+struct tt_prof_scope {
+  tt_ctx *ctx;
+  long idx = -1;
+  tt_prof_scope(tt_ctx *c, const char *name, double flops, double bytes);
+  ~tt_prof_scope();
 };
 
 // Validate a context handle (magic word catches freed or foreign pointers,

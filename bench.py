@@ -45,7 +45,7 @@ def step_flops(L, C, V, T, B, F=None, **_):
     return 3.0 * (L * (linear + attn) + head)
 
 
-def cpu_baseline(w, seconds_budget=20.0):
+def cpu_baseline(w):
     """Time the CPU oracle (float64 NumPy, as it stands) on a bounded sample of
     the same workload: one training step of the same model on one sequence of
     a reduced length, scaled to tokens/s."""
@@ -60,7 +60,7 @@ def cpu_baseline(w, seconds_budget=20.0):
                        block_size=w["T"])
     p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=3).items()}
     zeros = {k: np.zeros_like(v) for k, v in p.items()}
-    T = 128
+    T = 512
     tok, tgt = syn.gpt2_tokens(1, T, w["V"], seed=3)
     t0 = time.perf_counter()
     og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16")
@@ -132,6 +132,17 @@ def main():
     last_loss = float(loss.item())
     if not math.isfinite(last_loss) or int(flag.item()) != 0:
         log(f"[bench] WARNING: non-finite loss {last_loss}")
+    # Second pass over the same number of steps with every kernel launch
+    # bracketed by HIP events on the context stream: per-kernel durations for
+    # the roofline of the dominant kernel (events add small gaps between
+    # kernels, so this pass is not the throughput figure).
+    ctx.profile(True)
+    for _ in range(args.steps):
+        step(t)
+        t += 1
+    kernels = ctx.profile_report()
+    ctx.profile(False)
+    ctx.sync()
     tokens = B * T
     flops = step_flops(**w)
     value = tokens / (ms / 1e3)
@@ -159,6 +170,31 @@ def main():
         "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "loss": round(last_loss, 5),
     }
+    dom = max(kernels, key=lambda k: k["ms"])
+    avg_ms = dom["ms"] / dom["calls"]
+    if dom["flops"] > 0:
+        per_launch = dom["flops"] / dom["calls"]
+        achieved = per_launch / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        per_launch = dom["bytes"] / dom["calls"]
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom["name"]
+    roof["calls_per_step"] = dom["calls"] / args.steps
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+    roof["share_of_step"] = round(dom["ms"] / args.steps / ms, 4)
+    out["roofline"] = roof
+    top = sorted(kernels, key=lambda k: -k["ms"])[:8]
+    for k in top:
+        rate = (f"{k['flops'] / (k['ms'] / 1e3) / 1e12:7.1f} TFLOP/s" if k["flops"] > 0 else
+                f"{k['bytes'] / (k['ms'] / 1e3) / 1e9:7.1f} GB/s")
+        log(f"[bench]   {k['ms'] / args.steps:7.3f} ms/step  {k['calls'] // args.steps:4d} calls  "
+            f"{rate}  {k['name']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -100,6 +100,26 @@ int tt_ctx_sync(tt_ctx *ctx);
 const char *tt_strerror(int status);
 const char *tt_ctx_last_error(const tt_ctx *ctx);
 
+/* Kernel timing (the C++/CUDA page, section 2.2, records an event pair per
+ * op on its stream).  tt_ctx_profile(ctx, 1) clears earlier records and
+ * starts bracketing every kernel launch with HIP events on the context's
+ * stream; tt_ctx_profile(ctx, 0) stops.  tt_ctx_profile_report waits for the
+ * stream and aggregates the records by kernel name: calls, total
+ * milliseconds, and the algorithmic work of those launches (FLOPs for
+ * matrix-core kernels, HBM bytes for bandwidth-bound ones; 0 where the other
+ * measure applies).  out [host] may be NULL to query *count; otherwise it
+ * holds *count entries on input and *count receives the number of kernels.
+ * Names point to static strings inside the library. */
+typedef struct {
+  const char *name;
+  int calls;
+  double ms;
+  double flops;
+  double bytes;
+} tt_prof_entry;
+int tt_ctx_profile(tt_ctx *ctx, int enable);
+int tt_ctx_profile_report(tt_ctx *ctx, tt_prof_entry *out /* [host] */, int *count /* [host] */);
+
 /* ------------------------------------------------------------------------ */
 /* Op level.                                                                 */
 /* ------------------------------------------------------------------------ */
