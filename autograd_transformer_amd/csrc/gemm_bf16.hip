@@ -110,9 +110,10 @@ struct Cfg {
 };
 
 // Occupancy target: two waves per SIMD (two 4-wave or one 8-wave workgroup
-// per CU), which caps registers at 256 per lane.
+// per CU, capping registers at 256 per lane), except the 256x256 tile whose
+// four waves each hold a 128x128 accumulator (one wave per SIMD).
 template <int BM, int BN, int WM, int WN, bool A_KM, bool B_KM>
-__global__ void __launch_bounds__(64 * WM * WN, (WM * WN == 4) ? 2 : 1)
+__global__ void __launch_bounds__(64 * WM * WN, (WM * WN == 4 && BM * BN < 256 * 256) ? 2 : 1)
 gemm_bf16_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, A_KM, B_KM>;
   using OA = typename C::OA;
@@ -280,6 +281,249 @@ int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
 }
 
 
+// --------------------------------------------------------------------------
+// v3: direct-to-LDS loads (buffer_load ... lds: lane i of a wave writes the
+// 16 bytes it fetched at LDS base + 16 i), so no staging registers; an
+// NSTAGE-deep ring of LDS tiles; one barrier per stage.  Tiles are unpadded
+// and their 16-byte chunks XOR-swizzled so that the 16 lanes of one MFMA
+// fragment read land on distinct banks:
+//   k-major rows (BK elements):   physical chunk = chunk ^ swz_k(row)
+//   row-major rows (ROWS elems):  physical chunk = chunk ^ rswz(k)
+// (rswz spreads the rows k..k+3 and k+8..k+11 that two lane groups read in
+// the same LDS cycle over 8 distinct chunk pairs).
+// Each loading lane owns a fixed LDS slot and fetches the global chunk that
+// belongs there.
+// --------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int ROWS, int BKV, bool KM>
+struct DOp {
+  static constexpr int ELEMS = ROWS * BKV;            // bf16 per stage
+  static constexpr int BYTES = ELEMS * 2;
+  static constexpr int CHUNKS = BYTES / 1024;         // 1 KB per wave instruction
+  static constexpr int CPR = KM ? BKV / 8 : ROWS / 8; // 16-byte chunks per LDS row
+  static constexpr int RB = KM ? BKV * 2 : ROWS * 2;  // bytes per LDS row
+  static_assert(BYTES % 1024 == 0, "tile must be whole 1 KB wave loads");
+
+  __device__ __forceinline__ static int swz_k(int r) { return (r / (256 / RB)) % CPR; }
+  __device__ __forceinline__ static int rswz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+  // Issue this wave's share of the tile's loads (chunk instructions w, w+NW, ...).
+  template <int NW>
+  __device__ __forceinline__ static void issue(bf16_t *tile, __amdgpu_buffer_rsrc_t rs, int ld,
+                                               int r0, int k0, int R, int K, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS / NW; ++i) {
+      const int ci = wave + i * NW;
+      const int L = ci * 64 + lane;            // linear 16-byte slot in the tile
+      uint32_t off;
+      if constexpr (KM) {
+        const int r = L / CPR, pc = L % CPR;
+        const int lc = pc ^ swz_k(r);
+        const int gr = r0 + r, gk = k0 + lc * 8;
+        off = (gr < R && gk < K) ? (uint32_t)(((size_t)gr * ld + gk) * 2) : OOB;
+      } else {
+        const int k = L / CPR, pc = L % CPR;
+        const int lc = pc ^ rswz(k);
+        const int gk = k0 + k, gr = r0 + lc * 8;
+        off = (gk < K && gr < R) ? (uint32_t)(((size_t)gk * ld + gr) * 2) : OOB;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)((char *)tile + ci * 1024), 16, off,
+                                               0, 0, 0);
+    }
+  }
+
+  // Fragment: rows rb + lane%16, k = kk + 8 (lane/16) .. +7.
+  __device__ __forceinline__ static bf16x8_t frag(const bf16_t *t, int rb, int kk, int lr, int lg) {
+    if constexpr (KM) {
+      const int r = rb + lr;
+      const int pc = ((kk >> 3) + lg) ^ swz_k(r);
+      return *(const bf16x8_t *)(t + r * BKV + pc * 8);
+    } else {
+      const int c = rb + 4 * (lr & 3);
+      const int kr0 = kk + 8 * lg + (lr >> 2);
+      const int kr1 = kr0 + 4;
+      const int pc0 = (c >> 3) ^ rswz(kr0), pc1 = (c >> 3) ^ rswz(kr1);
+      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7)));
+      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr1 * ROWS + pc1 * 8 + (c & 7)));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
+struct Cfg3 {
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  using OA = DOp<BM, BKV, A_KM>;
+  using OB = DOp<BN, BKV, B_KM>;
+  static constexpr int STAGE = OA::ELEMS + OB::ELEMS;
+  static constexpr int LPS = OA::CHUNKS / NW + OB::CHUNKS / NW;   // loads per stage per wave
+  static constexpr int OPER_BYTES = NS * STAGE * 2;
+  static constexpr int LDC = BN + 4;
+  static constexpr int EPI_BYTES = WTM * LDC * 4;
+  static constexpr int SMEM = OPER_BYTES > EPI_BYTES ? OPER_BYTES : EPI_BYTES;
+  static_assert(OA::CHUNKS % NW == 0 && OB::CHUNKS % NW == 0, "loads not divisible by waves");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert((NS - 2) * LPS < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
+__global__ void __launch_bounds__(64 * WM * WN, 1)
+gemm_bf16_v3_kernel(GemmParams p) {
+  using C = Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>;
+  using OA = typename C::OA;
+  using OB = typename C::OB;
+  constexpr int NW = C::NW, NT = C::NT, FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::SMEM];
+  bf16_t *smem = (bf16_t *)smem_raw;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lg = lane >> 4;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto At = [&](int s) { return smem + s * C::STAGE; };
+  auto Bt = [&](int s) { return smem + s * C::STAGE + OA::ELEMS; };
+  auto issue = [&](int stage, int buf) {
+    const int k0 = kbeg + stage * BKV;
+    OA::template issue<NW>(At(buf), rsa, p.lda, m0, k0, p.M, kend, wave, lane);
+    OB::template issue<NW>(Bt(buf), rsb, p.ldb, n0, k0, p.N, kend, wave, lane);
+  };
+  const int nk = (kend - kbeg + BKV - 1) / BKV;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int it = 0; it < nk; ++it) {
+    // Stage it must have landed (from every wave) before anyone reads it:
+    // each wave waits for its own loads of that stage, then a bare barrier
+    // (no memory fence, which would also drain the loads still in flight for
+    // later stages).  The buffer refilled below was last read in iteration
+    // it-1, whose LDS reads every wave has consumed before reaching here.
+    // The empty asm statements keep the compiler from moving LDS accesses
+    // across the barrier (the barrier builtin is not a memory operation to
+    // it); they emit no instruction and no wait.
+    if (it + NS - 2 < nk) wait_vm<(NS - 2) * C::LPS>();
+    else wait_vm<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+    const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
+#pragma unroll
+    for (int kk = 0; kk < BKV; kk += 32) {
+      bf16x8_t fb[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (p.out_zstride) p.out = (float *)p.out + blockIdx.z * p.out_zstride;
+  float *Cs = (float *)smem_raw;
+  constexpr int TPR = BN / 4, RPP = NT / TPR;
+  const int cc = (tid % TPR) * 4;
+  const int n = n0 + cc;
+  const int nv = p.n_valid;
+  float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.bias && blockIdx.z == 0) {
+    if (n + 3 < nv) {
+      bias = *(const float4 *)(p.bias + n);
+    } else {
+      if (n < nv) bias.x = p.bias[n];
+      if (n + 1 < nv) bias.y = p.bias[n + 1];
+      if (n + 2 < nv) bias.z = p.bias[n + 2];
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < WM; ++pass) {
+    if (pass > 0) __syncthreads();
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
+    }
+    __syncthreads();
+    for (int rr = tid / TPR; rr < C::WTM; rr += RPP) {
+      const int m = m0 + pass * C::WTM + rr;
+      if (m >= p.M || n >= nv) continue;
+      float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
+      v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
+      epilogue4(p, m, n, v, nv - n);
+    }
+  }
+}
+
+template <int BM, int BN, int BKV, int WM, int WN, int NS>
+int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
+  GemmParams p;
+  p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
+  p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
+  p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
+  p.vec_out = gemm_vec_out(g) ? 1 : 0;
+  p.out_zstride = out_zstride;
+  p.a_bytes = (uint32_t)gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda);
+  p.b_bytes = (uint32_t)gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb);
+  p.tiles_m = (g.M + BM - 1) / BM;
+  p.tiles_n = (g.N + BN - 1) / BN;
+  const int kb = (g.K + BKV - 1) / BKV;
+  const int per = (kb + split - 1) / split;
+  p.k_chunk = per * BKV;
+  split = (kb + per - 1) / per;
+  dim3 grid(p.tiles_m * p.tiles_n, 1, split);
+  static char names[4][96];
+  const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0);
+  if (!names[li][0])
+    snprintf(names[li], sizeof names[li], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s>", BM,
+             BN, BKV, WM, WN, NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
+  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, 0.0);
+#define TT_L3(AK, BKM)                                                                          \
+  if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                  \
+    hipLaunchKernelGGL((gemm_bf16_v3_kernel<BM, BN, BKV, WM, WN, NS, AK, BKM>), grid,           \
+                       dim3(64 * WM * WN), 0, ctx->stream, p);                                  \
+    return tt_check_launch(ctx, "gemm_bf16_v3");                                                \
+  }
+  TT_L3(true, true) TT_L3(true, false) TT_L3(false, true) TT_L3(false, false)
+#undef TT_L3
+  return TT_EINVAL;
+}
+
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ out, int ldo,
                                                              const float *__restrict__ ws, int M,
                                                              int N, int split) {
@@ -318,22 +562,30 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
   return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
 }
 
-// Tile: 256 x 128 with 8 waves (two per SIMD).
+// Tile: 256 x 128 with 8 waves (two per SIMD).  Products whose operands are
+// both k-major (dX = dY W, the LM-head logits) and all weight gradients take
+// the direct-to-LDS v3 kernel (3-stage ring, BK 64); products with exactly one
+// row-major operand (the forward GEMMs with W stored [K, N], the LM-head dH)
+// take the register-prefetch v2 kernel, which is faster there.
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
 // split accumulates with a plain read-modify-write (a workgroup owns its
 // output tile); several splits write fp32 partials to arena scratch, then
-// one coalesced pass adds them into the output.
+// one coalesced pass adds them into the output.  The split is the largest
+// that keeps the grid within one wave of 256 workgroups (one per CU), with at
+// least four 64-deep k-blocks per split.
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
-  if (g.epi != EPI_ACCUM) return launch<256, 128, 4, 2>(ctx, g, 1);
-  const int kb = (g.K + BK - 1) / BK;
-  int split = 1;
-  while (tiles * split < 256 && split * 2 <= kb / 8) split *= 2;
+  if (g.epi != EPI_ACCUM) {
+    if (g.a_kmajor && g.b_kmajor) return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
+    return launch<256, 128, 4, 2>(ctx, g, 1);
+  }
+  const int kb = (g.K + 63) / 64;
+  int split = (int)std::max<long>(1, std::min<long>(256 / tiles, std::min(kb / 4, 16)));
   if (g.split_k > 0) split = g.split_k;
   GemmArgs h = g;
   if (split == 1) {
     h.epi = EPI_STORE_ACC;
-    return launch<256, 128, 4, 2>(ctx, h, 1);
+    return launch3<256, 128, 64, 4, 2, 3>(ctx, h, 1);
   }
   tt_scratch_scope scope(ctx);
   void *ws;
@@ -343,7 +595,11 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   h.ldo = g.N;
   h.out_bf16 = false;
   h.bias = nullptr;
-  TT_TRY((launch<256, 128, 4, 2>(ctx, h, split, (size_t)g.M * g.N)));
+  // launch3 may round the split down (whole k-blocks per split); the
+  // partials it does not write must not be summed.
+  const int per = (kb + split - 1) / split;
+  split = (kb + per - 1) / per;
+  TT_TRY((launch3<256, 128, 64, 4, 2, 3>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
   tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0, (split + 2.0) * g.M * g.N * 4.0);

@@ -75,7 +75,8 @@ def test_gradient_accumulation_2_plus_3(ctx, mode, golden):
 
 # ------------------------------------------------------------------ linear
 
-SHAPES = [(64, 3, 32), (300, 200, 130), (256, 256, 384), (129, 64, 17), (1000, 768, 2304)]
+SHAPES = [(64, 3, 32), (300, 200, 130), (256, 256, 384), (129, 64, 17), (1000, 768, 2304),
+          (4160, 768, 768)]
 
 
 @pytest.mark.parametrize("mode", MODES)
