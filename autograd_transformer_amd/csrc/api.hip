@@ -21,13 +21,18 @@ GemmArgs gemm_args() {
 }
 
 // y[M,N] (+)= A[M,K] (k-major, lda) · B where B is W[K,N] row-major (ldb = N),
-// i.e. the forward of a linear layer.
+// i.e. the forward of a linear layer.  Wt, when not NULL, is the same weight
+// stored transposed ([N,K], k-major), which the bf16 GEMM reads faster.
 int linear_fwd_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X, int ldx,
-                    const void *W, const float *bias, int epi, void *out, int ldo, bool out_lowp,
-                    const float *resid, int ldr, void *aux, int ldaux) {
+                    const void *W, const void *Wt, const float *bias, int epi, void *out,
+                    int ldo, bool out_lowp, const float *resid, int ldr, void *aux, int ldaux) {
   GemmArgs g = gemm_args();
   g.A = X; g.lda = ldx; g.a_kmajor = true;
-  g.B = W; g.ldb = N; g.b_kmajor = false;
+  if (Wt) {
+    g.B = Wt; g.ldb = K; g.b_kmajor = true;
+  } else {
+    g.B = W; g.ldb = N; g.b_kmajor = false;
+  }
   g.M = M; g.N = N; g.K = K;
   g.epi = epi; g.out = out; g.ldo = ldo; g.out_bf16 = out_lowp;
   g.bias = bias; g.resid = resid; g.ldr = ldr; g.aux = aux; g.ldx = ldaux;
@@ -59,6 +64,12 @@ int linear_dw_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X
 }
 
 // ------------------------------------------------------------ block pieces
+
+// Transposed bf16 copies of a layer's weight matrices (all NULL: use the
+// [K,N] weights).
+struct LayerWT {
+  const void *w_qkv = nullptr, *w_proj = nullptr, *w_fc = nullptr, *w_fcp = nullptr;
+};
 
 struct LayerBufs {
   void *ln1; float *mean1, *rstd1;
@@ -109,19 +120,20 @@ int alloc_bwd_scratch(tt_ctx *ctx, tt_mode mode, int N, int C, int F, int B, int
 
 // Pre-LN block forward (tinytorch page §3 item 6).
 int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, float eps,
-              const tt_block_w &w, const float *x, float *y, const LayerBufs &s) {
+              const tt_block_w &w, const LayerWT &wt, const float *x, float *y,
+              const LayerBufs &s) {
   const int N = B * T;
   const bool lp = mode == TT_BF16;
   TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, eps, x, w.ln1_g, w.ln1_b, s.ln1, s.mean1, s.rstd1));
-  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, w.w_qkv, w.b_qkv, EPI_STORE, s.qkv,
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, w.w_qkv, wt.w_qkv, w.b_qkv, EPI_STORE, s.qkv,
                          3 * C, lp, nullptr, 0, nullptr, 0));
   TT_TRY(tt_attn_fwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse));
-  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, C, s.att, C, w.w_proj, w.b_proj, EPI_RESID, s.x1, C, false,
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, C, s.att, C, w.w_proj, wt.w_proj, w.b_proj, EPI_RESID, s.x1, C, false,
                          x, C, nullptr, 0));
   TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, eps, s.x1, w.ln2_g, w.ln2_b, s.ln2, s.mean2, s.rstd2));
-  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, F, s.ln2, C, w.w_fc, w.b_fc, EPI_GELU, s.g, F, lp,
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, C, F, s.ln2, C, w.w_fc, wt.w_fc, w.b_fc, EPI_GELU, s.g, F, lp,
                          nullptr, 0, s.h, F));
-  TT_TRY(linear_fwd_gemm(ctx, mode, N, F, C, s.g, F, w.w_fcp, w.b_fcp, EPI_RESID, y, C, false,
+  TT_TRY(linear_fwd_gemm(ctx, mode, N, F, C, s.g, F, w.w_fcp, wt.w_fcp, w.b_fcp, EPI_RESID, y, C, false,
                          s.x1, C, nullptr, 0));
   return TT_OK;
 }
@@ -195,7 +207,7 @@ extern "C" int tt_linear_fwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, con
       break;
     default: return tt_set_error(ctx, TT_EINVAL, "linear_fwd: bad epilogue %d", epilogue);
   }
-  return linear_fwd_gemm(ctx, mode, M, K, N, X, K, W, b, epi, Y, N, mode == TT_BF16, resid, N,
+  return linear_fwd_gemm(ctx, mode, M, K, N, X, K, W, nullptr, b, epi, Y, N, mode == TT_BF16, resid, N,
                          preact, N);
 }
 
@@ -275,9 +287,13 @@ extern "C" int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, voi
 }
 
 // LM head + CE on an [N, ld] logits scratch buffer (ld >= V, ld % 8 == 0).
+// wte_t (nullable): the bf16 token table transposed, [C, V_pad] with
+// V_pad >= round_up(V, 8); dh then reads it k-major.  The reduction runs to
+// round_up(V, 8): the CE pass writes zeros to the gradient's pad columns, so
+// the extra terms vanish.
 static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld, const void *h,
-                          const void *wte, const int32_t *targets, float *loss, float *dh,
-                          float *dwte, void *logits, float *row_loss) {
+                          const void *wte, const void *wte_t, int V_pad, const int32_t *targets,
+                          float *loss, float *dh, float *dwte, void *logits, float *row_loss) {
   const bool lp = mode == TT_BF16;
   GemmArgs g = gemm_args();
   // z = h · wteᵀ
@@ -291,8 +307,14 @@ static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld
   // dh = dz · wte
   g = gemm_args();
   g.A = logits; g.lda = ld; g.a_kmajor = true;
-  g.B = wte; g.ldb = C; g.b_kmajor = false;
-  g.M = N; g.N = C; g.K = V;
+  const int V8 = (V + 7) / 8 * 8;
+  if (wte_t && V8 <= V_pad && V8 <= ld) {
+    g.B = wte_t; g.ldb = V_pad; g.b_kmajor = true;
+    g.M = N; g.N = C; g.K = V8;
+  } else {
+    g.B = wte; g.ldb = C; g.b_kmajor = false;
+    g.M = N; g.N = C; g.K = V;
+  }
   g.epi = EPI_STORE; g.out = dh; g.ldo = C; g.out_bf16 = false;
   TT_TRY(tt_gemm(ctx, mode, g));
   // dwte += dzᵀ · h
@@ -317,8 +339,8 @@ extern "C" int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int 
   void *logits, *rows;
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * ld * esize(mode), &logits));
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * 4, &rows));
-  return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, targets, loss, dh, dwte, logits,
-                        (float *)rows);
+  return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, nullptr, 0, targets, loss, dh, dwte,
+                        logits, (float *)rows);
 }
 
 // ------------------------------------------------------------ block ABI
@@ -371,7 +393,7 @@ extern "C" int tt_block_fwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
                                 hipMemcpyDeviceToDevice, ctx->stream);
   if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_fwd copy: %s", hipGetErrorString(e));
   return layer_fwd(ctx, cfg->mode, cfg->B, cfg->T, cfg->C, cfg->NH, cfg->F, cfg->ln_eps, *w,
-                   saved->xin, y, saved->s);
+                   LayerWT(), saved->xin, y, saved->s);
 }
 
 extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
@@ -423,6 +445,13 @@ struct tt_model {
   std::vector<size_t> off, numel;
   float *w = nullptr, *g = nullptr, *m = nullptr, *v = nullptr;
   bf16_t *lowp = nullptr;
+  // TT_BF16: the weight matrices' bf16 shadows transposed (same slot offsets
+  // as lowp), rebuilt from lowp whenever lowp changes.
+  bf16_t *lowp_t = nullptr;
+  std::vector<tt_tdesc> tdesc;
+  tt_tdesc *tdesc_dev = nullptr;
+  int t_tiles = 0;
+  double t_elems = 0;
   std::vector<LayerBufs> layers;
   std::vector<float *> xs;
   void *lnf = nullptr;
@@ -452,8 +481,21 @@ const void *mat(const tt_model *md, int idx) {
   return md->w + md->off[idx];
 }
 
-void layer_views(const tt_model *md, int l, tt_block_w &w, tt_block_g &gr) {
+const void *mat_t(const tt_model *md, int idx) {
+  return md->lowp_t ? (const void *)(md->lowp_t + md->off[idx]) : nullptr;
+}
+
+// Rebuild the transposed shadows from lowp (one launch for all matrices).
+int refresh_transposed(tt_model *md) {
+  if (!md->lowp_t) return TT_OK;
+  return tt_transpose_bf16(md->ctx, md->tdesc_dev, (int)md->tdesc.size(), md->t_tiles,
+                           md->t_elems);
+}
+
+void layer_views(const tt_model *md, int l, tt_block_w &w, LayerWT &wt, tt_block_g &gr) {
   const int b = P_LAYER0 + PER_LAYER * l;
+  wt.w_qkv = mat_t(md, b + 2); wt.w_proj = mat_t(md, b + 4);
+  wt.w_fc = mat_t(md, b + 8); wt.w_fcp = mat_t(md, b + 10);
   auto W = [&](int i) { return (const float *)(md->w + md->off[b + i]); };
   auto G = [&](int i) { return md->g + md->off[b + i]; };
   w.ln1_g = W(0); w.ln1_b = W(1); w.w_qkv = mat(md, b + 2); w.b_qkv = W(3);
@@ -508,7 +550,33 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   md->g = (float *)alloc(md->n_slots * 4);
   md->m = (float *)alloc(md->n_slots * 4);
   md->v = (float *)alloc(md->n_slots * 4);
-  if (c.mode == TT_BF16) md->lowp = (bf16_t *)alloc(md->n_slots * 2);
+  if (c.mode == TT_BF16) {
+    md->lowp = (bf16_t *)alloc(md->n_slots * 2);
+    md->lowp_t = (bf16_t *)alloc(md->n_slots * 2);
+    // transpose table: wte [V_pad, C], then per layer qkv, proj, fc, fcproj
+    auto addt = [&](int idx, int rows, int cols) {
+      tt_tdesc d;
+      d.src = md->lowp ? md->lowp + md->off[idx] : nullptr;
+      d.dst = md->lowp_t ? md->lowp_t + md->off[idx] : nullptr;
+      d.rows = rows; d.cols = cols; d.tiles_c = (cols + 63) / 64; d.tile0 = md->t_tiles;
+      md->tdesc.push_back(d);
+      md->t_tiles += ((rows + 63) / 64) * d.tiles_c;
+      md->t_elems += (double)rows * cols;
+    };
+    addt(P_WTE, c.V_pad, c.C);
+    for (int l = 0; l < c.L; ++l) {
+      const int b = P_LAYER0 + PER_LAYER * l;
+      addt(b + 2, c.C, 3 * c.C); addt(b + 4, c.C, c.C);
+      addt(b + 8, c.C, c.F); addt(b + 10, c.F, c.C);
+    }
+    md->tdesc_dev = (tt_tdesc *)alloc(md->tdesc.size() * sizeof(tt_tdesc));
+    if (rc == TT_OK) {
+      hipError_t e = hipMemcpyAsync(md->tdesc_dev, md->tdesc.data(),
+                                    md->tdesc.size() * sizeof(tt_tdesc), hipMemcpyHostToDevice,
+                                    ctx->stream);
+      if (e != hipSuccess) rc = tt_set_error(ctx, TT_EHIP, "model_create copy: %s", hipGetErrorString(e));
+    }
+  }
   const int N = c.B_max * c.T_max;
   const size_t es = esize(c.mode);
   md->layers.resize(c.L);
@@ -527,6 +595,7 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   for (float *buf : {md->w, md->g, md->m, md->v})
     if (rc == TT_OK) rc = tt_fill_f32(ctx, buf, md->n_slots, 0.f);
   if (rc == TT_OK && md->lowp) rc = tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp);
+  if (rc == TT_OK) rc = refresh_transposed(md);
   if (rc != TT_OK) {
     ctx->offset = save;
     md->magic = 0;
@@ -575,6 +644,7 @@ extern "C" int tt_model_refresh_shadow(tt_model *md) {
   TT_TRY(check_model(md));
   tt_ctx *ctx = md->ctx;
   if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp));
+  TT_TRY(refresh_transposed(md));
   TT_TRY(tt_fill_f32(ctx, md->m, md->n_slots, 0.f));
   return tt_fill_f32(ctx, md->v, md->n_slots, 0.f);
 }
@@ -596,23 +666,25 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   TT_TRY(tt_embed_fwd(ctx, B, T, C, c.V, tok, md->w + md->off[P_WTE], md->w + md->off[P_WPE],
                       md->xs[0]));
   tt_block_w w;
+  LayerWT wt;
   tt_block_g gr;
   for (int l = 0; l < c.L; ++l) {
-    layer_views(md, l, w, gr);
-    TT_TRY(layer_fwd(ctx, mode, B, T, C, c.NH, c.F, c.ln_eps, w, md->xs[l], md->xs[l + 1],
+    layer_views(md, l, w, wt, gr);
+    TT_TRY(layer_fwd(ctx, mode, B, T, C, c.NH, c.F, c.ln_eps, w, wt, md->xs[l], md->xs[l + 1],
                      md->layers[l]));
   }
   const int lf = p_lnf_g(md);
   TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, c.ln_eps, md->xs[c.L], md->w + md->off[lf],
                                md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
-  TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), targets, loss,
-                        md->sc.dtmp, md->g + md->off[P_WTE], md->logits, md->row_loss));
+  TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), mat_t(md, P_WTE),
+                        c.V_pad, targets, loss, md->sc.dtmp, md->g + md->off[P_WTE], md->logits,
+                        md->row_loss));
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
                                md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
                                lp ? (bf16_t *)md->Rl : nullptr, md->g + md->off[lf],
                                md->g + md->off[lf + 1]));
   for (int l = c.L - 1; l >= 0; --l) {
-    layer_views(md, l, w, gr);
+    layer_views(md, l, w, wt, gr);
     TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, md->Rl, gr,
                      md->sc));
   }
@@ -626,8 +698,9 @@ extern "C" int tt_model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, 
   int rc = check_model(md);
   if (rc != TT_OK) return tt_set_error(ctx, rc, "adamw: bad model handle");
   TT_REQUIRE(ctx, t >= 1, "adamw: t is 1-based");
-  return tt_adamw_flat(ctx, md->w, md->g, md->m, md->v, md->lowp, md->n_slots, lr, beta1, beta2,
-                       eps, wd, t);
+  TT_TRY(tt_adamw_flat(ctx, md->w, md->g, md->m, md->v, md->lowp, md->n_slots, lr, beta1, beta2,
+                       eps, wd, t));
+  return refresh_transposed(md);
 }
 
 extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int32_t *tok,

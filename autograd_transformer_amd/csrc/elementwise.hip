@@ -123,6 +123,58 @@ __global__ void __launch_bounds__(256) cast_kernel(size_t n, const float *__rest
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) d[i] = f2bf(s[i]);
 }
 
+// Batched bf16 transpose: descriptor i maps src [rows, cols] (row pitch cols)
+// to dst [cols, rows] (row pitch rows).  One workgroup per 64 x 64 tile,
+// staged through LDS so that both the reads and the writes are 16-byte
+// coalesced; ragged edges fall back to element accesses.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const tt_tdesc *__restrict__ d,
+                                                             int nd) {
+  __shared__ bf16_t t[64][66];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int i = 0;
+  while (i + 1 < nd && d[i + 1].tile0 <= b) ++i;
+  const bf16_t *src = d[i].src;
+  bf16_t *dst = d[i].dst;
+  const int rows = d[i].rows, cols = d[i].cols;
+  const int local = b - d[i].tile0;
+  const int r0 = (local / d[i].tiles_c) * 64, c0 = (local % d[i].tiles_c) * 64;
+  const bool vec_in = (cols & 7) == 0, vec_out = (rows & 7) == 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + k * 256;
+    const int r = q >> 3, c = (q & 7) * 8;
+    const int gr = r0 + r, gc = c0 + c;
+    if (gr >= rows) continue;
+    if (vec_in && gc + 7 < cols) {
+      const uint4 u = *(const uint4 *)(src + (size_t)gr * cols + gc);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(uint32_t *)&t[r][c + 2 * j] = w[j];
+    } else {
+      for (int j = 0; j < 8; ++j)
+        if (gc + j < cols) t[r][c + j] = src[(size_t)gr * cols + gc + j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + k * 256;
+    const int c = q >> 3, r = (q & 7) * 8;
+    const int gc = c0 + c, gr = r0 + r;
+    if (gc >= cols) continue;
+    if (vec_out && gr + 7 < rows) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)t[r + 2 * j][c] | ((uint32_t)t[r + 2 * j + 1][c] << 16);
+      *(uint4 *)(dst + (size_t)gc * rows + gr) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int j = 0; j < 8; ++j)
+        if (gr + j < rows) dst[(size_t)gc * rows + gr + j] = t[r + j][c];
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) gelu_fwd_kernel(size_t n, const T *__restrict__ x,
                                                        T *__restrict__ y) {
@@ -163,6 +215,15 @@ int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst) {
   tt_prof_scope prof(ctx, "cast_kernel", 0.0, 6.0 * n);
   hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src, dst);
   return tt_check_launch(ctx, "cast");
+}
+
+int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles,
+                      double elems) {
+  if (nd == 0 || total_tiles == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "transpose_bf16_kernel", 0.0, 4.0 * elems);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(total_tiles), dim3(256), 0, ctx->stream, d_dev,
+                     nd);
+  return tt_check_launch(ctx, "transpose_bf16");
 }
 
 int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,

@@ -562,30 +562,53 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
   return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
 }
 
-// Tile: 256 x 128 with 8 waves (two per SIMD).  Products whose operands are
-// both k-major (dX = dY W, the LM-head logits) and all weight gradients take
-// the direct-to-LDS v3 kernel (3-stage ring, BK 64); products with exactly one
-// row-major operand (the forward GEMMs with W stored [K, N], the LM-head dH)
-// take the register-prefetch v2 kernel, which is faster there.
+// Tiles: 256 x 128 or 256 x 256, 8 waves (two per SIMD).  Products whose
+// operands are both k-major (dX = dY W, forward GEMMs against transposed
+// weights, the LM head) and all weight gradients take the direct-to-LDS v3
+// kernel (BK 64); products with exactly one row-major operand take the
+// register-prefetch v2 kernel, which is faster there.  256 x 256 serves
+// products with enough tiles to fill the chip several times over.
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
 // split accumulates with a plain read-modify-write (a workgroup owns its
 // output tile); several splits write fp32 partials to arena scratch, then
-// one coalesced pass adds them into the output.  The split is the largest
-// that keeps the grid within one wave of 256 workgroups (one per CU), with at
-// least four 64-deep k-blocks per split.
+// one coalesced pass adds them into the output.  For each tile size the
+// split is the largest that keeps the grid within one wave of 256
+// workgroups (one per CU) with at least four k-blocks per split; the tile
+// size is then the one with the smaller cost estimate
+//   (k-blocks per split) x (tile area / efficiency) x max(1, workgroups / 256).
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
-  const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
+  const long tm = (g.M + 255) / 256;
+  const long tiles128 = tm * ((g.N + 127) / 128), tiles256 = tm * ((g.N + 255) / 256);
   if (g.epi != EPI_ACCUM) {
-    if (g.a_kmajor && g.b_kmajor) return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
+    if (g.a_kmajor && g.b_kmajor) {
+      if (tiles256 >= 1024) return launch3<256, 256, 64, 4, 2, 2>(ctx, g, 1);
+      return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
+    }
     return launch<256, 128, 4, 2>(ctx, g, 1);
   }
   const int kb = (g.K + 63) / 64;
-  int split = (int)std::max<long>(1, std::min<long>(256 / tiles, std::min(kb / 4, 16)));
-  if (g.split_k > 0) split = g.split_k;
+  auto rounded = [&](int split, int &per) {  // the split launch3 will run
+    per = (kb + split - 1) / split;
+    return (kb + per - 1) / per;
+  };
+  auto choose = [&](long tiles, int &per) {
+    const int s = (int)std::max<long>(1, std::min<long>(256 / tiles, std::min(kb / 4, 16)));
+    return rounded(s, per);
+  };
+  int per128, per256;
+  const int s128 = choose(tiles128, per128), s256 = choose(tiles256, per256);
+  const double cost128 = per128 * 32768.0 * std::max(1.0, tiles128 * s128 / 256.0);
+  const double cost256 = per256 * (65536.0 / 1.1) * std::max(1.0, tiles256 * s256 / 256.0);
+  const bool big = cost256 < cost128;
+  int split = big ? s256 : s128;
+  if (g.split_k > 0) {
+    int per;
+    split = rounded(g.split_k, per);
+  }
   GemmArgs h = g;
   if (split == 1) {
     h.epi = EPI_STORE_ACC;
-    return launch3<256, 128, 64, 4, 2, 3>(ctx, h, 1);
+    return big ? launch3<256, 256, 64, 4, 2, 2>(ctx, h, 1) : launch3<256, 128, 64, 4, 2, 3>(ctx, h, 1);
   }
   tt_scratch_scope scope(ctx);
   void *ws;
@@ -595,11 +618,12 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   h.ldo = g.N;
   h.out_bf16 = false;
   h.bias = nullptr;
-  // launch3 may round the split down (whole k-blocks per split); the
-  // partials it does not write must not be summed.
-  const int per = (kb + split - 1) / split;
-  split = (kb + per - 1) / per;
-  TT_TRY((launch3<256, 128, 64, 4, 2, 3>(ctx, h, split, (size_t)g.M * g.N)));
+  // split is already what launch3 runs (whole k-blocks per split), so the
+  // reduction sums exactly the partials written.
+  if (big)
+    TT_TRY((launch3<256, 256, 64, 4, 2, 2>(ctx, h, split, (size_t)g.M * g.N)));
+  else
+    TT_TRY((launch3<256, 128, 64, 4, 2, 3>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
   tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0, (split + 2.0) * g.M * g.N * 4.0);

@@ -184,6 +184,16 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
 int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out);
 int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v);
 int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst);
+// One 64 x 64 tile range of a batched bf16 transpose (src [rows, cols] ->
+// dst [cols, rows]); tile0 is the first workgroup of this matrix, tiles are
+// numbered row-major with tiles_c = ceil(cols / 64) per tile row.
+struct tt_tdesc {
+  const bf16_t *src;
+  bf16_t *dst;
+  int rows, cols, tiles_c, tile0;
+};
+// d_dev: device copy of the descriptor table, ordered by tile0.
+int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles, double elems);
 int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      void *out, float *lse);
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,

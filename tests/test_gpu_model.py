@@ -57,17 +57,7 @@ def test_small_model_train_step(mode):
     p64 = {k: v.astype(np.float64) for k, v in params.items()}
     l_ref, g_ref = og.model_fwd_bwd(p64, tok, tgt, cfg, mode)
     assert abs(host(loss)[0] - l_ref) / l_ref <= tol(mode)
-    errs, kb = {}, {}
-    for k in g_ref:
-        got = g[k][: g_ref[k].shape[0]] if k == "wte" else g[k]
-        rest, rest_ref, key = split_key_bias(k, got, g_ref[k], 128)
-        errs[k] = rel_l2(rest, rest_ref)
-        if key is not None:
-            kb[k] = np.linalg.norm(key) / np.linalg.norm(rest_ref)
-    assert np.all(g["wte"][97:] == 0)           # padding rows get no gradient
-    bad = {k: e for k, e in errs.items() if not e <= tol(mode)}
-    assert not bad, bad
-    assert max(kb.values()) <= KEY_BIAS_NOISE[mode], kb
+    _check_grads(g, g_ref, mode)
     # AdamW on the model's gradient buffer, t = 1
     tt.tt_model_adamw(ctx, model, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"], 1)
     sync()
@@ -85,8 +75,31 @@ def test_small_model_train_step(mode):
     if mode == "bf16":
         wl = host(model.tensor("h0.w_fc", "w_lowp"))
         assert np.array_equal(wl, oracle.round_bf16(host(model.tensor("h0.w_fc", "w"))))
+    # A second forward/backward runs on the updated weights: every low-precision
+    # copy the kernels read (shadow and transposed shadow) follows the master.
+    w1 = {k: host(model.tensor(k, "w")).astype(np.float64) for k in params}
+    w1["wte"] = w1["wte"][:97]
+    tt.tt_model_fwd_bwd(ctx, model, B, T, tok_d, tgt_d, loss)
+    sync()
+    l2_ref, g2_ref = og.model_fwd_bwd(w1, tok, tgt, cfg, mode)
+    assert abs(host(loss)[0] - l2_ref) / l2_ref <= tol(mode)
+    _check_grads(grads_of(model), g2_ref, mode)
     model.close()
     ctx.close()
+
+
+def _check_grads(g, g_ref, mode):
+    errs, kb = {}, {}
+    for k in g_ref:
+        got = g[k][: g_ref[k].shape[0]] if k == "wte" else g[k]
+        rest, rest_ref, key = split_key_bias(k, got, g_ref[k], 128)
+        errs[k] = rel_l2(rest, rest_ref)
+        if key is not None:
+            kb[k] = np.linalg.norm(key) / np.linalg.norm(rest_ref)
+    assert np.all(g["wte"][97:] == 0)           # padding rows get no gradient
+    bad = {k: e for k, e in errs.items() if not e <= tol(mode)}
+    assert not bad, bad
+    assert max(kb.values()) <= KEY_BIAS_NOISE[mode], kb
 
 
 def test_train_step_matches_fwd_bwd_then_adamw():
