@@ -12,7 +12,15 @@
 //    at 4 elements of token row t0 + s/4, columns c0 + 4(s%4); lane j then
 //    holds column c0 + j of rows t0 .. t0+3), in the permuted slot order of
 //    the accumulator it is multiplied with (rows 4g..4g+3 and 16+4g..+3);
-//  * probabilities and dS are packed to bf16 with v_cvt_pk_bf16_f32.
+//  * probabilities and dS are packed to bf16 with v_cvt_pk_bf16_f32;
+//  * the causal mask is applied only on tiles that cross the diagonal (a
+//    compile-time specialised tile body), exp2 is the bare v_exp_f32;
+//  * forward: the running row maximum is moved (and O, l rescaled) only when
+//    a row's new maximum exceeds it by more than RESCALE (log2 units), so
+//    unnormalised probabilities stay below 2^RESCALE; the final O / l and
+//    lse = m + log2 l are the same quotient and log-sum.
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace {
@@ -26,6 +34,9 @@ constexpr int LDT = HS + 8;            // LDS row: 144 bytes
 constexpr uint32_t OOB = 0x7ffffff0u;  // buffer offset past every tensor (host checks sizes)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SL2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) folded into exp2
+constexpr float RESCALE = 8.0f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)bytes, 0x00020000);
@@ -136,41 +147,62 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
         for (int qs = 0; qs < 2; ++qs)
           s[j][qs] = mfma(k_1, qf[qs][1], mfma(k_0, qf[qs][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
       }
-      const bool diag = k0 + 64 > q0;
+      auto softmax = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float mx[2];
+        bool grow = false;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const int q = q0 + qs * 16 + lr;
-        float mx = -INFINITY;
+        for (int qs = 0; qs < 2; ++qs) {
+          const int q = q0 + qs * 16 + lr;
+          float m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + j * 16 + lg * 4 + r;
-            float v = s[j][qs][r];
-            if (diag && (key > q || key >= T)) v = -INFINITY;
-            s[j][qs][r] = v;
-            mx = fmaxf(mx, v);
+            for (int r = 0; r < 4; ++r) {
+              float v = s[j][qs][r];
+              if constexpr (MASK) {
+                const int key = k0 + j * 16 + lg * 4 + r;
+                if (key > q || key >= T) v = -INFINITY;
+                s[j][qs][r] = v;
+              }
+              m = fmaxf(m, v);
+            }
+          m = fmaxf(m, __shfl_xor(m, 16, 64));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          mx[qs] = m * SL2;
+          grow |= mx[qs] > mrow[qs] + RESCALE;
+        }
+        if (__ballot(grow)) {
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) {
+            const float mnew = fmaxf(mrow[qs], mx[qs]);
+            const float alpha = ex2(mrow[qs] - mnew);
+            lrow[qs] *= alpha;
+            mrow[qs] = mnew;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[d][qs][r] *= alpha;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[qs], mx * SL2);
-        const float alpha = exp2f(mrow[qs] - mnew);
-        float ps = 0.f;
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int qs = 0; qs < 2; ++qs) {
+          float ps = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(fmaf(s[j][qs][r], SL2, -mnew));
-            s[j][qs][r] = p;
-            ps += p;
-          }
-        lrow[qs] = lrow[qs] * alpha + ps;
-        mrow[qs] = mnew;
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[d][qs][r] *= alpha;
-      }
+            for (int r = 0; r < 4; ++r) {
+              const float pv = ex2(fmaf(s[j][qs][r], SL2, -mrow[qs]));
+              s[j][qs][r] = pv;
+              ps += pv;
+            }
+          lrow[qs] += ps;
+        }
+      };
+      if (k0 + 64 > q0)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         bf16x8_t pb[2];
@@ -219,7 +251,7 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
                       bf16_t *__restrict__ dqkv, int nkb, uint32_t qkv_bytes, uint32_t do_bytes) {
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][64 * LDT];
   __shared__ __attribute__((aligned(16))) bf16_t Os[2][64 * LDT];
-  __shared__ float ls[2][64], ds[2][64];
+  __shared__ __attribute__((aligned(16))) float ls[2][64], ds[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
   const int kb = blockIdx.x % nkb;
@@ -273,21 +305,34 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
     if (qb + 1 < nqb) fetch(q0 + 64);
     const bf16_t *qs_t = Qs[cur], *os_t = Os[cur];
     f32x4_t p[4], dsv[4];
+    // Rows past T read zero Q and lse = +inf, so their P is 0; keys past T
+    // have zero K and V and only feed their own (unstored) dK, dV columns.
+    auto tile = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int qs = 0; qs < 4; ++qs) {
-      const bf16x8_t a0 = row_frag(qs_t, qs * 16, 0, lr, lg), a1 = row_frag(qs_t, qs * 16, 32, lr, lg);
-      const bf16x8_t o0 = row_frag(os_t, qs * 16, 0, lr, lg), o1 = row_frag(os_t, qs * 16, 32, lr, lg);
-      const f32x4_t sacc = mfma(a1, kf[1], mfma(a0, kf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-      const f32x4_t dpacc = mfma(o1, vf[1], mfma(o0, vf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      for (int qs = 0; qs < 4; ++qs) {
+        const bf16x8_t a0 = row_frag(qs_t, qs * 16, 0, lr, lg), a1 = row_frag(qs_t, qs * 16, 32, lr, lg);
+        const bf16x8_t o0 = row_frag(os_t, qs * 16, 0, lr, lg), o1 = row_frag(os_t, qs * 16, 32, lr, lg);
+        const f32x4_t sacc = mfma(a1, kf[1], mfma(a0, kf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t dpacc = mfma(o1, vf[1], mfma(o0, vf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const float4 l4 = *(const float4 *)&ls[cur][qs * 16 + lg * 4];
+        const float4 d4 = *(const float4 *)&ds[cur][qs * 16 + lg * 4];
+        const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ql = qs * 16 + lg * 4 + r;
-        const int q = q0 + ql;
-        const float pv = (key > q || key >= T) ? 0.f : exp2f(fmaf(sacc[r], SL2, -ls[cur][ql]));
-        p[qs][r] = pv;
-        dsv[qs][r] = pv * (dpacc[r] - ds[cur][ql]);
+        for (int r = 0; r < 4; ++r) {
+          float pv = ex2(fmaf(sacc[r], SL2, -lq[r]));
+          if constexpr (MASK) {
+            if (key > q0 + qs * 16 + lg * 4 + r) pv = 0.f;
+          }
+          p[qs][r] = pv;
+          dsv[qs][r] = pv * (dpacc[r] - dq4[r]);
+        }
       }
-    }
+    };
+    if (qb == kb)
+      tile(std::true_type{});
+    else
+      tile(std::false_type{});
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const bf16x8_t pb = pack8(p[2 * t2], p[2 * t2 + 1]);
@@ -362,20 +407,31 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
     }
     if (k0 <= qw0 + 15) {
       const bf16_t *ks = Ks[cur], *vs = Vs[cur];
+      // Keys past T have zero K, V: their dS multiplies a zero K row.  Lanes
+      // with q >= T compute finite values that are never stored.
       f32x4_t dsv[4];
+      auto tile = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t sacc = mfma(row_frag(ks, j * 16, 32, lr, lg), qf[1],
-                                  mfma(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-        const f32x4_t dpacc = mfma(row_frag(vs, j * 16, 32, lr, lg), of[1],
-                                   mfma(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t sacc = mfma(row_frag(ks, j * 16, 32, lr, lg), qf[1],
+                                    mfma(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          const f32x4_t dpacc = mfma(row_frag(vs, j * 16, 32, lr, lg), of[1],
+                                     mfma(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + j * 16 + lg * 4 + r;
-          const float pv = (key > q || key >= T || q >= T) ? 0.f : exp2f(fmaf(sacc[r], SL2, -lq));
-          dsv[j][r] = pv * (dpacc[r] - Dq);
+          for (int r = 0; r < 4; ++r) {
+            float pv = ex2(fmaf(sacc[r], SL2, -lq));
+            if constexpr (MASK) {
+              if (k0 + j * 16 + lg * 4 + r > q) pv = 0.f;
+            }
+            dsv[j][r] = pv * (dpacc[r] - Dq);
+          }
         }
-      }
+      };
+      if (k0 + 64 > qw0)
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const bf16x8_t sb = pack8(dsv[2 * t2], dsv[2 * t2 + 1]);
