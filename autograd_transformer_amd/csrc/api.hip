@@ -39,16 +39,18 @@ int linear_fwd_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *
   return tt_gemm(ctx, mode, g);
 }
 
-// dX[M,K] = dY[M,N] · Wᵀ  (W [K,N]), with an epilogue.
+// dX[M,K] = dY[M,N] · Wᵀ  (W [K,N]), with an epilogue; colsum (nullable)
+// accumulates the column sums of the stored dX.
 int linear_dx_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *dY, int ldy,
                    const void *W, int epi, void *out, int ldo, bool out_lowp, void *aux,
-                   int ldaux) {
+                   int ldaux, float *colsum = nullptr) {
   GemmArgs g = gemm_args();
   g.A = dY; g.lda = ldy; g.a_kmajor = true;
   g.B = W; g.ldb = N; g.b_kmajor = true;
   g.M = M; g.N = K; g.K = N;
   g.epi = epi; g.out = out; g.ldo = ldo; g.out_bf16 = out_lowp;
   g.aux = aux; g.ldx = ldaux;
+  g.colsum = colsum;
   return tt_gemm(ctx, mode, g);
 }
 
@@ -140,29 +142,35 @@ int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, flo
 
 // Block backward, in place on the residual gradient R (fp32) and its GEMM
 // operand copy Rl (bf16 copy in TT_BF16, == R in TT_F32).  On entry R holds
-// dL/dy; on return it holds dL/dx.
+// dL/dy; on return it holds dL/dx.  The bias gradient of the MLP
+// down-projection is the column sum of Rl on entry: computed here when
+// fcp_bias_here, else already accumulated by whoever produced R (the
+// LayerNorm backward above this block).  dsum_below (nullable) receives the
+// column sums of the returned Rl, i.e. the down-projection bias gradient of
+// the block below.
 int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
               const tt_block_w &w, const LayerBufs &s, const float *x, float *R, void *Rl,
-              const tt_block_g &gr, const BwdScratch &sc) {
+              const tt_block_g &gr, const BwdScratch &sc, bool fcp_bias_here, float *dsum_below) {
   const int N = B * T;
   const bool lp = mode == TT_BF16;
   bf16_t *Rb = lp ? (bf16_t *)Rl : nullptr;
-  // MLP down-projection: dh = (dy · W_fpᵀ) * gelu'(h); dW_fp += gᵀ dy; db_fp.
-  TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, Rl, C, w.w_fcp, EPI_GELU_BWD, sc.dh, F, lp, s.h, F));
+  // MLP down-projection: dh = (dy · W_fpᵀ) * gelu'(h), whose column sums are
+  // the up-projection's bias gradient; dW_fp += gᵀ dy; db_fp.
+  TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, Rl, C, w.w_fcp, EPI_GELU_BWD, sc.dh, F, lp, s.h, F,
+                        gr.b_fc));
   TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, Rl, C, gr.w_fcp));
-  TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_fcp));
+  if (fcp_bias_here) TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_fcp));
   // MLP up-projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, sc.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
                         nullptr, 0));
   TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, sc.dh, F, gr.w_fc));
-  TT_TRY(tt_colsum(ctx, lp, N, F, F, sc.dh, gr.b_fc));
-  // LN2 backward + residual: R = R + LN2_bwd(dtmp).
+  // LN2 backward + residual: R = R + LN2_bwd(dtmp); its column sums are the
+  // attention projection's bias gradient.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R, Rb,
-                               gr.ln2_g, gr.ln2_b));
+                               gr.ln2_g, gr.ln2_b, gr.b_proj));
   // Attention projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, Rl, C, w.w_proj, EPI_STORE, sc.datt, C, lp, nullptr, 0));
   TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, Rl, C, gr.w_proj));
-  TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_proj));
   // Attention.
   TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, sc.dqkv, sc.Dv));
   // QKV projection.
@@ -172,7 +180,7 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, sc.dqkv, gr.b_qkv));
   // LN1 backward + residual.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R, Rb,
-                               gr.ln1_g, gr.ln1_b));
+                               gr.ln1_g, gr.ln1_b, dsum_below));
   return TT_OK;
 }
 
@@ -423,7 +431,7 @@ extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
     TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl));
   }
   return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, Rl,
-                   *g, sc);
+                   *g, sc, true, nullptr);
 }
 
 extern "C" void tt_block_saved_destroy(tt_block_saved *saved) {
@@ -679,14 +687,17 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), mat_t(md, P_WTE),
                         c.V_pad, targets, loss, md->sc.dtmp, md->g + md->off[P_WTE], md->logits,
                         md->row_loss));
+  // Each LayerNorm backward also sums its output's columns into the
+  // down-projection bias gradient of the block below it.
+  auto fcp_bias = [&](int l) { return md->g + md->off[P_LAYER0 + PER_LAYER * l + 11]; };
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
                                md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
                                lp ? (bf16_t *)md->Rl : nullptr, md->g + md->off[lf],
-                               md->g + md->off[lf + 1]));
+                               md->g + md->off[lf + 1], fcp_bias(c.L - 1)));
   for (int l = c.L - 1; l >= 0; --l) {
     layer_views(md, l, w, wt, gr);
     TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, md->Rl, gr,
-                     md->sc));
+                     md->sc, false, l > 0 ? fcp_bias(l - 1) : nullptr));
   }
   return tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
                       md->g + md->off[P_WPE]);

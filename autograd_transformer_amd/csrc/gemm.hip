@@ -340,7 +340,7 @@ gemm_kernel(GemmParams p) {
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool A_KM, bool B_KM, bool VECLD>
 int launch_gemm(tt_ctx *ctx, const GemmArgs &g, int split) {
-  GemmParams p;
+  GemmParams p{};
   p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
@@ -392,7 +392,21 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
     while (tiles * split < 512 && split * 2 <= kb / 4) split *= 2;
     if (g.split_k > 0) split = g.split_k;
   }
-  if (mode == TT_BF16 && vec && tt_gemm_bf16_ok(g)) return tt_gemm_bf16(ctx, g);
-  if (mode == TT_BF16) return dispatch_layout<bf16_t, 128, 128, 64, 2, 2>(ctx, g, split, vec);
-  return dispatch_layout<float, 128, 128, 32, 2, 2>(ctx, g, split, vec);
+  // Column sums of the output (g.colsum) are fused into the epilogue of the
+  // direct-to-LDS bf16 kernel; every other path sums the stored output after.
+  const bool fast = mode == TT_BF16 && vec && tt_gemm_bf16_ok(g);
+  const bool fused_sum = fast && g.epi != EPI_ACCUM && g.a_kmajor && g.b_kmajor;
+  GemmArgs h = g;
+  if (!fused_sum) h.colsum = nullptr;
+  if (fast)
+    TT_TRY(tt_gemm_bf16(ctx, h));
+  else if (mode == TT_BF16)
+    TT_TRY((dispatch_layout<bf16_t, 128, 128, 64, 2, 2>(ctx, h, split, vec)));
+  else
+    TT_TRY((dispatch_layout<float, 128, 128, 32, 2, 2>(ctx, h, split, vec)));
+  if (g.colsum && !fused_sum) {
+    TT_REQUIRE(ctx, g.epi == EPI_STORE || g.epi == EPI_GELU_BWD, "gemm: column sums of this epilogue");
+    return tt_colsum(ctx, g.out_bf16, g.M, g.N, g.ldo, g.out, g.colsum);
+  }
+  return TT_OK;
 }

@@ -245,7 +245,7 @@ gemm_bf16_kernel(GemmParams p) {
 
 template <int BM, int BN, int WM, int WN>
 int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
-  GemmParams p;
+  GemmParams p{};
   p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
@@ -465,6 +465,7 @@ gemm_bf16_v3_kernel(GemmParams p) {
       if (n + 2 < nv) bias.z = p.bias[n + 2];
     }
   }
+  float4 csum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int pass = 0; pass < WM; ++pass) {
     if (pass > 0) __syncthreads();
@@ -483,14 +484,29 @@ gemm_bf16_v3_kernel(GemmParams p) {
       if (m >= p.M || n >= nv) continue;
       float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
       v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
-      epilogue4(p, m, n, v, nv - n);
+      const float4 st = epilogue4(p, m, n, v, nv - n);
+      csum.x += st.x; csum.y += st.y; csum.z += st.z; csum.w += st.w;
+    }
+  }
+  // Column sums of the stored tile (bias gradients): combine the RPP row
+  // groups in LDS, then one atomic per column and workgroup.
+  if (p.colsum) {
+    __syncthreads();
+    float *red = (float *)smem_raw;   // [RPP][BN]
+    *(float4 *)&red[(tid / TPR) * BN + cc] = csum;
+    __syncthreads();
+    for (int c = tid; c < BN; c += NT) {
+      float t = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) t += red[r * BN + c];
+      if (n0 + c < nv) unsafeAtomicAdd(&p.colsum[n0 + c], t);
     }
   }
 }
 
 template <int BM, int BN, int BKV, int WM, int WN, int NS>
 int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
-  GemmParams p;
+  GemmParams p{};
   p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
@@ -498,6 +514,7 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
   p.vec_out = gemm_vec_out(g) ? 1 : 0;
   p.out_zstride = out_zstride;
+  p.colsum = split == 1 ? g.colsum : nullptr;
   p.a_bytes = (uint32_t)gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda);
   p.b_bytes = (uint32_t)gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb);
   p.tiles_m = (g.M + BM - 1) / BM;
@@ -580,6 +597,8 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   const long tm = (g.M + 255) / 256;
   const long tiles128 = tm * ((g.N + 127) / 128), tiles256 = tm * ((g.N + 255) / 256);
   if (g.epi != EPI_ACCUM) {
+    if (g.colsum && !(g.a_kmajor && g.b_kmajor))
+      return tt_set_error(ctx, TT_EINVAL, "gemm_bf16: column sums need the k-major kernel");
     if (g.a_kmajor && g.b_kmajor) {
       if (tiles256 >= 1024) return launch3<256, 256, 64, 4, 2, 2>(ctx, g, 1);
       return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);

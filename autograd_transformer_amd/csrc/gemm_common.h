@@ -20,6 +20,7 @@ struct GemmParams {
   int vec_out;   // output/aux/resid rows allow 4-wide vector access
   uint32_t a_bytes, b_bytes;  // operand extents for buffer range checks
   size_t out_zstride;         // split-K partials: output offset per blockIdx.z (elements)
+  float *colsum;              // nullable: += column sums of the stored output (v3 kernel)
 };
 
 __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
@@ -32,8 +33,17 @@ __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int 
 // Epilogue for 4 consecutive columns n..n+3 of row m (only the first `cnt`
 // of them exist when the tile sticks out of the matrix).  Vector accesses
 // need 16-byte (f32) / 8-byte (bf16) aligned rows, which the host checks
-// (p.vec_out); otherwise elements are handled one by one.
-__device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
+// (p.vec_out); otherwise elements are handled one by one.  Returns the values
+// as stored for EPI_STORE / EPI_GELU_BWD (bf16-rounded when the output is
+// bf16, 0 past cnt), for column sums.
+__device__ __forceinline__ float4 round_stored(const GemmParams &p, const float *a, int lim) {
+  float r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = q < lim ? (p.out_bf16 ? bf2f(f2bf(a[q])) : a[q]) : 0.f;
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
+__device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
   const bool full = cnt >= 4 && p.vec_out;
   float a[4] = {v.x, v.y, v.z, v.w};
   const int lim = cnt < 4 ? cnt : 4;
@@ -60,7 +70,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, flo
       } else {
         for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
       }
-      break;
+      return round_stored(p, a, lim);
     }
     case EPI_RESID: {
       const float *rp = p.resid + (size_t)m * p.ldr + n;
@@ -95,7 +105,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, flo
             make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
       else
         for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
-      break;
+      return round_stored(p, a, lim);
     }
     case EPI_ACCUM: {
       float *op = (float *)p.out + (size_t)m * p.ldo + n;
@@ -108,6 +118,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, flo
       break;
     }
   }
+  return make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 

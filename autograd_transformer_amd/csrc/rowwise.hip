@@ -75,88 +75,219 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(int N, int C, float 
 //   dgamma += sum_rows dy * xhat ; dbeta += sum_rows dy.
 // A block of 4 waves handles ROWS_PER_BLOCK rows; gamma/beta partials are
 // kept per lane in registers and flushed with one atomic per column.
-constexpr int LNB_ROWS = 32;
+// LayerNorm backward: lnb_rpw rows per wave with all of a wave's row loads
+// issued before any arithmetic.  Column partials of dgamma = sum dy * xhat,
+// dbeta = sum dy and the column sums of the produced dx (as stored:
+// bf16-rounded when a bf16 copy is written) go to a per-wave LDS slice
+// (plain stores: LDS float atomics are far slower), are summed over the
+// workgroup's waves and written to part[blockIdx.x][3][C];
+// layernorm_bwd_reduce_kernel then adds the workgroups' partials up.
+constexpr uint32_t LN_OOB = 0x7ffffff0u;   // past every range below
+// p and bytes must be wave-uniform; readfirstlane makes that visible to the
+// compiler (a resource it believes divergent costs a waterfall loop per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ln_rsrc(const float *p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ float4 ln_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
-template <int LN_MAXV>
-__global__ void __launch_bounds__(256) layernorm_bwd_kernel(
+// waves per workgroup and rows per wave by row width (NV float4 per lane):
+// the LDS slices (waves x 3 x NV*64 float4) stay within 160 KB.
+__host__ __device__ constexpr int lnb_waves(int nv) { return nv <= 4 ? 4 : (nv <= 8 ? 2 : 1); }
+__host__ __device__ constexpr int lnb_rpw(int nv) { return nv <= 3 ? 2 : 1; }
+
+template <int NV>
+__global__ void __launch_bounds__(64 * lnb_waves(NV)) layernorm_bwd_kernel(
     int N, int C, const float *__restrict__ x, const float *__restrict__ mean,
     const float *__restrict__ rstd, const float *__restrict__ gamma, const float *__restrict__ dy,
-    const float *dres, float *dx, bf16_t *__restrict__ dx_bf16, float *__restrict__ dgamma,
-    float *__restrict__ dbeta) {
+    const float *dres, float *dx, bf16_t *__restrict__ dx_bf16, float *__restrict__ part) {
+  constexpr int LNB_WAVES = lnb_waves(NV);
+  __shared__ float4 red[LNB_WAVES][3][NV * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nv = C >> 2;
   const float4 *g4 = (const float4 *)gamma;
-  float4 pg[LN_MAXV], pb[LN_MAXV];
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float inv_c = 1.0f / (float)C;
+  constexpr int LNB_RPW = lnb_rpw(NV);
+  float4 pg[NV], pb[NV], ps[NV];
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    pg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    pb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < NV; ++i) {
+    pg[i] = z4; pb[i] = z4; ps[i] = z4;
   }
-  const int r0 = blockIdx.x * LNB_ROWS;
-  for (int rr = wave; rr < LNB_ROWS; rr += 4) {
-    const int row = r0 + rr;
+  // wave-uniform (readfirstlane: the compiler cannot see that threadIdx.x >> 6
+  // is uniform, and a per-lane buffer resource would need a waterfall loop)
+  const int rbase = __builtin_amdgcn_readfirstlane((blockIdx.x * LNB_WAVES + wave) * LNB_RPW);
+  // Branch-free loads: buffer resources spanning this wave's valid rows;
+  // columns past C take an out-of-range offset and read zero.
+  const int nrows = max(0, min(LNB_RPW, N - rbase));
+  const size_t base = (size_t)rbase * C;
+  const uint32_t bytes = (uint32_t)nrows * C * 4;
+  const __amdgpu_buffer_rsrc_t rx = ln_rsrc(x + base, bytes), rd = ln_rsrc(dy + base, bytes),
+                               rr = ln_rsrc(dres ? dres + base : x, dres ? bytes : 0u);
+  float4 xv[LNB_RPW][NV], dv[LNB_RPW][NV], rv[LNB_RPW][NV];
+  float mu[LNB_RPW], rs[LNB_RPW];
+#pragma unroll
+  for (int r = 0; r < LNB_RPW; ++r) {
+    const int row = min(rbase + r, N - 1);
+    mu[r] = mean[row];
+    rs[r] = rstd[row];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + i * 64;
+      const uint32_t off = c < nv ? (uint32_t)(r * C + 4 * c) * 4u : LN_OOB;
+      xv[r][i] = ln_load4(rx, off);
+      dv[r][i] = ln_load4(rd, off);
+      rv[r][i] = ln_load4(rr, off);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < LNB_RPW; ++r) {
+    const int row = rbase + r;
     if (row >= N) break;
-    const float mu = mean[row], rs = rstd[row];
-    const float4 *xr = (const float4 *)(x + (size_t)row * C);
-    const float4 *dyr = (const float4 *)(dy + (size_t)row * C);
-    float4 xh[LN_MAXV], gg[LN_MAXV];
+    float4 xh[NV], gg[NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-      int c = lane + i * 64;
-      if (c < nv) {
-        float4 xv = xr[c], d = dyr[c], ga = g4[c];
-        xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-        gg[i] = make_float4(d.x * ga.x, d.y * ga.y, d.z * ga.z, d.w * ga.w);
-        s1 += (gg[i].x + gg[i].y) + (gg[i].z + gg[i].w);
-        s2 += (gg[i].x * xh[i].x + gg[i].y * xh[i].y) + (gg[i].z * xh[i].z + gg[i].w * xh[i].w);
-        pg[i].x += d.x * xh[i].x; pg[i].y += d.y * xh[i].y;
-        pg[i].z += d.z * xh[i].z; pg[i].w += d.w * xh[i].w;
-        pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
-      }
+    for (int i = 0; i < NV; ++i) {
+      const float4 d = dv[r][i];
+      const float4 xq = xv[r][i];
+      const float4 ga = lane + i * 64 < nv ? g4[lane + i * 64] : z4;   // cached
+      xh[i] = make_float4((xq.x - mu[r]) * rs[r], (xq.y - mu[r]) * rs[r], (xq.z - mu[r]) * rs[r],
+                          (xq.w - mu[r]) * rs[r]);
+      gg[i] = make_float4(d.x * ga.x, d.y * ga.y, d.z * ga.z, d.w * ga.w);
+      s1 += (gg[i].x + gg[i].y) + (gg[i].z + gg[i].w);
+      s2 += (gg[i].x * xh[i].x + gg[i].y * xh[i].y) + (gg[i].z * xh[i].z + gg[i].w * xh[i].w);
+      pg[i].x += d.x * xh[i].x; pg[i].y += d.y * xh[i].y;
+      pg[i].z += d.z * xh[i].z; pg[i].w += d.w * xh[i].w;
+      pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
-    const float m1 = wave_sum(s1) / (float)C;
-    const float m2 = wave_sum(s2) / (float)C;
-    float4 *dxr = (float4 *)(dx + (size_t)row * C);
-    const float4 *drr = dres ? (const float4 *)(dres + (size_t)row * C) : nullptr;
+    const float m1 = wave_sum(s1) * inv_c;
+    const float m2 = wave_sum(s2) * inv_c;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-      int c = lane + i * 64;
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + i * 64;
       if (c < nv) {
         float4 o;
-        o.x = rs * (gg[i].x - m1 - xh[i].x * m2);
-        o.y = rs * (gg[i].y - m1 - xh[i].y * m2);
-        o.z = rs * (gg[i].z - m1 - xh[i].z * m2);
-        o.w = rs * (gg[i].w - m1 - xh[i].w * m2);
-        if (drr) {
-          float4 r = drr[c];
-          o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+        o.x = rs[r] * (gg[i].x - m1 - xh[i].x * m2) + rv[r][i].x;
+        o.y = rs[r] * (gg[i].y - m1 - xh[i].y * m2) + rv[r][i].y;
+        o.z = rs[r] * (gg[i].z - m1 - xh[i].z * m2) + rv[r][i].z;
+        o.w = rs[r] * (gg[i].w - m1 - xh[i].w * m2) + rv[r][i].w;
+        ((float4 *)dx)[(size_t)row * nv + c] = o;
+        if (dx_bf16) {
+          const uint32_t lo = pack_bf2(o.x, o.y), hi = pack_bf2(o.z, o.w);
+          ((uint2 *)dx_bf16)[(size_t)row * nv + c] = make_uint2(lo, hi);
+          o = make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
         }
-        dxr[c] = o;
-        if (dx_bf16)
-          ((uint2 *)(dx_bf16 + (size_t)row * C))[c] =
-              make_uint2(pack_bf2(o.x, o.y), pack_bf2(o.z, o.w));
+        ps[i].x += o.x; ps[i].y += o.y; ps[i].z += o.z; ps[i].w += o.w;
       }
     }
   }
-  // Combine the 4 waves' partials through LDS, then one atomic per column.
-  __shared__ float red[2][4096];
-  for (int i = threadIdx.x; i < C; i += 256) { red[0][i] = 0.f; red[1][i] = 0.f; }
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    int c = lane + i * 64;
-    if (c < nv) {
-      atomicAdd(&red[0][4 * c + 0], pg[i].x); atomicAdd(&red[0][4 * c + 1], pg[i].y);
-      atomicAdd(&red[0][4 * c + 2], pg[i].z); atomicAdd(&red[0][4 * c + 3], pg[i].w);
-      atomicAdd(&red[1][4 * c + 0], pb[i].x); atomicAdd(&red[1][4 * c + 1], pb[i].y);
-      atomicAdd(&red[1][4 * c + 2], pb[i].z); atomicAdd(&red[1][4 * c + 3], pb[i].w);
-    }
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + i * 64;
+    red[wave][0][c] = pg[i];
+    red[wave][1][c] = pb[i];
+    red[wave][2][c] = ps[i];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < C; i += 256) {
-    if (dgamma) unsafeAtomicAdd(&dgamma[i], red[0][i]);
-    if (dbeta) unsafeAtomicAdd(&dbeta[i], red[1][i]);
+  float4 *out = (float4 *)(part + (size_t)blockIdx.x * 3 * C);
+  for (int f = threadIdx.x; f < 3 * nv; f += 64 * LNB_WAVES) {
+    const int k = f / nv, c = f % nv;
+    float4 a = red[0][k][c];
+#pragma unroll
+    for (int w = 1; w < LNB_WAVES; ++w) {
+      const float4 b = red[w][k][c];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    out[f] = a;
+  }
+}
+
+// out_k[c] += sum_g part[g][k][c] for k = 0 (dgamma), 1 (dbeta), 2 (dx
+// column sums); a NULL output is skipped.  Thread: one float4 of the [3][C]
+// partial row, one of 4 row groups of a 32-row slice of the partials; LDS
+// combines the groups, then one atomic per element and slice.
+constexpr int LNR_SLICE = 32;
+
+__global__ void __launch_bounds__(256) layernorm_bwd_reduce_kernel(int G, int C,
+                                                                   const float *__restrict__ part,
+                                                                   float *dg, float *db,
+                                                                   float *dsum) {
+  const int nf = 3 * C / 4;
+  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int grp = threadIdx.x >> 6;
+  const int g0 = blockIdx.y * LNR_SLICE, g1 = min(G, g0 + LNR_SLICE);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (f < nf)
+    for (int g = g0 + grp; g < g1; g += 4) {
+      const float4 v = ((const float4 *)(part + (size_t)g * 3 * C))[f];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+  __shared__ float4 red[4][64];
+  red[grp][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (grp != 0 || f >= nf) return;
+  const float4 a = red[0][threadIdx.x], b = red[1][threadIdx.x], c = red[2][threadIdx.x],
+               d = red[3][threadIdx.x];
+  const int k = (4 * f) / C, col = (4 * f) % C;
+  float *dst = k == 0 ? dg : (k == 1 ? db : dsum);
+  if (!dst) return;
+  unsafeAtomicAdd(&dst[col + 0], (a.x + b.x) + (c.x + d.x));
+  unsafeAtomicAdd(&dst[col + 1], (a.y + b.y) + (c.y + d.y));
+  unsafeAtomicAdd(&dst[col + 2], (a.z + b.z) + (c.z + d.z));
+  unsafeAtomicAdd(&dst[col + 3], (a.w + b.w) + (c.w + d.w));
+}
+
+// Vectorised column sums: each thread owns 16 bytes of a row (8 bf16 or 4
+// f32 columns) and walks CS_ROWS rows of the workgroup's row slice in one of
+// 8 row groups; LDS combines the groups, then one atomic per column.  Needs
+// 16-byte aligned rows (host-checked).
+constexpr int CS_ROWS = 128;   // rows per workgroup
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) colsum_vec_kernel(int M, int N, int ld,
+                                                         const void *__restrict__ src,
+                                                         float *__restrict__ out) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  const int ct = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int c0 = (blockIdx.x * 32 + ct) * VEC;
+  const int m0 = blockIdx.y * CS_ROWS;
+  const int m1 = min(M, m0 + CS_ROWS);
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  if (c0 < N) {
+#pragma unroll 4
+    for (int m = m0 + grp; m < m1; m += 8) {
+      if (BF16) {
+        const uint4 u = *(const uint4 *)((const bf16_t *)src + (size_t)m * ld + c0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += __uint_as_float(w[q] << 16);
+          acc[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+        }
+      } else {
+        const float4 f = *(const float4 *)((const float *)src + (size_t)m * ld + c0);
+        acc[0] += f.x; acc[1] += f.y; acc[2] += f.z; acc[3] += f.w;
+      }
+    }
+  }
+  __shared__ float red[8][32 * VEC + 1];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) red[grp][ct * VEC + i] = acc[i];
+  __syncthreads();
+  const int c = blockIdx.x * 32 * VEC + threadIdx.x;
+  if (threadIdx.x < 32 * VEC && c < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) t += red[g][threadIdx.x];
+    unsafeAtomicAdd(&out[c], t);
   }
 }
 
@@ -329,35 +460,59 @@ int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, co
 
 int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
                           const float *mean, const float *rstd, const float *g, const float *dy,
-                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db) {
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
+                          float *dsum) {
   (void)mode;
   TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
   TT_REQUIRE(ctx, x && mean && rstd && g && dy && dx, "layernorm_bwd: NULL pointer");
   if (N == 0) return TT_OK;
-  dim3 grid((N + LNB_ROWS - 1) / LNB_ROWS);
   const int nv = (C / 4 + 63) / 64;
-  tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
-                     (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
-                         16.0 * C + 8.0 * N);
-#define TT_LNB(NV)                                                                              \
-  if (nv <= NV) {                                                                               \
-    hipLaunchKernelGGL((layernorm_bwd_kernel<NV>), grid, dim3(256), 0, ctx->stream, N, C, x, mean, \
-                       rstd, g, dy, dres, dx, dx_bf16, dg, db);                                 \
-    return tt_check_launch(ctx, "layernorm_bwd");                                               \
-  }
-  TT_LNB(1) TT_LNB(2) TT_LNB(3) TT_LNB(4) TT_LNB(8) TT_LNB(16)
+  // the dispatched template width: the smallest of 1, 2, 3, 4, 8, 16 >= nv
+  const int nvt = nv <= 4 ? nv : (nv <= 8 ? 8 : 16);
+  const int rows_per_wg = lnb_waves(nvt) * lnb_rpw(nvt);
+  const int G = (N + rows_per_wg - 1) / rows_per_wg;
+  tt_scratch_scope scope(ctx);
+  void *part;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)G * 3 * C * 4, &part));
+  {
+    tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
+                       (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
+                           8.0 * N + 12.0 * G * C);
+#define TT_LNB(NV)                                                                        \
+    if (nv <= NV) {                                                                       \
+      hipLaunchKernelGGL((layernorm_bwd_kernel<NV>), dim3(G), dim3(64 * lnb_waves(NV)), 0, \
+                         ctx->stream, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,      \
+                         (float *)part);                                                  \
+    } else
+    TT_LNB(1) TT_LNB(2) TT_LNB(3) TT_LNB(4) TT_LNB(8) TT_LNB(16) return TT_EUNSUPPORTED;
 #undef TT_LNB
-  return TT_EUNSUPPORTED;
+  }
+  TT_TRY(tt_check_launch(ctx, "layernorm_bwd"));
+  if (!dg && !db && !dsum) return TT_OK;
+  tt_prof_scope prof(ctx, "layernorm_bwd_reduce_kernel", 0.0, 12.0 * G * C + 24.0 * C);
+  hipLaunchKernelGGL(layernorm_bwd_reduce_kernel,
+                     dim3((3 * C / 4 + 63) / 64, (G + LNR_SLICE - 1) / LNR_SLICE), dim3(256), 0,
+                     ctx->stream, G, C, (const float *)part, dg, db, dsum);
+  return tt_check_launch(ctx, "layernorm_bwd_reduce");
 }
 
 int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out) {
   if (M == 0 || N == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "colsum_kernel", 0.0, (double)M * N * (src_bf16 ? 2.0 : 4.0) + 4.0 * N);
+  const int vec = src_bf16 ? 8 : 4;
+  if (tt_aligned16(src) && N % vec == 0 && ld % vec == 0) {
+    dim3 grid((N / vec + 31) / 32, (M + CS_ROWS - 1) / CS_ROWS);
+    if (src_bf16)
+      hipLaunchKernelGGL(colsum_vec_kernel<true>, grid, dim3(256), 0, ctx->stream, M, N, ld, src, out);
+    else
+      hipLaunchKernelGGL(colsum_vec_kernel<false>, grid, dim3(256), 0, ctx->stream, M, N, ld, src, out);
+    return tt_check_launch(ctx, "colsum");
+  }
   int colblocks = (N + 63) / 64;
   int rowsplit = 1;
   while (colblocks * rowsplit < 1024 && rowsplit * 64 < M) rowsplit *= 2;
   int rpb = (M + rowsplit - 1) / rowsplit;
   dim3 grid(colblocks, (M + rpb - 1) / rpb);
-  tt_prof_scope prof(ctx, "colsum_kernel", 0.0, (double)M * N * (src_bf16 ? 2.0 : 4.0) + 4.0 * N);
   if (src_bf16)
     hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(256), 0, ctx->stream, M, N, ld, rpb, src, out);
   else

@@ -169,6 +169,7 @@ struct GemmArgs {
   void *aux; int ldx;          // EPI_GELU (written preact) / EPI_GELU_BWD (read preact)
   int split_k;                 // >= 1 (EPI_ACCUM only)
   int n_valid;                 // columns >= n_valid of C are not stored (ragged pad); 0 = N
+  float *colsum;               // nullable: colsum[n] += sum over rows of the stored output
 };
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
 // bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
@@ -177,10 +178,13 @@ bool tt_gemm_bf16_ok(const GemmArgs &g);
 
 int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, const float *x,
                           const float *g, const float *b, void *y, float *mean, float *rstd);
-// dx_out = dres + LN_bwd(dy); also writes a bf16 copy when dx_bf16 != NULL.
+// dx = dres + LayerNorm backward, also written as a bf16 copy when dx_bf16 is
+// not NULL (dres may alias dx or be NULL); dg, db and dsum (column sums of dx
+// as stored, nullable each) are accumulated (+=).
 int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
                           const float *mean, const float *rstd, const float *g, const float *dy,
-                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db);
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
+                          float *dsum = nullptr);
 int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out);
 int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v);
 int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst);
