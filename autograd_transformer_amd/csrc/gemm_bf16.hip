@@ -375,10 +375,14 @@ struct Cfg3 {
   static_assert(OA::CHUNKS % NW == 0 && OB::CHUNKS % NW == 0, "loads not divisible by waves");
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((NS - 2) * LPS < 64, "vmcnt range");
+  // workgroups per CU that the LDS allows (at most 2), as waves per SIMD
+  static constexpr int WG_PER_CU = 2 * SMEM <= 160 * 1024 ? 2 : 1;
+  static constexpr int WAVES_PER_EU = (NW * WG_PER_CU + 3) / 4;
 };
 
 template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
-__global__ void __launch_bounds__(64 * WM * WN, 1)
+__global__ void __launch_bounds__(64 * WM * WN,
+                                  (Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>::WAVES_PER_EU))
 gemm_bf16_v3_kernel(GemmParams p) {
   using C = Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>;
   using OA = typename C::OA;
@@ -579,55 +583,42 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
   return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
 }
 
-// Tiles: 256 x 128 or 256 x 256, 8 waves (two per SIMD).  Products whose
-// operands are both k-major (dX = dY W, forward GEMMs against transposed
-// weights, the LM head) and all weight gradients take the direct-to-LDS v3
-// kernel (BK 64); products with exactly one row-major operand take the
-// register-prefetch v2 kernel, which is faster there.  256 x 256 serves
-// products with enough tiles to fill the chip several times over.
+// Tile 256 x 128, 8 waves.  Products whose operands are both k-major (dX =
+// dY W, forward GEMMs against transposed weights, the LM head) and all weight
+// gradients take the direct-to-LDS v3 kernel; products with exactly one
+// row-major operand take the register-prefetch v2 kernel, which is faster
+// there.  v3 depth: BK 32 (72 KB of LDS for 3 stages, two workgroups per CU,
+// so one workgroup's prologue and epilogue overlap the other's main loop)
+// when the grid fills the two slots of every CU (>= 512 tiles), else BK 64
+// (one workgroup per CU, fewer barriers per flop).
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
 // split accumulates with a plain read-modify-write (a workgroup owns its
 // output tile); several splits write fp32 partials to arena scratch, then
-// one coalesced pass adds them into the output.  For each tile size the
-// split is the largest that keeps the grid within one wave of 256
-// workgroups (one per CU) with at least four k-blocks per split; the tile
-// size is then the one with the smaller cost estimate
-//   (k-blocks per split) x (tile area / efficiency) x max(1, workgroups / 256).
+// one coalesced pass adds them into the output.  They run BK 32 with 2
+// stages (two workgroups per CU) and the largest split that keeps the grid
+// within 512 workgroups, at most 16, with at least 256 of K per split.
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
-  const long tm = (g.M + 255) / 256;
-  const long tiles128 = tm * ((g.N + 127) / 128), tiles256 = tm * ((g.N + 255) / 256);
+  const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
   if (g.epi != EPI_ACCUM) {
     if (g.colsum && !(g.a_kmajor && g.b_kmajor))
       return tt_set_error(ctx, TT_EINVAL, "gemm_bf16: column sums need the k-major kernel");
     if (g.a_kmajor && g.b_kmajor) {
-      if (tiles256 >= 1024) return launch3<256, 256, 64, 4, 2, 2>(ctx, g, 1);
+      if (tiles >= 512) return launch3<256, 128, 32, 4, 2, 3>(ctx, g, 1);
       return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
     }
     return launch<256, 128, 4, 2>(ctx, g, 1);
   }
-  const int kb = (g.K + 63) / 64;
-  auto rounded = [&](int split, int &per) {  // the split launch3 will run
-    per = (kb + split - 1) / split;
+  const int kb = (g.K + 31) / 32;
+  auto rounded = [&](int split) {  // the split launch3 will run (whole k-blocks)
+    const int per = (kb + split - 1) / split;
     return (kb + per - 1) / per;
   };
-  auto choose = [&](long tiles, int &per) {
-    const int s = (int)std::max<long>(1, std::min<long>(256 / tiles, std::min(kb / 4, 16)));
-    return rounded(s, per);
-  };
-  int per128, per256;
-  const int s128 = choose(tiles128, per128), s256 = choose(tiles256, per256);
-  const double cost128 = per128 * 32768.0 * std::max(1.0, tiles128 * s128 / 256.0);
-  const double cost256 = per256 * (65536.0 / 1.1) * std::max(1.0, tiles256 * s256 / 256.0);
-  const bool big = cost256 < cost128;
-  int split = big ? s256 : s128;
-  if (g.split_k > 0) {
-    int per;
-    split = rounded(g.split_k, per);
-  }
+  int split = rounded((int)std::max<long>(1, std::min<long>(512 / tiles, std::min(kb / 8, 16))));
+  if (g.split_k > 0) split = rounded(g.split_k);
   GemmArgs h = g;
   if (split == 1) {
     h.epi = EPI_STORE_ACC;
-    return big ? launch3<256, 256, 64, 4, 2, 2>(ctx, h, 1) : launch3<256, 128, 64, 4, 2, 3>(ctx, h, 1);
+    return launch3<256, 128, 32, 4, 2, 2>(ctx, h, 1);
   }
   tt_scratch_scope scope(ctx);
   void *ws;
@@ -639,10 +630,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   h.bias = nullptr;
   // split is already what launch3 runs (whole k-blocks per split), so the
   // reduction sums exactly the partials written.
-  if (big)
-    TT_TRY((launch3<256, 256, 64, 4, 2, 2>(ctx, h, split, (size_t)g.M * g.N)));
-  else
-    TT_TRY((launch3<256, 128, 64, 4, 2, 3>(ctx, h, split, (size_t)g.M * g.N)));
+  TT_TRY((launch3<256, 128, 32, 4, 2, 2>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
   tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0, (split + 2.0) * g.M * g.N * 4.0);
