@@ -92,7 +92,10 @@ struct TileRegs {
 };
 
 // ------------------------------------------------------------------ forward
-// 4 waves x 32 queries; K/V tiles of 64 keys; Sᵀ = K Qᵀ, Oᵀ += Vᵀ Pᵀ.
+// 4 waves x 16 QS queries; K/V tiles of 64 keys; Sᵀ = K Qᵀ, Oᵀ += Vᵀ Pᵀ.
+// Workgroups run heaviest query blocks first across all heads (block index
+// outer, batch-head inner), so freed CU slots take the longest remaining work.
+template <int QS>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out,
                      float *__restrict__ lse, int nqb, uint32_t qkv_bytes) {
@@ -100,29 +103,33 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][64 * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
-  const int qb = nqb - 1 - (blockIdx.x % nqb);   // heavy query blocks first
-  const int bh = blockIdx.x / nqb, b = bh / NH, h = bh % NH;
+  const int nbh = gridDim.x / nqb;
+  const int qb = nqb - 1 - blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh, b = bh / NH, h = bh % NH;
   const int C = NH * HS, ld = 3 * C;
   const size_t row0 = (size_t)b * T;
   const __amdgpu_buffer_rsrc_t rs = rsrc(qkv, qkv_bytes);
 
-  const int q0 = qb * 128 + wave * 32;
-  bf16x8_t qf[2][2];
+  const int q0 = qb * 64 * QS + wave * 16 * QS;
+  bf16x8_t qf[QS][2];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int t = q0 + qs * 16 + lr;
       qf[qs][st] = as_frag(bload(rs, t < T ? (uint32_t)(((row0 + t) * ld + h * HS + st * 32 + lg * 8) * 2) : OOB));
     }
-  f32x4_t o[4][2];
+  f32x4_t o[4][QS];
+  float mrow[QS], lrow[QS];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int qs = 0; qs < QS; ++qs) {
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) o[d][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+    for (int d = 0; d < 4; ++d) o[d][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mrow[qs] = -INFINITY;
+    lrow[qs] = 0.f;
+  }
 
-  const int kend = min(T, qb * 128 + 128);
+  const int kend = min(T, (qb + 1) * 64 * QS);
   const int nkb = (kend + 63) / 64;
   TileRegs kr, vr;
   kr.load(rs, row0, 0, T, ld, C + h * HS, tid);
@@ -137,22 +144,22 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
       kr.load(rs, row0, k0 + 64, T, ld, C + h * HS, tid);
       vr.load(rs, row0, k0 + 64, T, ld, 2 * C + h * HS, tid);
     }
-    if (k0 <= q0 + 31 && q0 < T) {
+    if (k0 <= q0 + 16 * QS - 1 && q0 < T) {
       const bf16_t *ks = Ks[cur], *vs = Vs[cur];
-      f32x4_t s[4][2];
+      f32x4_t s[4][QS];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t k_0 = row_frag(ks, j * 16, 0, lr, lg), k_1 = row_frag(ks, j * 16, 32, lr, lg);
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
+        for (int qs = 0; qs < QS; ++qs)
           s[j][qs] = mfma(k_1, qf[qs][1], mfma(k_0, qf[qs][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
       }
       auto softmax = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        float mx[2];
+        float mx[QS];
         bool grow = false;
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
+        for (int qs = 0; qs < QS; ++qs) {
           const int q = q0 + qs * 16 + lr;
           float m = -INFINITY;
 #pragma unroll
@@ -174,7 +181,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
         }
         if (__ballot(grow)) {
 #pragma unroll
-          for (int qs = 0; qs < 2; ++qs) {
+          for (int qs = 0; qs < QS; ++qs) {
             const float mnew = fmaxf(mrow[qs], mx[qs]);
             const float alpha = ex2(mrow[qs] - mnew);
             lrow[qs] *= alpha;
@@ -186,7 +193,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
           }
         }
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
+        for (int qs = 0; qs < QS; ++qs) {
           float ps = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -205,14 +212,14 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
         softmax(std::false_type{});
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x8_t pb[2];
+        bf16x8_t pb[QS];
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) pb[qs] = pack8(s[2 * t2][qs], s[2 * t2 + 1][qs]);
+        for (int qs = 0; qs < QS; ++qs) pb[qs] = pack8(s[2 * t2][qs], s[2 * t2 + 1][qs]);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const bf16x8_t va = tr_frag(vs, t2 * 32, d * 16, lr, lg);
 #pragma unroll
-          for (int qs = 0; qs < 2; ++qs) o[d][qs] = mfma(va, pb[qs], o[d][qs]);
+          for (int qs = 0; qs < QS; ++qs) o[d][qs] = mfma(va, pb[qs], o[d][qs]);
         }
       }
     }
@@ -224,7 +231,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
   }
 
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < QS; ++qs) {
     float l = lrow[qs];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -254,8 +261,9 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
   __shared__ __attribute__((aligned(16))) float ls[2][64], ds[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
-  const int kb = blockIdx.x % nkb;
-  const int bh = blockIdx.x / nkb, b = bh / NH, h = bh % NH;
+  const int nbh = gridDim.x / nkb;
+  const int kb = blockIdx.x / nbh;   // heaviest key blocks (most queries) first
+  const int bh = blockIdx.x % nbh, b = bh / NH, h = bh % NH;
   const int C = NH * HS, ld = 3 * C;
   const size_t row0 = (size_t)b * T;
   const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes);
@@ -369,8 +377,9 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][64 * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
-  const int qb = nqb - 1 - (blockIdx.x % nqb);
-  const int bh = blockIdx.x / nqb, b = bh / NH, h = bh % NH;
+  const int nbh = gridDim.x / nqb;
+  const int qb = nqb - 1 - blockIdx.x / nbh;   // heaviest query blocks first
+  const int bh = blockIdx.x % nbh, b = bh / NH, h = bh % NH;
   const int C = NH * HS, ld = 3 * C;
   const size_t row0 = (size_t)b * T;
   const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes);
@@ -485,12 +494,13 @@ bool tt_attn_bf16_ok(int B, int T, int NH) {
 }
 
 int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse) {
-  const int nqb = (T + 127) / 128;
+  constexpr int QS = 1;   // 64 queries per workgroup
+  const int nqb = (T + 64 * QS - 1) / (64 * QS);
   const uint32_t qb = (uint32_t)((size_t)B * T * 3 * NH * HS * 2);
   const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
   tt_prof_scope prof(ctx, "attn_fwd_bf16_kernel", 2.0 * pass, 0.0);
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(B * NH * nqb), dim3(256), 0, ctx->stream, T, NH,
-                     (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<QS>, dim3(B * NH * nqb), dim3(256), 0, ctx->stream, T,
+                     NH, (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
   return tt_check_launch(ctx, "attn_fwd_bf16");
 }
 
