@@ -304,6 +304,10 @@ struct DOp {
   static constexpr int CPR = KM ? BKV / 8 : ROWS / 8; // 16-byte chunks per LDS row
   static constexpr int RB = KM ? BKV * 2 : ROWS * 2;  // bytes per LDS row
   static_assert(BYTES % 1024 == 0, "tile must be whole 1 KB wave loads");
+  // The XOR swizzles stay inside a row only for power-of-two chunk counts, and
+  // the row-major one flips chunk bits up to 8 (needs >= 16 chunks per row).
+  static constexpr bool VALID =
+      (CPR & (CPR - 1)) == 0 && (KM || CPR >= 16);
 
   __device__ __forceinline__ static int swz_k(int r) { return (r / (256 / RB)) % CPR; }
   __device__ __forceinline__ static int rswz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
@@ -455,7 +459,54 @@ gemm_bf16_v3_kernel(GemmParams p) {
 
   if (p.out_zstride) p.out = (float *)p.out + blockIdx.z * p.out_zstride;
   float *Cs = (float *)smem_raw;
-  constexpr int TPR = BN / 4, RPP = NT / TPR;
+  constexpr int TPR = BN / 4;
+  if constexpr (NT % TPR != 0) {
+    // Flattened epilogue (a thread's column group changes between rows).
+    // Column sums: the stored values go back into the staged tile and
+    // thread t < BN adds up column t after each pass.
+    const int nv = p.n_valid;
+    float csum = 0.f;
+#pragma unroll
+    for (int pass = 0; pass < WM; ++pass) {
+      if (pass > 0) __syncthreads();
+      if (wm == pass) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
+      }
+      __syncthreads();
+      for (int idx = tid; idx < C::WTM * TPR; idx += NT) {
+        const int rr = idx / TPR, cc = (idx % TPR) * 4;
+        const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
+        float4 *cp = (float4 *)(Cs + rr * C::LDC + cc);
+        if (m >= p.M || n >= nv) {
+          if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
+          continue;
+        }
+        float4 v = *cp;
+        if (p.bias && blockIdx.z == 0) {
+          v.x += p.bias[n];
+          if (n + 1 < nv) v.y += p.bias[n + 1];
+          if (n + 2 < nv) v.z += p.bias[n + 2];
+          if (n + 3 < nv) v.w += p.bias[n + 3];
+        }
+        const float4 st = epilogue4(p, m, n, v, nv - n);
+        if (p.colsum) *cp = st;
+      }
+      if (p.colsum) {
+        __syncthreads();
+        if (tid < BN)
+          for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
+      }
+    }
+    if (p.colsum && tid < BN && n0 + tid < nv) unsafeAtomicAdd(&p.colsum[n0 + tid], csum);
+    return;
+  }
+  constexpr int RPP = NT / TPR;
   const int cc = (tid % TPR) * 4;
   const int n = n0 + cc;
   const int nv = p.n_valid;
@@ -536,9 +587,13 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, 0.0);
 #define TT_L3(AK, BKM)                                                                          \
   if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                  \
-    hipLaunchKernelGGL((gemm_bf16_v3_kernel<BM, BN, BKV, WM, WN, NS, AK, BKM>), grid,           \
-                       dim3(64 * WM * WN), 0, ctx->stream, p);                                  \
-    return tt_check_launch(ctx, "gemm_bf16_v3");                                                \
+    if constexpr (DOp<BM, BKV, AK>::VALID && DOp<BN, BKV, BKM>::VALID) {                        \
+      hipLaunchKernelGGL((gemm_bf16_v3_kernel<BM, BN, BKV, WM, WN, NS, AK, BKM>), grid,         \
+                         dim3(64 * WM * WN), 0, ctx->stream, p);                                \
+      return tt_check_launch(ctx, "gemm_bf16_v3");                                              \
+    } else {                                                                                    \
+      return tt_set_error(ctx, TT_EUNSUPPORTED, "gemm_bf16_v3: tile/layout not supported");    \
+    }                                                                                           \
   }
   TT_L3(true, true) TT_L3(true, false) TT_L3(false, true) TT_L3(false, false)
 #undef TT_L3
@@ -583,30 +638,38 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
   return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
 }
 
-// Tile 256 x 128, 8 waves.  Products whose operands are both k-major (dX =
-// dY W, forward GEMMs against transposed weights, the LM head) and all weight
-// gradients take the direct-to-LDS v3 kernel; products with exactly one
-// row-major operand take the register-prefetch v2 kernel, which is faster
-// there.  v3 depth: BK 32 (72 KB of LDS for 3 stages, two workgroups per CU,
-// so one workgroup's prologue and epilogue overlap the other's main loop)
-// when the grid fills the two slots of every CU (>= 512 tiles), else BK 64
-// (one workgroup per CU, fewer barriers per flop).
+// Tiles (8 waves, direct-to-LDS v3 kernel unless noted), chosen from sweeps
+// of the GPT-2 step's shapes on MI355X:
+//  * k-major x k-major products (dX = dY W, forward GEMMs against transposed
+//    weights, the LM head):
+//      K >= 8192 (LM-head dH)                   128 x 192, BK 64, 3 stages
+//      >= 512 tiles of 256 x 128:  GELU-backward epilogue -> 128 x 192, BK 64,
+//                                  2 stages; others -> 256 x 128, BK 32, 3
+//                                  stages (two workgroups per CU)
+//      fewer tiles (N = 768)                    256 x 128, BK 64, 3 stages
+//    (timed inside the training step: with operands arriving from HBM the
+//    N = 768 products run faster on 256 x 128 than on the 128 x 192 grid that
+//    fills all 256 CUs)
+//  * one row-major operand: the register-prefetch v2 kernel, 256 x 128;
+//  * weight gradients: 256 x 128, BK 32, 2 stages (below).
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
 // split accumulates with a plain read-modify-write (a workgroup owns its
 // output tile); several splits write fp32 partials to arena scratch, then
-// one coalesced pass adds them into the output.  They run BK 32 with 2
-// stages (two workgroups per CU) and the largest split that keeps the grid
-// within 512 workgroups, at most 16, with at least 256 of K per split.
+// one coalesced pass adds them into the output.  The split is the largest
+// that keeps the grid within 512 workgroups (two per CU), at most 16, with at
+// least 256 of K per split.
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
   if (g.epi != EPI_ACCUM) {
     if (g.colsum && !(g.a_kmajor && g.b_kmajor))
       return tt_set_error(ctx, TT_EINVAL, "gemm_bf16: column sums need the k-major kernel");
-    if (g.a_kmajor && g.b_kmajor) {
-      if (tiles >= 512) return launch3<256, 128, 32, 4, 2, 3>(ctx, g, 1);
-      return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
+    if (!(g.a_kmajor && g.b_kmajor)) return launch<256, 128, 4, 2>(ctx, g, 1);
+    if (g.K >= 8192) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
+    if (tiles >= 512) {
+      if (g.epi == EPI_GELU_BWD) return launch3<128, 192, 64, 2, 4, 2>(ctx, g, 1);
+      return launch3<256, 128, 32, 4, 2, 3>(ctx, g, 1);
     }
-    return launch<256, 128, 4, 2>(ctx, g, 1);
+    return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
   }
   const int kb = (g.K + 31) / 32;
   auto rounded = [&](int split) {  // the split launch3 will run (whole k-blocks)
