@@ -363,6 +363,7 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+
 template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
 struct Cfg3 {
   static constexpr int NW = WM * WN, NT = 64 * NW;
@@ -425,37 +426,38 @@ gemm_bf16_v3_kernel(GemmParams p) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, s);
-  for (int it = 0; it < nk; ++it) {
-    // Stage it must have landed (from every wave) before anyone reads it:
-    // each wave waits for its own loads of that stage, then a bare barrier
-    // (no memory fence, which would also drain the loads still in flight for
-    // later stages).  The buffer refilled below was last read in iteration
-    // it-1, whose LDS reads every wave has consumed before reaching here.
-    // The empty asm statements keep the compiler from moving LDS accesses
-    // across the barrier (the barrier builtin is not a memory operation to
-    // it); they emit no instruction and no wait.
-    if (it + NS - 2 < nk) wait_vm<(NS - 2) * C::LPS>();
-    else wait_vm<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
-    const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
+  {
+    for (int it = 0; it < nk; ++it) {
+      // Stage it must have landed (from every wave) before anyone reads it:
+      // each wave waits for its own loads of that stage, then a bare barrier
+      // (no memory fence, which would also drain the loads still in flight
+      // for later stages).  The buffer refilled below was last read in
+      // iteration it-1, whose LDS reads every wave has consumed before
+      // reaching here.  The empty asm statements keep the compiler from
+      // moving LDS accesses across the barrier (the barrier builtin is not a
+      // memory operation to it); they emit no instruction and no wait.
+      if (it + NS - 2 < nk) wait_vm<(NS - 2) * C::LPS>();
+      else wait_vm<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+      const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
 #pragma unroll
-    for (int kk = 0; kk < BKV; kk += 32) {
-      bf16x8_t fb[FN];
+      for (int kk = 0; kk < BKV; kk += 32) {
+        bf16x8_t fb[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+        for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+        for (int i = 0; i < FM; ++i) {
+          const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
-  }
-  __syncthreads();
+  }  __syncthreads();
 
   if (p.out_zstride) p.out = (float *)p.out + blockIdx.z * p.out_zstride;
   float *Cs = (float *)smem_raw;
@@ -646,10 +648,11 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 //      >= 512 tiles of 256 x 128:  GELU-backward epilogue -> 128 x 192, BK 64,
 //                                  2 stages; others -> 256 x 128, BK 32, 3
 //                                  stages (two workgroups per CU)
-//      fewer tiles (N = 768)                    256 x 128, BK 64, 3 stages
-//    (timed inside the training step: with operands arriving from HBM the
-//    N = 768 products run faster on 256 x 128 than on the 128 x 192 grid that
-//    fills all 256 CUs)
+//      fewer tiles (N = 768): K >= 2304 -> 128 x 192, BK 64, 3 stages (256
+//                             tiles fill the 256 CUs where 256 x 128 gives
+//                             192); else 256 x 128, BK 64, 3 stages
+//    (ranked with operands arriving cold from HBM, as in the step; with
+//    cache-resident operands the ranking differs)
 //  * one row-major operand: the register-prefetch v2 kernel, 256 x 128;
 //  * weight gradients: 256 x 128, BK 32, 2 stages (below).
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
@@ -669,6 +672,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
       if (g.epi == EPI_GELU_BWD) return launch3<128, 192, 64, 2, 4, 2>(ctx, g, 1);
       return launch3<256, 128, 32, 4, 2, 3>(ctx, g, 1);
     }
+    if (g.K >= 2304) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
     return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
   }
   const int kb = (g.K + 31) / 32;
