@@ -1,6 +1,7 @@
 """Benchmark: one GPT-2 training step (forward, backward, AdamW) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
+    python bench.py --calibrate-copy     (1 GiB device copies, for HBM counter scaling)
 
 Workload (default): GPT-2 124M — 12 layers, d=768, 12 heads, vocab 50257
 (token table padded to 50304 rows), context 1024, batch 8; synthetic seeded
@@ -60,7 +61,7 @@ def cpu_baseline(w):
                        block_size=w["T"])
     p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=3).items()}
     zeros = {k: np.zeros_like(v) for k, v in p.items()}
-    T = 512
+    T = w["T"]
     tok, tgt = syn.gpt2_tokens(1, T, w["V"], seed=3)
     t0 = time.perf_counter()
     og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16")
@@ -70,6 +71,26 @@ def cpu_baseline(w):
                       f"rounding, float64 NumPy) on 1 sequence of {T} tokens; {dt:.1f} s"}
 
 
+def measured_traffic(workload, B, T, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the library
+    sources changed since the counters were taken."""
+    from autograd_transformer_amd.pmc_traffic import source_digest
+    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_t{T}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != source_digest():
+        log(f"[bench] {os.path.basename(path)} was measured on other sources: traffic null")
+        return None
+    k = rec["kernels"].get(kernel)
+    if k is None:   # timer names drop template arguments that rocprofv3 keeps
+        hits = [v for n, v in rec["kernels"].items() if n.split("<")[0] == kernel]
+        k = hits[0] if len(hits) == 1 else None
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +98,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 device copies of 1 GiB (reference for rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE scaling) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -85,6 +109,16 @@ def main():
 
     import numpy as np
     import torch
+    if args.calibrate_copy:
+        from autograd_transformer_amd.pmc_traffic import COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES,
+                          "bytes_written": COPY_BYTES, "launches": 5}), flush=True)
+        return
     import autograd_transformer_amd as tt
     from autograd_transformer_amd import synthetic as syn
 
@@ -183,7 +217,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(achieved / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload, B, T, dom["name"])
     roof["kernel"] = dom["name"]
     roof["calls_per_step"] = dom["calls"] / args.steps
     roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
