@@ -127,7 +127,7 @@ gemm_bf16_kernel(GemmParams p) {
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = blockIdx.z * p.k_chunk;
   const int kend = min(p.K, kbeg + p.k_chunk);
@@ -253,6 +253,7 @@ int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
   p.vec_out = gemm_vec_out(g) ? 1 : 0;
   p.out_zstride = 0;
+  p.raster_n = g.raster == 2 ? 1 : 0;
   p.a_bytes = (uint32_t)gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda);
   p.b_bytes = (uint32_t)gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb);
   p.tiles_m = (g.M + BM - 1) / BM;
@@ -400,7 +401,7 @@ gemm_bf16_v3_kernel(GemmParams p) {
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = blockIdx.z * p.k_chunk;
   const int kend = min(p.K, kbeg + p.k_chunk);
@@ -572,6 +573,7 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   p.vec_out = gemm_vec_out(g) ? 1 : 0;
   p.out_zstride = out_zstride;
   p.colsum = split == 1 ? g.colsum : nullptr;
+  p.raster_n = g.raster == 2 ? 1 : 0;
   p.a_bytes = (uint32_t)gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda);
   p.b_bytes = (uint32_t)gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb);
   p.tiles_m = (g.M + BM - 1) / BM;
@@ -655,6 +657,9 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 //    cache-resident operands the ranking differs)
 //  * one row-major operand: the register-prefetch v2 kernel, 256 x 128;
 //  * weight gradients: 256 x 128, BK 32, 2 stages (below).
+// Tile order within an XCD: m fastest (neighbouring workgroups share B
+// panels) except on the 256 x 128 BK-32 path, where n fastest (shared A
+// panels) measured faster inside the step.
 // Weight gradients (EPI_ACCUM, output += product) never use atomics: one
 // split accumulates with a plain read-modify-write (a workgroup owns its
 // output tile); several splits write fp32 partials to arena scratch, then
@@ -670,7 +675,9 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
     if (g.K >= 8192) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
     if (tiles >= 512) {
       if (g.epi == EPI_GELU_BWD) return launch3<128, 192, 64, 2, 4, 2>(ctx, g, 1);
-      return launch3<256, 128, 32, 4, 2, 3>(ctx, g, 1);
+      GemmArgs h = g;
+      if (h.raster == 0) h.raster = 2;
+      return launch3<256, 128, 32, 4, 2, 3>(ctx, h, 1);
     }
     if (g.K >= 2304) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
     return launch3<256, 128, 64, 4, 2, 3>(ctx, g, 1);
@@ -683,6 +690,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   int split = rounded((int)std::max<long>(1, std::min<long>(512 / tiles, std::min(kb / 8, 16))));
   if (g.split_k > 0) split = rounded(g.split_k);
   GemmArgs h = g;
+  if (h.raster == 0) h.raster = 1;
   if (split == 1) {
     h.epi = EPI_STORE_ACC;
     return launch3<256, 128, 32, 4, 2, 2>(ctx, h, 1);

@@ -21,6 +21,7 @@ struct GemmParams {
   uint32_t a_bytes, b_bytes;  // operand extents for buffer range checks
   size_t out_zstride;         // split-K partials: output offset per blockIdx.z (elements)
   float *colsum;              // nullable: += column sums of the stored output (v3 kernel)
+  int raster_n;               // tile order: 1 = n fastest (share A panels), 0 = m fastest
 };
 
 __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
@@ -124,19 +125,22 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
 
 // Block id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so first give every XCD a contiguous
-// range of tiles, then walk that range in groups of GM tile-rows so that
-// neighbouring workgroups share both A rows and B columns in L2.
-__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, int &tm,
-                                            int &tn) {
-  constexpr int XCDS = 8, GM = 8;
+// range of tiles, then walk that range in groups of G tile-rows (m fastest:
+// consecutive workgroups share B panels) or, with raster_n, of G tile-columns
+// (n fastest: they share A panels), whichever operand is larger.
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
+                                            int raster_n, int &tm, int &tn) {
+  constexpr int XCDS = 8, G = 8;
   if (nwg % XCDS == 0) bid = (bid % XCDS) * (nwg / XCDS) + bid / XCDS;
-  const int per_group = GM * tiles_n;
+  const int major = raster_n ? tiles_n : tiles_m, minor = raster_n ? tiles_m : tiles_n;
+  const int per_group = G * minor;
   const int group = bid / per_group;
-  const int first_m = group * GM;
-  const int gm = min(GM, tiles_m - first_m);
+  const int first = group * G;
+  const int g = min(G, major - first);
   const int in = bid % per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
+  const int a = first + in % g, b = in / g;
+  tm = raster_n ? b : a;
+  tn = raster_n ? a : b;
 }
 
 // Host: may the epilogue use 4-wide vector accesses on out / aux / resid?
