@@ -310,7 +310,10 @@ struct DOp {
   static constexpr bool VALID =
       (CPR & (CPR - 1)) == 0 && (KM || CPR >= 16);
 
-  __device__ __forceinline__ static int swz_k(int r) { return (r / (256 / RB)) % CPR; }
+  // chunk swizzle of k-major row r: rows are paired (measured: pairing gives
+  // fewer LDS bank conflicts than one swizzle value per 256 bytes of rows
+  // for 64-byte rows, and is the same thing for 128-byte rows)
+  __device__ __forceinline__ static int swz_k(int r) { return (r >> 1) % CPR; }
   __device__ __forceinline__ static int rswz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
   // Issue this wave's share of the tile's loads (chunk instructions w, w+NW, ...).
