@@ -420,6 +420,86 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
   }
 }
 
+// One-pass cross-entropy for bf16 rows of up to CE_VPT * 8 * 1024 columns: a
+// 1024-thread workgroup holds its row in registers (CE_VPT 16-byte vectors per
+// thread, branch-free buffer loads: vectors past the row read zero), reduces
+// (max, sum exp) over the workgroup, then overwrites the row with
+// (softmax - onehot) * scale; pad columns (>= V) become 0.  One read and one
+// write of the logits instead of two reads and a write.
+constexpr int CE_VPT = 7;
+constexpr int CE_THREADS = 1024;
+
+__device__ __forceinline__ float ce_block_reduce(float v, bool is_max, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = is_max ? wave_max(v) : wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < CE_THREADS / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld, bf16_t *logits,
+                                                            const int32_t *__restrict__ targets,
+                                                            float *__restrict__ row_loss,
+                                                            float scale, int32_t *flags) {
+  __shared__ float red[CE_THREADS / 64];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int y = targets[row];
+  const bool y_ok = (y >= 0 && y < V);
+  bf16_t *z = logits + (size_t)row * ld;
+  const int nv8 = ld >> 3;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)z, (short)0, ld * 2, 0x00020000);
+  uint4 v[CE_VPT];
+#pragma unroll
+  for (int i = 0; i < CE_VPT; ++i) {
+    const int idx = tid + i * CE_THREADS;
+    v[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, idx < nv8 ? (uint32_t)idx * 16u : 0x7ffffff0u,
+                                                     0, 0));
+  }
+  const float zy = (tid == 0 && y_ok) ? bf2f(z[y]) : 0.f;   // read before any thread writes
+  auto val = [&](int i, int q) {
+    const uint32_t w = (&v[i].x)[q >> 1];
+    return __uint_as_float((q & 1) ? (w & 0xffff0000u) : (w << 16));
+  };
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CE_VPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if ((tid + i * CE_THREADS) * 8 + q < V) m = fmaxf(m, val(i, q));
+  const float gm = ce_block_reduce(m, true, red);
+  float sacc = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_VPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if ((tid + i * CE_THREADS) * 8 + q < V) sacc += __expf(val(i, q) - gm);
+  const float lse = gm + __logf(ce_block_reduce(sacc, false, red));
+#pragma unroll
+  for (int i = 0; i < CE_VPT; ++i) {
+    const int idx = tid + i * CE_THREADS;
+    if (idx >= nv8) continue;
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c0 = idx * 8 + 2 * q, c1 = c0 + 1;
+      const float d0 = c0 < V ? (__expf(val(i, 2 * q) - lse) - (c0 == y ? 1.f : 0.f)) * scale : 0.f;
+      const float d1 = c1 < V ? (__expf(val(i, 2 * q + 1) - lse) - (c1 == y ? 1.f : 0.f)) * scale : 0.f;
+      o[q] = pack_bf2(d0, d1);
+    }
+    ((uint4 *)z)[idx] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (tid == 0) {
+    row_loss[row] = y_ok ? lse - zy : NAN;
+    if (!y_ok) atomicOr(flags, 1);
+  }
+}
+
 // Deterministic mean of n floats in one block.
 __global__ void __launch_bounds__(256) mean_kernel(int n, const float *__restrict__ src,
                                                    float *__restrict__ out) {
@@ -525,11 +605,16 @@ int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
   TT_REQUIRE(ctx, N > 0 && V > 0 && ld >= V, "ce: bad shape N=%d V=%d ld=%d", N, V, ld);
   TT_REQUIRE(ctx, logits && targets && per_row_loss && loss, "ce: NULL pointer");
   {
+  // algorithmic: one read and one write of the logits
   tt_prof_scope prof(ctx, "ce_kernel", 0.0, 2.0 * N * (double)ld * (mode == TT_BF16 ? 2.0 : 4.0) + 8.0 * N);
   if (mode == TT_BF16) {
     TT_REQUIRE(ctx, ld % 8 == 0 && tt_aligned16(logits), "ce(bf16): ld %% 8 and 16-byte alignment required");
-    hipLaunchKernelGGL(ce_kernel<true>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
-                       targets, per_row_loss, grad_scale, ctx->dev_flags);
+    if (ld <= CE_VPT * 8 * CE_THREADS)
+      hipLaunchKernelGGL(ce_reg_kernel, dim3(N), dim3(CE_THREADS), 0, ctx->stream, N, V, ld,
+                         (bf16_t *)logits, targets, per_row_loss, grad_scale, ctx->dev_flags);
+    else
+      hipLaunchKernelGGL(ce_kernel<true>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
+                         targets, per_row_loss, grad_scale, ctx->dev_flags);
   } else {
     hipLaunchKernelGGL(ce_kernel<false>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
                        targets, per_row_loss, grad_scale, ctx->dev_flags);
