@@ -30,7 +30,7 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int HS = 64;
-constexpr int LDT = HS + 8;            // LDS row: 144 bytes
+constexpr int LDT = HS + 16;           // LDS row: 160 bytes
 constexpr uint32_t OOB = 0x7ffffff0u;  // buffer offset past every tensor (host checks sizes)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SL2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) folded into exp2
