@@ -54,14 +54,16 @@ int linear_dx_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *d
   return tt_gemm(ctx, mode, g);
 }
 
-// dW[K,N] += Xᵀ · dY  (X [M,K] row-major with ldx, dY [M,N] with ldy).
+// dW[K,N] += Xᵀ · dY  (X [M,K] row-major with ldx, dY [M,N] with ldy); with
+// overwrite, dW = Xᵀ · dY.
 int linear_dw_gemm(tt_ctx *ctx, tt_mode mode, int M, int K, int N, const void *X, int ldx,
-                   const void *dY, int ldy, float *dW) {
+                   const void *dY, int ldy, float *dW, bool overwrite = false) {
   GemmArgs g = gemm_args();
   g.A = X; g.lda = ldx; g.a_kmajor = false;
   g.B = dY; g.ldb = ldy; g.b_kmajor = false;
   g.M = K; g.N = N; g.K = M;
   g.epi = EPI_ACCUM; g.out = dW; g.ldo = N; g.out_bf16 = false;
+  g.overwrite = overwrite;
   return tt_gemm(ctx, mode, g);
 }
 
@@ -147,10 +149,12 @@ int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, flo
 // fcp_bias_here, else already accumulated by whoever produced R (the
 // LayerNorm backward above this block).  dsum_below (nullable) receives the
 // column sums of the returned Rl, i.e. the down-projection bias gradient of
-// the block below.
+// the block below.  overwrite_dw: the weight-matrix gradients are stored
+// (=) instead of accumulated (+=).
 int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
               const tt_block_w &w, const LayerBufs &s, const float *x, float *R, void *Rl,
-              const tt_block_g &gr, const BwdScratch &sc, bool fcp_bias_here, float *dsum_below) {
+              const tt_block_g &gr, const BwdScratch &sc, bool fcp_bias_here, float *dsum_below,
+              bool overwrite_dw) {
   const int N = B * T;
   const bool lp = mode == TT_BF16;
   bf16_t *Rb = lp ? (bf16_t *)Rl : nullptr;
@@ -158,25 +162,25 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   // the up-projection's bias gradient; dW_fp += gᵀ dy; db_fp.
   TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, Rl, C, w.w_fcp, EPI_GELU_BWD, sc.dh, F, lp, s.h, F,
                         gr.b_fc));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, Rl, C, gr.w_fcp));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, Rl, C, gr.w_fcp, overwrite_dw));
   if (fcp_bias_here) TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_fcp));
   // MLP up-projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, sc.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
                         nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, sc.dh, F, gr.w_fc));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, sc.dh, F, gr.w_fc, overwrite_dw));
   // LN2 backward + residual: R = R + LN2_bwd(dtmp); its column sums are the
   // attention projection's bias gradient.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R, Rb,
                                gr.ln2_g, gr.ln2_b, gr.b_proj));
   // Attention projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, Rl, C, w.w_proj, EPI_STORE, sc.datt, C, lp, nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, Rl, C, gr.w_proj));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, Rl, C, gr.w_proj, overwrite_dw));
   // Attention.
   TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, sc.dqkv, sc.Dv));
   // QKV projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, 3 * C, sc.dqkv, 3 * C, w.w_qkv, EPI_STORE, sc.dtmp, C,
                         false, nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, sc.dqkv, 3 * C, gr.w_qkv));
+  TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, sc.dqkv, 3 * C, gr.w_qkv, overwrite_dw));
   TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, sc.dqkv, gr.b_qkv));
   // LN1 backward + residual.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R, Rb,
@@ -301,7 +305,8 @@ extern "C" int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, voi
 // the extra terms vanish.
 static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld, const void *h,
                           const void *wte, const void *wte_t, int V_pad, const int32_t *targets,
-                          float *loss, float *dh, float *dwte, void *logits, float *row_loss) {
+                          float *loss, float *dh, float *dwte, void *logits, float *row_loss,
+                          bool overwrite_dwte) {
   const bool lp = mode == TT_BF16;
   GemmArgs g = gemm_args();
   // z = h · wteᵀ
@@ -331,6 +336,7 @@ static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld
   g.B = h; g.ldb = C; g.b_kmajor = false;
   g.M = V; g.N = C; g.K = N;
   g.epi = EPI_ACCUM; g.out = dwte; g.ldo = C; g.out_bf16 = false;
+  g.overwrite = overwrite_dwte;   // rows < V only: the pad rows stay as they are
   return tt_gemm(ctx, mode, g);
 }
 
@@ -348,7 +354,7 @@ extern "C" int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int 
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * ld * esize(mode), &logits));
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * 4, &rows));
   return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, nullptr, 0, targets, loss, dh, dwte,
-                        logits, (float *)rows);
+                        logits, (float *)rows, false);
 }
 
 // ------------------------------------------------------------ block ABI
@@ -431,7 +437,7 @@ extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
     TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl));
   }
   return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, Rl,
-                   *g, sc, true, nullptr);
+                   *g, sc, true, nullptr, false);
 }
 
 extern "C" void tt_block_saved_destroy(tt_block_saved *saved) {
@@ -450,6 +456,7 @@ struct tt_model {
   tt_ctx *ctx;
   tt_model_cfg cfg;
   size_t n_slots = 0, n_params = 0;
+  size_t small_begin = 0;   // first slot of the accumulated (non-matrix) tensors
   std::vector<size_t> off, numel;
   float *w = nullptr, *g = nullptr, *m = nullptr, *v = nullptr;
   bf16_t *lowp = nullptr;
@@ -532,20 +539,34 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   md->magic = TT_MODEL_MAGIC;
   md->ctx = ctx;
   md->cfg = c;
-  auto add = [&](size_t n) {
-    md->off.push_back(md->n_slots);
+  // Slots: the weight matrices first (each gradient is written whole by one
+  // GEMM per step), then every other tensor in one contiguous region (their
+  // gradients accumulate and are cleared each step with one fill).  Tensor
+  // indices keep the documented order.
+  std::vector<bool> whole;
+  auto add = [&](size_t n, bool w) {
     md->numel.push_back(n);
+    whole.push_back(w);
     md->n_params += n;
-    md->n_slots += (n + 63) / 64 * 64;  // 256-byte aligned tensors
   };
   const size_t C = c.C, F = c.F;
-  add((size_t)c.V_pad * C);
-  add((size_t)c.T_max * C);
+  add((size_t)c.V_pad * C, true);
+  add((size_t)c.T_max * C, false);
   for (int l = 0; l < c.L; ++l) {
-    add(C); add(C); add(C * 3 * C); add(3 * C); add(C * C); add(C);
-    add(C); add(C); add(C * F); add(F); add(F * C); add(C);
+    add(C, false); add(C, false); add(C * 3 * C, true); add(3 * C, false); add(C * C, true);
+    add(C, false); add(C, false); add(C, false); add(C * F, true); add(F, false); add(F * C, true);
+    add(C, false);
   }
-  add(C); add(C);
+  add(C, false); add(C, false);
+  md->off.assign(md->numel.size(), 0);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) md->small_begin = md->n_slots;
+    for (size_t i = 0; i < md->numel.size(); ++i)
+      if (whole[i] == (pass == 0)) {
+        md->off[i] = md->n_slots;
+        md->n_slots += (md->numel[i] + 63) / 64 * 64;  // 256-byte aligned tensors
+      }
+  }
   const size_t save = ctx->offset;
   int rc = TT_OK;
   void *p;
@@ -670,7 +691,9 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   const int N = B * T, C = c.C;
   const bool lp = mode == TT_BF16;
 
-  TT_TRY(tt_fill_f32(ctx, md->g, md->n_slots, 0.f));
+  // Matrix gradients are overwritten by their GEMMs; clear the rest.  (The
+  // token table's pad rows are never written and stay zero from creation.)
+  TT_TRY(tt_fill_f32(ctx, md->g + md->small_begin, md->n_slots - md->small_begin, 0.f));
   TT_TRY(tt_embed_fwd(ctx, B, T, C, c.V, tok, md->w + md->off[P_WTE], md->w + md->off[P_WPE],
                       md->xs[0]));
   tt_block_w w;
@@ -686,7 +709,7 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
                                md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
   TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), mat_t(md, P_WTE),
                         c.V_pad, targets, loss, md->sc.dtmp, md->g + md->off[P_WTE], md->logits,
-                        md->row_loss));
+                        md->row_loss, true));
   // Each LayerNorm backward also sums its output's columns into the
   // down-projection bias gradient of the block below it.
   auto fcp_bias = [&](int l) { return md->g + md->off[P_LAYER0 + PER_LAYER * l + 11]; };
@@ -697,7 +720,7 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   for (int l = c.L - 1; l >= 0; --l) {
     layer_views(md, l, w, wt, gr);
     TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, md->Rl, gr,
-                     md->sc, false, l > 0 ? fcp_bias(l - 1) : nullptr));
+                     md->sc, false, l > 0 ? fcp_bias(l - 1) : nullptr, true));
   }
   return tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
                       md->g + md->off[P_WPE]);

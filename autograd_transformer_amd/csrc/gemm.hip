@@ -395,6 +395,11 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
   // Column sums of the output (g.colsum) are fused into the epilogue of the
   // direct-to-LDS bf16 kernel; every other path sums the stored output after.
   const bool fast = mode == TT_BF16 && vec && tt_gemm_bf16_ok(g);
+  if (g.epi == EPI_ACCUM && g.overwrite && !fast) {
+    // the generic kernels accumulate with atomics: clear the output first
+    TT_REQUIRE(ctx, g.ldo == g.N, "gemm: overwrite needs a dense output");
+    TT_TRY(tt_fill_f32(ctx, (float *)g.out, (size_t)g.M * g.N, 0.f));
+  }
   const bool fused_sum = fast && g.epi != EPI_ACCUM && g.a_kmajor && g.b_kmajor;
   GemmArgs h = g;
   if (!fused_sum) h.colsum = nullptr;

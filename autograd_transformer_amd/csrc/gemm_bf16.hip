@@ -607,9 +607,10 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   return TT_EINVAL;
 }
 
+// out (+)= sum of the split partials (accumulate = 0: out is overwritten).
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ out, int ldo,
                                                              const float *__restrict__ ws, int M,
-                                                             int N, int split) {
+                                                             int N, int split, int accumulate) {
   const size_t mn = (size_t)M * N;
   const size_t n4 = mn / 4;
   const size_t stride = (size_t)gridDim.x * 256;
@@ -623,14 +624,18 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ 
       const size_t e = i * 4;
       const int m = (int)(e / N), n = (int)(e % N);
       float4 *o = (float4 *)(out + (size_t)m * ldo + n);
-      float4 c = *o;
-      *o = make_float4(c.x + s.x, c.y + s.y, c.z + s.z, c.w + s.w);
+      if (accumulate) {
+        const float4 c = *o;
+        s.x += c.x; s.y += c.y; s.z += c.z; s.w += c.w;
+      }
+      *o = s;
     }
   } else {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += stride) {
       float s = ws[i];
       for (int z = 1; z < split; ++z) s += ws[z * mn + i];
-      out[(i / N) * ldo + i % N] += s;
+      float *o = out + (i / N) * ldo + i % N;
+      *o = accumulate ? *o + s : s;
     }
   }
 }
@@ -695,7 +700,9 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   GemmArgs h = g;
   if (h.raster == 0) h.raster = 1;
   if (split == 1) {
-    h.epi = EPI_STORE_ACC;
+    h.epi = g.overwrite ? EPI_STORE : EPI_STORE_ACC;
+    h.out_bf16 = false;
+    h.bias = nullptr;
     return launch3<256, 128, 32, 4, 2, 2>(ctx, h, 1);
   }
   tt_scratch_scope scope(ctx);
@@ -711,8 +718,9 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   TT_TRY((launch3<256, 128, 32, 4, 2, 2>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
-  tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0, (split + 2.0) * g.M * g.N * 4.0);
+  tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0,
+                     (split + (g.overwrite ? 1.0 : 2.0)) * g.M * g.N * 4.0);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, ctx->stream, (float *)g.out,
-                     g.ldo, (const float *)ws, g.M, g.N, split);
+                     g.ldo, (const float *)ws, g.M, g.N, split, g.overwrite ? 0 : 1);
   return tt_check_launch(ctx, "splitk_reduce");
 }

@@ -171,6 +171,7 @@ struct GemmArgs {
   int n_valid;                 // columns >= n_valid of C are not stored (ragged pad); 0 = N
   float *colsum;               // nullable: colsum[n] += sum over rows of the stored output
   int raster;                  // tile order: 0 auto, 1 m fastest, 2 n fastest
+  bool overwrite;              // EPI_ACCUM only: store the product instead of adding it
 };
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
 // bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
