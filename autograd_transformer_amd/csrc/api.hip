@@ -142,49 +142,66 @@ int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, flo
   return TT_OK;
 }
 
-// Block backward, in place on the residual gradient R (fp32) and its GEMM
-// operand copy Rl (bf16 copy in TT_BF16, == R in TT_F32).  On entry R holds
-// dL/dy; on return it holds dL/dx.  The bias gradient of the MLP
-// down-projection is the column sum of Rl on entry: computed here when
+// Where one block's backward reads and writes its activation gradients.
+// rl_in is the GEMM operand copy of the residual gradient on entry (bf16 in
+// TT_BF16, the fp32 gradient itself in TT_F32), rl_mid the copy written by the
+// LN2 backward, rl_out (nullable in TT_BF16) the copy of the returned
+// gradient; dh and dqkv receive the MLP and attention input gradients.  One
+// buffer may serve all three copies when nothing reads them later; kept
+// apart, they let the weight gradients run after the whole backward.
+struct BwdIO {
+  void *rl_in, *rl_mid, *rl_out;
+  void *dh, *dqkv;
+  bool defer_dw;   // leave the four weight-matrix gradients to the caller
+};
+
+// Block backward, in place on the residual gradient R (fp32): on entry R
+// holds dL/dy, on return dL/dx.  The bias gradient of the MLP
+// down-projection is the column sum of rl_in: computed here when
 // fcp_bias_here, else already accumulated by whoever produced R (the
 // LayerNorm backward above this block).  dsum_below (nullable) receives the
-// column sums of the returned Rl, i.e. the down-projection bias gradient of
-// the block below.  overwrite_dw: the weight-matrix gradients are stored
-// (=) instead of accumulated (+=).
+// column sums of rl_out, i.e. the down-projection bias gradient of the block
+// below.  overwrite_dw: the weight-matrix gradients are stored (=) instead of
+// accumulated (+=).
 int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
-              const tt_block_w &w, const LayerBufs &s, const float *x, float *R, void *Rl,
+              const tt_block_w &w, const LayerBufs &s, const float *x, float *R, const BwdIO &io,
               const tt_block_g &gr, const BwdScratch &sc, bool fcp_bias_here, float *dsum_below,
               bool overwrite_dw) {
   const int N = B * T;
   const bool lp = mode == TT_BF16;
-  bf16_t *Rb = lp ? (bf16_t *)Rl : nullptr;
   // MLP down-projection: dh = (dy · W_fpᵀ) * gelu'(h), whose column sums are
   // the up-projection's bias gradient; dW_fp += gᵀ dy; db_fp.
-  TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, Rl, C, w.w_fcp, EPI_GELU_BWD, sc.dh, F, lp, s.h, F,
-                        gr.b_fc));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, Rl, C, gr.w_fcp, overwrite_dw));
-  if (fcp_bias_here) TT_TRY(tt_colsum(ctx, lp, N, C, C, Rl, gr.b_fcp));
+  TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, io.rl_in, C, w.w_fcp, EPI_GELU_BWD, io.dh, F, lp, s.h,
+                        F, gr.b_fc));
+  if (!io.defer_dw)
+    TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, io.rl_in, C, gr.w_fcp, overwrite_dw));
+  if (fcp_bias_here) TT_TRY(tt_colsum(ctx, lp, N, C, C, io.rl_in, gr.b_fcp));
   // MLP up-projection.
-  TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, sc.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, io.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
                         nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, sc.dh, F, gr.w_fc, overwrite_dw));
+  if (!io.defer_dw)
+    TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, io.dh, F, gr.w_fc, overwrite_dw));
   // LN2 backward + residual: R = R + LN2_bwd(dtmp); its column sums are the
   // attention projection's bias gradient.
-  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R, Rb,
-                               gr.ln2_g, gr.ln2_b, gr.b_proj));
+  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
+                               lp ? (bf16_t *)io.rl_mid : nullptr, gr.ln2_g, gr.ln2_b, gr.b_proj));
   // Attention projection.
-  TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, Rl, C, w.w_proj, EPI_STORE, sc.datt, C, lp, nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, Rl, C, gr.w_proj, overwrite_dw));
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, io.rl_mid, C, w.w_proj, EPI_STORE, sc.datt, C, lp,
+                        nullptr, 0));
+  if (!io.defer_dw)
+    TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, io.rl_mid, C, gr.w_proj, overwrite_dw));
   // Attention.
-  TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, sc.dqkv, sc.Dv));
+  TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, io.dqkv, sc.Dv));
   // QKV projection.
-  TT_TRY(linear_dx_gemm(ctx, mode, N, C, 3 * C, sc.dqkv, 3 * C, w.w_qkv, EPI_STORE, sc.dtmp, C,
+  TT_TRY(linear_dx_gemm(ctx, mode, N, C, 3 * C, io.dqkv, 3 * C, w.w_qkv, EPI_STORE, sc.dtmp, C,
                         false, nullptr, 0));
-  TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, sc.dqkv, 3 * C, gr.w_qkv, overwrite_dw));
-  TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, sc.dqkv, gr.b_qkv));
+  if (!io.defer_dw)
+    TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, io.dqkv, 3 * C, gr.w_qkv,
+                          overwrite_dw));
+  TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, io.dqkv, gr.b_qkv));
   // LN1 backward + residual.
-  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R, Rb,
-                               gr.ln1_g, gr.ln1_b, dsum_below));
+  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
+                               lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b, dsum_below));
   return TT_OK;
 }
 
@@ -306,7 +323,7 @@ extern "C" int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, voi
 static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld, const void *h,
                           const void *wte, const void *wte_t, int V_pad, const int32_t *targets,
                           float *loss, float *dh, float *dwte, void *logits, float *row_loss,
-                          bool overwrite_dwte) {
+                          bool overwrite_dwte, bool skip_dwte = false) {
   const bool lp = mode == TT_BF16;
   GemmArgs g = gemm_args();
   // z = h · wteᵀ
@@ -330,6 +347,7 @@ static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld
   }
   g.epi = EPI_STORE; g.out = dh; g.ldo = C; g.out_bf16 = false;
   TT_TRY(tt_gemm(ctx, mode, g));
+  if (skip_dwte) return TT_OK;
   // dwte += dzᵀ · h
   g = gemm_args();
   g.A = logits; g.lda = ld; g.a_kmajor = false;
@@ -436,7 +454,8 @@ extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
     TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * 2, &Rl));
     TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl));
   }
-  return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, Rl,
+  const BwdIO io{Rl, Rl, Rl, sc.dh, sc.dqkv, false};
+  return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, io,
                    *g, sc, true, nullptr, false);
 }
 
@@ -477,6 +496,12 @@ struct tt_model {
   float *R = nullptr;
   void *Rl = nullptr;
   BwdScratch sc;
+  // TT_BF16: every layer keeps the activation gradients its weight gradients
+  // need (the residual gradient's bf16 copies on entry and after the LN2
+  // backward, dh, dqkv), so that all weight-matrix gradients, the token
+  // table's included, run as one grouped GEMM after the backward.
+  std::vector<BwdIO> lio;
+  GemmGroup dw_group;
 };
 
 namespace {
@@ -621,6 +646,41 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   md->R = (float *)alloc((size_t)N * C * 4);
   md->Rl = c.mode == TT_BF16 ? alloc((size_t)N * C * 2) : (void *)md->R;
   if (rc == TT_OK) rc = alloc_bwd_scratch(ctx, c.mode, N, c.C, c.F, c.B_max, c.NH, c.T_max, md->sc);
+  if (rc == TT_OK && c.mode == TT_BF16) {
+    md->lio.resize(c.L);
+    for (int l = 0; l < c.L; ++l) {
+      BwdIO &io = md->lio[l];
+      io.rl_in = alloc((size_t)N * C * 2);
+      io.rl_mid = alloc((size_t)N * C * 2);
+      io.dh = alloc((size_t)N * F * 2);
+      io.dqkv = alloc((size_t)N * 3 * C * 2);
+      io.defer_dw = true;
+    }
+    for (int l = 0; l < c.L; ++l) md->lio[l].rl_out = l > 0 ? md->lio[l - 1].rl_in : nullptr;
+    // The grouped weight-gradient products: dW = Xᵀ · dY with both operands
+    // token-major.  Token table first (the largest product), then the layers.
+    std::vector<GemmGroupEntry> ent;
+    auto prod = [&](const void *X, int ldx, int rows, const void *dY, int ldy, int cols, float *out) {
+      GemmGroupEntry e{};
+      e.A = X; e.lda = ldx; e.M = rows;
+      e.B = dY; e.ldb = ldy; e.N = cols;
+      e.out = out; e.ldo = cols;
+      ent.push_back(e);
+    };
+    if (rc == TT_OK) {
+      prod(md->logits, md->ld, c.V, md->lnf, c.C, c.C, md->g + md->off[P_WTE]);
+      for (int l = c.L - 1; l >= 0; --l) {
+        const int b = P_LAYER0 + PER_LAYER * l;
+        const LayerBufs &s = md->layers[l];
+        const BwdIO &io = md->lio[l];
+        prod(s.g, c.F, c.F, io.rl_in, c.C, c.C, md->g + md->off[b + 10]);
+        prod(s.ln2, c.C, c.C, io.dh, c.F, c.F, md->g + md->off[b + 8]);
+        prod(s.att, c.C, c.C, io.rl_mid, c.C, c.C, md->g + md->off[b + 4]);
+        prod(s.ln1, c.C, c.C, io.dqkv, 3 * c.C, 3 * c.C, md->g + md->off[b + 2]);
+      }
+      rc = tt_gemm_group_plan(ctx, ent.data(), (int)ent.size(), N, &md->dw_group);
+    }
+  }
   for (float *buf : {md->w, md->g, md->m, md->v})
     if (rc == TT_OK) rc = tt_fill_f32(ctx, buf, md->n_slots, 0.f);
   if (rc == TT_OK && md->lowp) rc = tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp);
@@ -707,21 +767,28 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   const int lf = p_lnf_g(md);
   TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, c.ln_eps, md->xs[c.L], md->w + md->off[lf],
                                md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
+  const bool grouped = !md->lio.empty();
   TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), mat_t(md, P_WTE),
                         c.V_pad, targets, loss, md->sc.dtmp, md->g + md->off[P_WTE], md->logits,
-                        md->row_loss, true));
+                        md->row_loss, true, grouped));
   // Each LayerNorm backward also sums its output's columns into the
   // down-projection bias gradient of the block below it.
   auto fcp_bias = [&](int l) { return md->g + md->off[P_LAYER0 + PER_LAYER * l + 11]; };
+  void *rl_top = grouped ? md->lio[c.L - 1].rl_in : md->Rl;
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
                                md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
-                               lp ? (bf16_t *)md->Rl : nullptr, md->g + md->off[lf],
+                               lp ? (bf16_t *)rl_top : nullptr, md->g + md->off[lf],
                                md->g + md->off[lf + 1], fcp_bias(c.L - 1)));
   for (int l = c.L - 1; l >= 0; --l) {
     layer_views(md, l, w, wt, gr);
-    TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, md->Rl, gr,
+    const BwdIO io = grouped ? md->lio[l]
+                             : BwdIO{md->Rl, md->Rl, md->Rl, md->sc.dh, md->sc.dqkv, false};
+    TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, io, gr,
                      md->sc, false, l > 0 ? fcp_bias(l - 1) : nullptr, true));
   }
+  // Every weight-matrix gradient (stored, not accumulated) in one launch;
+  // then the token rows of the embedding add into the token table's.
+  if (grouped) TT_TRY(tt_gemm_group_run(ctx, md->dw_group, N));
   return tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
                       md->g + md->off[P_WPE]);
 }

@@ -16,6 +16,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "gemm_common.h"
 
@@ -370,6 +371,7 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
 struct Cfg3 {
+  static constexpr int BM_ = BM, BN_ = BN, WM_ = WM, WN_ = WN;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -389,80 +391,19 @@ struct Cfg3 {
   static constexpr int WAVES_PER_EU = (NW * WG_PER_CU + 3) / 4;
 };
 
-template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM>
-__global__ void __launch_bounds__(64 * WM * WN,
-                                  (Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>::WAVES_PER_EU))
-gemm_bf16_v3_kernel(GemmParams p) {
-  using C = Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>;
-  using OA = typename C::OA;
-  using OB = typename C::OB;
-  constexpr int NW = C::NW, NT = C::NT, FM = C::FM, FN = C::FN;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::SMEM];
-  bf16_t *smem = (bf16_t *)smem_raw;
+// Epilogue shared by the direct-to-LDS kernels: the C tile goes through LDS
+// one wave-row at a time (fp32), then every thread applies bias / activation /
+// residual to 4 consecutive columns with row-coalesced accesses; optional
+// column sums of the stored values (bias gradients).  The caller has passed
+// a barrier after the last LDS read of the main loop.
+template <class C>
+__device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM][C::FN], char *smem_raw,
+                                            int m0, int n0) {
+  constexpr int NT = C::NT, FM = C::FM, FN = C::FN, BN = C::BN_, WM = C::WM_, WN = C::WN_;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = blockIdx.z * p.k_chunk;
-  const int kend = min(p.K, kbeg + p.k_chunk);
-  const __amdgpu_buffer_rsrc_t rsa =
-      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
-
-  f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto At = [&](int s) { return smem + s * C::STAGE; };
-  auto Bt = [&](int s) { return smem + s * C::STAGE + OA::ELEMS; };
-  auto issue = [&](int stage, int buf) {
-    const int k0 = kbeg + stage * BKV;
-    OA::template issue<NW>(At(buf), rsa, p.lda, m0, k0, p.M, kend, wave, lane);
-    OB::template issue<NW>(Bt(buf), rsb, p.ldb, n0, k0, p.N, kend, wave, lane);
-  };
-  const int nk = (kend - kbeg + BKV - 1) / BKV;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
-  {
-    for (int it = 0; it < nk; ++it) {
-      // Stage it must have landed (from every wave) before anyone reads it:
-      // each wave waits for its own loads of that stage, then a bare barrier
-      // (no memory fence, which would also drain the loads still in flight
-      // for later stages).  The buffer refilled below was last read in
-      // iteration it-1, whose LDS reads every wave has consumed before
-      // reaching here.  The empty asm statements keep the compiler from
-      // moving LDS accesses across the barrier (the barrier builtin is not a
-      // memory operation to it); they emit no instruction and no wait.
-      if (it + NS - 2 < nk) wait_vm<(NS - 2) * C::LPS>();
-      else wait_vm<0>();
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
-      const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
-#pragma unroll
-      for (int kk = 0; kk < BKV; kk += 32) {
-        bf16x8_t fb[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }  __syncthreads();
-
   if (p.out_zstride) p.out = (float *)p.out + blockIdx.z * p.out_zstride;
   float *Cs = (float *)smem_raw;
   constexpr int TPR = BN / 4;
@@ -563,6 +504,103 @@ gemm_bf16_v3_kernel(GemmParams p) {
       if (n0 + c < nv) unsafeAtomicAdd(&p.colsum[n0 + c], t);
     }
   }
+}
+
+template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM, bool GROUP = false>
+__global__ void __launch_bounds__(64 * WM * WN,
+                                  (Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>::WAVES_PER_EU))
+gemm_bf16_v3_kernel(GemmParams p) {
+  using C = Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>;
+  using OA = typename C::OA;
+  using OB = typename C::OB;
+  constexpr int NW = C::NW, NT = C::NT, FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::SMEM];
+  bf16_t *smem = (bf16_t *)smem_raw;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lg = lane >> 4;
+  int tm, tn;
+  if constexpr (GROUP) {
+    // Grouped launch: spread the grid XCD-first (the grid is padded to a
+    // multiple of 8), find the problem that owns this workgroup, and take its
+    // operands, output and shape (the tile order inside a problem has no XCD
+    // step of its own).
+    const int nwg = gridDim.x;
+    const int bid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+    const int e = p.group_map[bid];
+    if (e == 0xffff) return;   // padding: the whole workgroup leaves
+    const GemmGroupEntry q = p.group[e];
+    p.A = q.A; p.B = q.B; p.out = q.out;
+    p.lda = q.lda; p.ldb = q.ldb; p.ldo = q.ldo;
+    p.M = q.M; p.N = q.N; p.n_valid = q.N;
+    p.tiles_m = q.tiles_m; p.tiles_n = q.tiles_n; p.vec_out = q.vec_out;
+    p.a_bytes = (uint32_t)(((size_t)(p.K - 1) * q.lda + q.M) * 2);
+    p.b_bytes = (uint32_t)(((size_t)(p.K - 1) * q.ldb + q.N) * 2);
+    tile_coords(bid - q.tile0, q.tiles_m * q.tiles_n, q.tiles_m, q.tiles_n, p.raster_n, tm, tn,
+                false);
+  } else {
+    tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.z * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto At = [&](int s) { return smem + s * C::STAGE; };
+  auto Bt = [&](int s) { return smem + s * C::STAGE + OA::ELEMS; };
+  auto issue = [&](int stage, int buf) {
+    const int k0 = kbeg + stage * BKV;
+    OA::template issue<NW>(At(buf), rsa, p.lda, m0, k0, p.M, kend, wave, lane);
+    OB::template issue<NW>(Bt(buf), rsb, p.ldb, n0, k0, p.N, kend, wave, lane);
+  };
+  const int nk = (kend - kbeg + BKV - 1) / BKV;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  {
+    for (int it = 0; it < nk; ++it) {
+      // Stage it must have landed (from every wave) before anyone reads it:
+      // each wave waits for its own loads of that stage, then a bare barrier
+      // (no memory fence, which would also drain the loads still in flight
+      // for later stages).  The buffer refilled below was last read in
+      // iteration it-1, whose LDS reads every wave has consumed before
+      // reaching here.  The empty asm statements keep the compiler from
+      // moving LDS accesses across the barrier (the barrier builtin is not a
+      // memory operation to it); they emit no instruction and no wait.
+      if (it + NS - 2 < nk) wait_vm<(NS - 2) * C::LPS>();
+      else wait_vm<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+      const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
+#pragma unroll
+      for (int kk = 0; kk < BKV; kk += 32) {
+        bf16x8_t fb[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  v3_epilogue<C>(p, acc, smem_raw, m0, n0);
 }
 
 template <int BM, int BN, int BKV, int WM, int WN, int NS>
@@ -723,4 +761,78 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, ctx->stream, (float *)g.out,
                      g.ldo, (const float *)ws, g.M, g.N, split, g.overwrite ? 0 : 1);
   return tt_check_launch(ctx, "splitk_reduce");
+}
+
+// ------------------------------------------------------------ grouped launch
+// The products of a group share one kernel configuration (the weight-gradient
+// tile: 256 x 128, BK 32, 2 stages, both operands read with the LDS transpose)
+// and one reduction length; each workgroup owns one output tile of one
+// product.  Run as one launch, the 48 weight gradients of a 12-layer model
+// and the token-table gradient fill the machine without splitting K.
+namespace {
+constexpr int GBM = 256, GBN = 128, GBK = 32;
+}
+
+int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max,
+                       GemmGroup *out) {
+  TT_REQUIRE(ctx, entries && out && n > 0 && k_max > 0, "gemm_group: bad arguments");
+  std::vector<GemmGroupEntry> t(entries, entries + n);
+  int tiles = 0;
+  double mn2 = 0;
+  for (auto &e : t) {
+    TT_REQUIRE(ctx, e.A && e.B && e.out && e.M > 0 && e.N > 0, "gemm_group: bad entry");
+    TT_REQUIRE(ctx, e.lda >= e.M && e.ldb >= e.N && e.ldo >= e.N, "gemm_group: bad leading dims");
+    TT_REQUIRE(ctx, tt_aligned16(e.A) && tt_aligned16(e.B) && e.lda % 8 == 0 && e.ldb % 8 == 0,
+               "gemm_group: operand rows must be 16-byte aligned");
+    TT_REQUIRE(ctx, gemm_extent_bytes(false, e.M, k_max, e.lda) < OOB &&
+                        gemm_extent_bytes(false, e.N, k_max, e.ldb) < OOB,
+               "gemm_group: operand too large for buffer addressing");
+    e.tiles_m = (e.M + GBM - 1) / GBM;
+    e.tiles_n = (e.N + GBN - 1) / GBN;
+    e.tile0 = tiles;
+    e.vec_out = ((uintptr_t)e.out % 16 == 0 && e.ldo % 4 == 0) ? 1 : 0;
+    tiles += e.tiles_m * e.tiles_n;
+    mn2 += 2.0 * e.M * e.N;
+  }
+  const int grid = (tiles + 7) / 8 * 8;
+  TT_REQUIRE(ctx, grid < 0xffff && n < 0xffff, "gemm_group: too many tiles");
+  std::vector<uint16_t> map(grid, 0xffff);
+  for (int i = 0; i < n; ++i)
+    for (int k = 0; k < t[i].tiles_m * t[i].tiles_n; ++k) map[t[i].tile0 + k] = (uint16_t)i;
+  void *pt, *pm;
+  TT_TRY(tt_arena_alloc(ctx, t.size() * sizeof(GemmGroupEntry), &pt));
+  TT_TRY(tt_arena_alloc(ctx, map.size() * sizeof(uint16_t), &pm));
+  hipError_t e1 = hipMemcpyAsync(pt, t.data(), t.size() * sizeof(GemmGroupEntry),
+                                 hipMemcpyHostToDevice, ctx->stream);
+  hipError_t e2 = hipMemcpyAsync(pm, map.data(), map.size() * sizeof(uint16_t),
+                                 hipMemcpyHostToDevice, ctx->stream);
+  if (e1 != hipSuccess || e2 != hipSuccess)
+    return tt_set_error(ctx, TT_EHIP, "gemm_group: table upload failed");
+  // the host vectors die here: make sure the copies have read them
+  hipError_t e3 = hipStreamSynchronize(ctx->stream);
+  if (e3 != hipSuccess) return tt_set_error(ctx, TT_EHIP, "gemm_group: %s", hipGetErrorString(e3));
+  out->table = (GemmGroupEntry *)pt;
+  out->map = (uint16_t *)pm;
+  out->n = n;
+  out->tiles = tiles;
+  out->grid = grid;
+  out->mn2 = mn2;
+  return TT_OK;
+}
+
+int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K) {
+  TT_REQUIRE(ctx, g.table && g.map && g.grid > 0 && K > 0, "gemm_group: not planned");
+  GemmParams p{};
+  p.K = K;
+  p.k_chunk = (K + GBK - 1) / GBK * GBK;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.raster_n = 0;
+  p.group = g.table;
+  p.group_map = g.map;
+  tt_prof_scope prof(ctx, "gemm_bf16_v3_kernel<256, 128, 32, 4, 2, 2, false, false, true>",
+                     g.mn2 * K, 0.0);
+  hipLaunchKernelGGL((gemm_bf16_v3_kernel<GBM, GBN, GBK, 4, 2, 2, false, false, true>),
+                     dim3(g.grid), dim3(512), 0, ctx->stream, p);
+  return tt_check_launch(ctx, "gemm_group");
 }

@@ -22,6 +22,8 @@ struct GemmParams {
   size_t out_zstride;         // split-K partials: output offset per blockIdx.z (elements)
   float *colsum;              // nullable: += column sums of the stored output (v3 kernel)
   int raster_n;               // tile order: 1 = n fastest (share A panels), 0 = m fastest
+  const GemmGroupEntry *group;   // grouped launch: problem table (device), else null
+  const uint16_t *group_map;     // grouped launch: workgroup -> table entry
 };
 
 __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
@@ -129,9 +131,9 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
 // consecutive workgroups share B panels) or, with raster_n, of G tile-columns
 // (n fastest: they share A panels), whichever operand is larger.
 __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
-                                            int raster_n, int &tm, int &tn) {
+                                            int raster_n, int &tm, int &tn, bool xcd = true) {
   constexpr int XCDS = 8, G = 8;
-  if (nwg % XCDS == 0) bid = (bid % XCDS) * (nwg / XCDS) + bid / XCDS;
+  if (xcd && nwg % XCDS == 0) bid = (bid % XCDS) * (nwg / XCDS) + bid / XCDS;
   const int major = raster_n ? tiles_n : tiles_m, minor = raster_n ? tiles_m : tiles_n;
   const int per_group = G * minor;
   const int group = bid / per_group;

@@ -174,6 +174,30 @@ struct GemmArgs {
   bool overwrite;              // EPI_ACCUM only: store the product instead of adding it
 };
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
+
+// One product of a grouped launch: out[M, N] (fp32, overwritten) =
+// sum over k < K of A[k, m] B[k, n], both operands bf16 with the reduction
+// index as their row index (A[k * lda + m], B[k * ldb + n]) -- the shape of
+// every weight gradient (Xᵀ · dY).  K is shared by the group and given at run
+// time; tiles_m, tiles_n, tile0 and vec_out are filled in by the planner.
+struct GemmGroupEntry {
+  const void *A; const void *B; float *out;
+  int lda, ldb, ldo;
+  int M, N;
+  int tiles_m, tiles_n, tile0, vec_out;
+};
+struct GemmGroup {
+  GemmGroupEntry *table = nullptr;   // device copy of the entries
+  uint16_t *map = nullptr;           // device: workgroup -> entry (0xffff: padding)
+  int n = 0, tiles = 0, grid = 0;
+  double mn2 = 0;                    // sum of 2 M N (FLOPs per unit of K)
+};
+// Plan a group (entries are copied; the device tables come from the arena
+// and stay valid as long as it does).  Every entry must satisfy the bf16
+// kernel's layout rules for K up to k_max.
+int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max, GemmGroup *out);
+// Run every product of the group in one launch with reduction length K.
+int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K);
 // bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g);
 bool tt_gemm_bf16_ok(const GemmArgs &g);
