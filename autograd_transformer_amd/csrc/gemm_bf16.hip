@@ -769,8 +769,19 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
 // and one reduction length; each workgroup owns one output tile of one
 // product.  Run as one launch, the 48 weight gradients of a 12-layer model
 // and the token-table gradient fill the machine without splitting K.
+// Tile of the grouped launch (BM, BN, BK, waves along M, along N, stages);
+// measured inside the GPT-2 124M step against 256x128 BK 32/64 with 2-3
+// stages, 256x256 and 128x256.
+#ifndef TT_GROUP_TILE
+#define TT_GROUP_TILE 256, 128, 32, 4, 2, 2
+#endif
 namespace {
-constexpr int GBM = 256, GBN = 128, GBK = 32;
+template <int BM, int BN, int BKV, int WM, int WN, int NS>
+struct GroupTile {
+  static constexpr int bm = BM, bn = BN, bk = BKV, wm = WM, wn = WN, ns = NS;
+};
+using GT = GroupTile<TT_GROUP_TILE>;
+constexpr int GBM = GT::bm, GBN = GT::bn, GBK = GT::bk;
 }
 
 int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max,
@@ -830,9 +841,12 @@ int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K) {
   p.raster_n = 0;
   p.group = g.table;
   p.group_map = g.map;
-  tt_prof_scope prof(ctx, "gemm_bf16_v3_kernel<256, 128, 32, 4, 2, 2, false, false, true>",
-                     g.mn2 * K, 0.0);
-  hipLaunchKernelGGL((gemm_bf16_v3_kernel<GBM, GBN, GBK, 4, 2, 2, false, false, true>),
-                     dim3(g.grid), dim3(512), 0, ctx->stream, p);
+  static char name[96];
+  if (!name[0])
+    snprintf(name, sizeof name, "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, false, false, true>",
+             GT::bm, GT::bn, GT::bk, GT::wm, GT::wn, GT::ns);
+  tt_prof_scope prof(ctx, name, g.mn2 * K, 0.0);
+  hipLaunchKernelGGL((gemm_bf16_v3_kernel<GBM, GBN, GBK, GT::wm, GT::wn, GT::ns, false, false, true>),
+                     dim3(g.grid), dim3(64 * GT::wm * GT::wn), 0, ctx->stream, p);
   return tt_check_launch(ctx, "gemm_group");
 }

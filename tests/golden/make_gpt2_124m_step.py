@@ -28,11 +28,12 @@ OUT = os.path.join(HERE, "gpt2_124m_step_b1_t1024_bf16.json")
 SAMPLES = 64
 
 
-def main():
+def write(cfg, shape, out, producer, about=None):
+    """One bf16 training step of `cfg` (weights seed 3, one 1024-token
+    sequence, seed 3) through the oracle; sampled values written to `out`."""
     t0 = time.time()
-    cfg = og.GPTConfig()
-    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(syn.GPT2_124M, seed=3).items()}
-    tok, tgt = syn.gpt2_tokens(1, 1024, seed=3)
+    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=3).items()}
+    tok, tgt = syn.gpt2_tokens(1, cfg.block_size, seed=3)
     zeros = {k: np.zeros_like(v) for k, v in p.items()}
     hp = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1)
     loss, grads, new_p, _, _ = og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16", **hp)
@@ -48,17 +49,22 @@ def main():
             w_new=[float(v) for v in new_p[name].reshape(-1)[idx]],
         )
     doc = dict(
-        about=__doc__.strip().splitlines()[0],
-        produced_by="tests/golden/make_gpt2_124m_step.py (CPU oracle, float64)",
-        workload=dict(n_layer=12, n_embd=768, n_head=12, vocab=50257, block_size=1024,
-                      B=1, T=1024, param_seed=3, token_seed=3, mode="bf16", t=1, **hp),
+        about=about or __doc__.strip().splitlines()[0],
+        produced_by=f"{producer} (CPU oracle, float64)",
+        workload=dict(n_layer=cfg.n_layer, n_embd=cfg.n_embd, n_head=cfg.n_head,
+                      vocab=cfg.vocab, block_size=cfg.block_size,
+                      B=1, T=cfg.block_size, param_seed=3, token_seed=3, mode="bf16", t=1, **hp),
         loss=float(loss),
         tensors=tensors,
         oracle_seconds=round(time.time() - t0, 1),
     )
-    with open(OUT, "w") as f:
+    with open(out, "w") as f:
         json.dump(doc, f, indent=0)
-    print(f"wrote {OUT}: loss {loss:.6f} in {time.time() - t0:.0f}s")
+    print(f"wrote {out}: loss {loss:.6f} in {time.time() - t0:.0f}s")
+
+
+def main():
+    write(og.GPTConfig(), syn.GPT2_124M, OUT, "tests/golden/make_gpt2_124m_step.py")
 
 
 if __name__ == "__main__":

@@ -336,6 +336,30 @@ def test_lmhead_ce(ctx, mode, NCV):
     assert rel_l2(host(dw) - dw0, dw_ref) <= tol(mode)
 
 
+def test_lmhead_ce_full_size_against_oracle_samples(ctx):
+    """hidden [8192, 768] x W_emb [50257, 768] in bf16: loss, the norms of
+    dHidden and dW_emb and 256 sampled entries of each against the values the
+    oracle wrote (tests/golden/make_lmhead_ce_full.py)."""
+    import json
+    import os
+    from tests.conftest import GOLDEN
+    with open(os.path.join(GOLDEN, "lmhead_ce_n8192_c768_v50257_bf16.json")) as f:
+        ref = json.load(f)
+    w = ref["workload"]
+    N, C, V = w["N"], w["C"], w["V"]
+    d = syn.lmhead_inputs(seed=w["seed"], N=N, C=C, V=V)
+    loss, dh, dw = empty((1,)), empty((N, C)), zeros((V, C))
+    tt.tt_lmhead_ce_fwdbwd(ctx, "bf16", N, C, V, dev(d["h"], "bf16"), dev(d["wte"], "bf16"),
+                           dev(d["targets"], "i32"), loss, dh, dw)
+    sync()
+    assert abs(host(loss)[0] - ref["loss"]) / ref["loss"] <= 2e-2
+    for name, got in (("dh", host(dh)), ("dwte", host(dw))):
+        r = ref["tensors"][name]
+        flat = got.reshape(-1)
+        assert abs(np.linalg.norm(flat) - r["norm"]) / r["norm"] <= 2e-2, name
+        assert rel_l2(flat[np.array(r["idx"])], np.array(r["val"])) <= 2e-2, name
+
+
 # ------------------------------------------------------------ error paths
 
 def test_errors_are_reported_not_raised_by_kernels(ctx):
