@@ -33,7 +33,7 @@ from .bf16 import round_bf16
 from .ops import (
     linear_fwd, linear_bwd, layernorm_fwd, layernorm_bwd, gelu_fwd, gelu_grad,
     attention_fwd, attention_bwd, lmhead_ce_fwdbwd, cross_entropy_fwdbwd,
-    embed_fwd, embed_bwd, adamw_update, sgd_update,
+    embed_fwd, embed_bwd, adamw_update, sgd_update, argmax_rows,
 )
 
 
@@ -206,6 +206,42 @@ def model_fwd_bwd(params, tokens, targets, cfg: GPTConfig, mode="f32"):
         grads["wte"] += dwte_e
         grads["wpe"] += dwpe
     return loss, grads
+
+
+def model_logits(params, tokens, cfg: GPTConfig, mode="f32"):
+    """Forward only: the tied head's logits [B, T, V] at every position, stored
+    in the mode's dtype -- the forward of the training step (tinytorch page
+    section 3 items 6-7) without the loss."""
+    S = _store_fn(mode)
+    tokens = np.asarray(tokens, np.int64)
+    B, T = tokens.shape
+    V = cfg.vocab
+    wte = np.asarray(params["wte"], np.float64)
+    wte_head = S(wte[:V])
+    out = np.empty((B, T, V))
+    for b in range(B):
+        x = embed_fwd(tokens[b:b + 1], wte, params["wpe"])
+        for l in range(cfg.n_layer):
+            x, _ = block_fwd(x, _layer_w(params, l), cfg.n_head, mode, cfg.ln_eps)
+        f, _, _ = layernorm_fwd(x, params["lnf_g"], params["lnf_b"], cfg.ln_eps)
+        out[b] = S(np.matmul(S(f)[0], wte_head.T))
+    return out
+
+
+def greedy_generate(params, prompt, n_new, cfg: GPTConfig, mode="f32"):
+    """Greedy generation by its definition (the Forge page's inference loop
+    picks the most likely next token; the pages' missing KV cache is only a way
+    to compute the same thing faster): every new token is the argmax (lowest
+    index on ties) of the last position's logits of the whole sequence so far,
+    recomputed from scratch.  Returns (tokens [B, T0 + n_new], the logits of
+    each step [n_new, B, V])."""
+    seq = np.asarray(prompt, np.int64)
+    steps = []
+    for _ in range(n_new):
+        z = model_logits(params, seq, cfg, mode)[:, -1, :]
+        steps.append(z)
+        seq = np.concatenate([seq, argmax_rows(z)[:, None]], axis=1)
+    return seq, np.stack(steps)
 
 
 def train_step(params, m, v, t, tokens, targets, cfg: GPTConfig, mode="f32",

@@ -185,7 +185,9 @@ def lmhead_ce_fwdbwd(h, wte, targets, store_logits=_ident, store_dlogits=_ident,
 
 
 def argmax_rows(z):
-    """Index of the row maximum, lowest index on ties (greedy decoding)."""
+    """Index of the row maximum, lowest index on ties (greedy decoding); a row
+    holding NaN gives its first NaN (NumPy's rule: NaN ranks above every
+    number)."""
     return np.argmax(np.asarray(z), axis=-1).astype(np.int64)
 
 

@@ -49,6 +49,12 @@ MUTANTS = {
     "gelu_on_rounded_preact_swapped": ("gpt2.py", "dh = S(dg * gelu_grad(c[\"h\"]))",
                                        "dh = S(dg * gelu_grad(c[\"g\"]))"),
     "bf16_round_toward_zero": ("bf16.py", "u = u + np.uint64((1 << 44) - 1) + lsb", "u = u"),
+    "argmax_highest_index_on_ties": ("ops.py",
+                                     "return np.argmax(np.asarray(z), axis=-1).astype(np.int64)",
+                                     "return (np.asarray(z).shape[-1] - 1 - np.argmax(np.asarray(z)[..., ::-1], axis=-1)).astype(np.int64)"),
+    "greedy_takes_first_position": ("gpt2.py",
+                                    "z = model_logits(params, seq, cfg, mode)[:, -1, :]",
+                                    "z = model_logits(params, seq, cfg, mode)[:, 0, :]"),
 }
 
 

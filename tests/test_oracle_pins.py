@@ -362,3 +362,77 @@ def test_bf16_mode_is_close_to_f32_mode():
     assert abs(l32 - l16) / l32 < 1e-2
     for k in g32:
         assert rel_l2(g16[k], g32[k]) < 5e-2, k
+
+
+# ------------------------------------------------------------ greedy decoding
+
+def test_argmax_lowest_index_on_ties_and_first_nan():
+    z = np.array([[1.0, 3.0, 3.0, 2.0],
+                  [2.0, 2.0, 2.0, 2.0],
+                  [-np.inf, -np.inf, -np.inf, -np.inf],
+                  [0.0, np.nan, 5.0, np.nan],
+                  [-1.0, -0.5, -0.5, -7.0]])
+    assert oracle.argmax_rows(z).tolist() == [1, 0, 0, 1, 1]
+
+
+def _tiny_cfg():
+    return og.GPTConfig(n_layer=2, n_embd=8, n_head=2, vocab=13, block_size=8)
+
+
+def _tiny_params(cfg, seed=7):
+    rng = np.random.default_rng(seed)
+    p = {}
+    for name, shape in og.param_shapes(cfg):
+        std = 0.3 if name.split(".")[-1] in ("ln1_g", "ln2_g") or name == "lnf_g" else 0.5
+        base = 1.0 if name.endswith("_g") else 0.0
+        p[name] = base + std * rng.standard_normal(shape)
+    return p
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_logits_of_a_prefix_do_not_depend_on_later_tokens(mode):
+    """Causality: the logits of position t from the prefix 0..t equal the
+    logits of position t in the forward over the whole sequence, which is what
+    lets a decoder reuse cached keys and values."""
+    cfg = _tiny_cfg()
+    p = _tiny_params(cfg)
+    tok = np.random.default_rng(3).integers(0, cfg.vocab, size=(2, 7))
+    full = og.model_logits(p, tok, cfg, mode)
+    for t in range(7):
+        pre = og.model_logits(p, tok[:, :t + 1], cfg, mode)
+        assert np.allclose(pre[:, t], full[:, t], rtol=1e-12, atol=1e-12), t
+    # and a later token does change a later position
+    tok2 = tok.copy()
+    tok2[:, 3] = (tok2[:, 3] + 1) % cfg.vocab
+    assert not np.allclose(og.model_logits(p, tok2, cfg, mode)[:, 5], full[:, 5])
+
+
+def test_greedy_copy_model_closed_form():
+    """Every block zero, token table 4 * one-hot rows, no position table: the
+    residual stream is wte[tok], so the logits are closed form and the argmax
+    is the current token -- greedy decoding repeats the prompt's last token."""
+    C, V = 16, 13
+    cfg = og.GPTConfig(n_layer=2, n_embd=C, n_head=2, vocab=V, block_size=8)
+    p = {name: np.zeros(shape) for name, shape in og.param_shapes(cfg)}
+    for name in p:
+        if name.endswith("_g"):
+            p[name][:] = 1.0
+    p["wte"][:V, :V] = 4.0 * np.eye(V)
+    prompt = np.array([[3, 9, 7], [0, 12, 5]])
+    seq, steps = og.greedy_generate(p, prompt, 4, cfg, "f32")
+    assert seq[:, 3:].tolist() == [[7] * 4, [5] * 4]
+    sd = math.sqrt(16.0 / C * (1.0 - 1.0 / C) + 1e-5)
+    for b, v in enumerate([7, 5]):
+        want = 4.0 * (4.0 * (np.arange(V) == v) - 4.0 / C) / sd
+        assert np.allclose(steps[0, b], want, rtol=1e-12, atol=1e-12)
+
+
+def test_greedy_tokens_are_argmaxes_of_the_full_forward():
+    cfg = _tiny_cfg()
+    p = _tiny_params(cfg, seed=11)
+    prompt = np.random.default_rng(5).integers(0, cfg.vocab, size=(3, 2))
+    seq, steps = og.greedy_generate(p, prompt, 5, cfg, "f32")
+    z = og.model_logits(p, seq, cfg, "f32")
+    for j in range(5):
+        assert np.array_equal(seq[:, 2 + j], np.argmax(z[:, 1 + j], axis=-1))
+        assert np.allclose(steps[j], z[:, 1 + j], rtol=1e-12, atol=1e-12)
