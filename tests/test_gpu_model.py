@@ -7,7 +7,9 @@
   one sequence against sampled values the oracle wrote (tests/golden), and
   at B=8 — the configuration the benchmark times — through the batch
   property: the B=8 loss and gradients equal the mean over the eight
-  sequences run one at a time.
+  sequences run one at a time;
+* the same two checks for the GPT-2 350M step (24 layers, C=1024, 16 heads)
+  at its batch of 16.
 """
 
 import json
@@ -167,9 +169,10 @@ def gpt2_124m():
     ctx.close()
 
 
-def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
-    ctx, model, _ = gpt2_124m
-    with open(os.path.join(GOLDEN, "gpt2_124m_step_b1_t1024_bf16.json")) as f:
+def _one_sequence_against_samples(ctx, model, shape, golden):
+    """One 1024-token sequence (seed 3) through tt_model_fwd_bwd and AdamW,
+    against the sampled oracle values in tests/golden/<golden>."""
+    with open(os.path.join(GOLDEN, golden)) as f:
         ref = json.load(f)
     tok, tgt = syn.gpt2_tokens(1, 1024, seed=3)
     loss = empty((1,))
@@ -177,7 +180,7 @@ def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
     sync()
     assert abs(host(loss)[0] - ref["loss"]) / ref["loss"] <= 2e-2
     g_all, norm_err, samp_err = {}, {}, {}
-    C = 768
+    C = shape.n_embd
     for name, r in ref["tensors"].items():
         g = host(model.tensor(name, "g")).reshape(-1)
         g_all[name] = g
@@ -200,7 +203,7 @@ def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
     sync()
     w_err = {}
     lr, wd = ref["workload"]["lr"], ref["workload"]["wd"]
-    params = syn.gpt2_params(syn.GPT2_124M, seed=3)
+    params = syn.gpt2_params(shape, seed=3)
     for name, r in ref["tensors"].items():
         idx = np.array(r["idx"])
         w = host(model.tensor(name, "w")).reshape(-1)[idx]
@@ -214,33 +217,65 @@ def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
           f"{max(norm_err.values()):.2e}; max sampled-grad err {max(samp_err.values()):.2e}")
 
 
-def test_gpt2_124m_batch_of_8_is_mean_of_sequences(gpt2_124m):
-    """At B=8, T=1024 (the benchmarked step) the loss and every gradient are the
-    mean of the eight single-sequence results — a property of the mean loss
-    that holds at any size."""
-    ctx, model, params = gpt2_124m
+def test_gpt2_124m_one_sequence_against_oracle_samples(gpt2_124m):
+    ctx, model, _ = gpt2_124m
+    _one_sequence_against_samples(ctx, model, syn.GPT2_124M, "gpt2_124m_step_b1_t1024_bf16.json")
+
+
+def _batch_is_mean_of_sequences(ctx, model, params, B, C, seed):
+    """The loss and every gradient of a batch of B sequences equal the mean of
+    the B single-sequence results -- a property of the mean loss that holds
+    at any size."""
     model.load(params)
-    tok, tgt = syn.gpt2_tokens(8, 1024, seed=41)
+    tok, tgt = syn.gpt2_tokens(B, 1024, seed=seed)
     loss = empty((1,))
-    tt.tt_model_fwd_bwd(ctx, model, 8, 1024, dev(tok, "i32"), dev(tgt, "i32"), loss)
+    tt.tt_model_fwd_bwd(ctx, model, B, 1024, dev(tok, "i32"), dev(tgt, "i32"), loss)
     sync()
-    l8 = host(loss)[0]
-    g8 = {k: host(model.tensor(k, "g")) for k in model.names}
-    acc = {k: np.zeros_like(v) for k, v in g8.items()}
+    lB = host(loss)[0]
+    gB = {k: host(model.tensor(k, "g")) for k in model.names}
+    acc = {k: np.zeros_like(v) for k, v in gB.items()}
     lsum = 0.0
-    for b in range(8):
+    for b in range(B):
         tt.tt_model_fwd_bwd(ctx, model, 1, 1024, dev(tok[b:b + 1], "i32"),
                             dev(tgt[b:b + 1], "i32"), loss)
         sync()
         lsum += host(loss)[0]
         for k in acc:
             acc[k] += host(model.tensor(k, "g"))
-    assert abs(l8 - lsum / 8) / l8 <= 1e-5
+    assert abs(lB - lsum / B) / lB <= 1e-5
     # Both sides store activation gradients in bf16; a float32 reordering
-    # (the weight-gradient reductions run over 8192 vs 1024 tokens) flips a
+    # (the weight-gradient reductions run over B*1024 vs 1024 tokens) flips a
     # few bf16 roundings and after a few layers the two runs differ by bf16
     # rounding noise (~2^-9), so the bf16 bar applies.
-    errs = {k: rel_l2(g8[k], acc[k] / 8) for k in acc}
+    errs = {k: rel_l2(gB[k], acc[k] / B) for k in acc}
     bad = {k: e for k, e in errs.items() if not e <= 2e-2}
     assert not bad, bad
-    assert abs(l8 - (np.log(50257) + 0.02 ** 2 * 768 / 2)) < 0.1
+    assert abs(lB - (np.log(50257) + 0.02 ** 2 * C / 2)) < 0.1
+
+
+def test_gpt2_124m_batch_of_8_is_mean_of_sequences(gpt2_124m):
+    """At B=8, T=1024 (the benchmarked step)."""
+    ctx, model, params = gpt2_124m
+    _batch_is_mean_of_sequences(ctx, model, params, 8, 768, seed=41)
+
+
+# GPT-2 350M (24 layers, C=1024, 16 heads, MLP 4096) at its batch of 16.
+
+@pytest.fixture(scope="module")
+def gpt2_350m():
+    params = syn.gpt2_params(syn.GPT2_350M, seed=3)
+    ctx = tt.Context(arena_bytes=48 << 30)
+    model = make_model(ctx, syn.GPT2_350M, 16, 1024, "bf16", params, V_pad=50304)
+    yield ctx, model, params
+    model.close()
+    ctx.close()
+
+
+def test_gpt2_350m_one_sequence_against_oracle_samples(gpt2_350m):
+    ctx, model, _ = gpt2_350m
+    _one_sequence_against_samples(ctx, model, syn.GPT2_350M, "gpt2_350m_step_b1_t1024_bf16.json")
+
+
+def test_gpt2_350m_batch_of_16_is_mean_of_sequences(gpt2_350m):
+    ctx, model, params = gpt2_350m
+    _batch_is_mean_of_sequences(ctx, model, params, 16, 1024, seed=43)
