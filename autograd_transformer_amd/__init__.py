@@ -340,3 +340,36 @@ def tt_model_fwd_bwd(ctx, model, B, T, tok, targets, loss):
 
 def tt_model_adamw(ctx, model, lr, beta1, beta2, eps, wd, t):
     return ctx.check(lib().tt_model_adamw(ctx.handle, model.handle, lr, beta1, beta2, eps, wd, t))
+
+
+# ------------------------------------------------------------------ inference
+
+def tt_argmax(ctx, mode, N, V, ld, logits, out):
+    """out[n] = argmax of logits[n, :V] (row stride ld), lowest index on ties."""
+    return ctx.check(lib().tt_argmax(ctx.handle, _mode(mode), N, V, ld, _ptr(logits), _ptr(out)))
+
+
+class KVCache:
+    """Key/value cache of a model for up to B_max sequences (tt_kvcache)."""
+
+    def __init__(self, ctx, model, B_max):
+        self.ctx = ctx
+        h = _C.c_void_p()
+        ctx.check(lib().tt_kvcache_create(ctx.handle, model.handle, B_max, _C.byref(h)))
+        self.handle = h
+        self.B_max = B_max
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().tt_kvcache_destroy(self.handle)
+            self.handle = None
+
+
+def tt_model_prefill(ctx, model, cache, B, T, tok, logits, next_tok):
+    return ctx.check(lib().tt_model_prefill(ctx.handle, model.handle, cache.handle, B, T,
+                                            _ptr(tok), _ptr(logits), _ptr(next_tok)))
+
+
+def tt_model_decode(ctx, model, cache, B, pos, tok, logits, next_tok):
+    return ctx.check(lib().tt_model_decode(ctx.handle, model.handle, cache.handle, B, pos,
+                                           _ptr(tok), _ptr(logits), _ptr(next_tok)))

@@ -90,6 +90,11 @@ SIGS = {
     "tt_train_step": (i32, [vp, vp, i32, i32, vp, vp, f32, f32, f32, f32, f32, i32, vp, vp]),
     "tt_model_fwd_bwd": (i32, [vp, vp, i32, i32, vp, vp, vp]),
     "tt_model_adamw": (i32, [vp, vp, f32, f32, f32, f32, f32, i32]),
+    "tt_argmax": (i32, [vp, i32, i32, i32, i32, vp, vp]),
+    "tt_kvcache_create": (i32, [vp, vp, i32, P(vp)]),
+    "tt_kvcache_destroy": (None, [vp]),
+    "tt_model_prefill": (i32, [vp, vp, vp, i32, i32, vp, vp, vp]),
+    "tt_model_decode": (i32, [vp, vp, vp, i32, i32, vp, vp, vp]),
 }
 
 _lib = None

@@ -816,3 +816,174 @@ extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int3
   }
   return tt_model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t);
 }
+
+// ------------------------------------------------------------ inference
+// Greedy generation with a key/value cache (the Forge page's inference loop
+// with the cache its sections "性能瓶颈与未来路线图" / "瓶颈分析是否合理"
+// call for): a prefill runs the training forward over the prompt and keeps
+// every layer's keys and values; each decode step then pushes one token per
+// sequence through the same ops on single rows and attends over the cache.
+
+struct tt_kvcache {
+  uint32_t magic;
+  tt_ctx *ctx;
+  tt_model *md;
+  int B_max, T_max;
+  std::vector<void *> kv;   // per layer [B_max, T_max, 2C], mode dtype
+  // decode step rows
+  float *x = nullptr, *x1 = nullptr, *mean = nullptr, *rstd = nullptr;
+  void *ln = nullptr, *qkv = nullptr, *att = nullptr, *h = nullptr, *g = nullptr;
+  void *logits = nullptr;   // [B_max, md->ld]
+};
+
+extern "C" int tt_kvcache_create(tt_ctx *ctx, tt_model *md, int B_max, tt_kvcache **out) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, out != nullptr, "kvcache_create: out is NULL");
+  *out = nullptr;
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "kvcache_create: bad model handle");
+  TT_REQUIRE(ctx, md->ctx == ctx, "kvcache_create: model belongs to another context");
+  const tt_model_cfg &c = md->cfg;
+  TT_REQUIRE(ctx, B_max > 0 && B_max <= c.B_max, "kvcache_create: B_max must be in [1, %d]",
+             c.B_max);
+  if (c.T_max > 16384)
+    return tt_set_error(ctx, TT_EUNSUPPORTED, "kvcache_create: T_max above 16384");
+  const size_t es = esize(c.mode), C = c.C, F = c.F, B = B_max;
+  tt_kvcache *kc = new tt_kvcache();
+  kc->magic = TT_KV_MAGIC;
+  kc->ctx = ctx;
+  kc->md = md;
+  kc->B_max = B_max;
+  kc->T_max = c.T_max;
+  const size_t save = ctx->offset;
+  void *p;
+  auto alloc = [&](size_t bytes) -> void * {
+    if (rc != TT_OK) return nullptr;
+    rc = tt_arena_alloc(ctx, bytes, &p);
+    return rc == TT_OK ? p : nullptr;
+  };
+  for (int l = 0; l < c.L; ++l) kc->kv.push_back(alloc(B * c.T_max * 2 * C * es));
+  kc->x = (float *)alloc(B * C * 4);
+  kc->x1 = (float *)alloc(B * C * 4);
+  kc->mean = (float *)alloc(B * 4);
+  kc->rstd = (float *)alloc(B * 4);
+  kc->ln = alloc(B * C * es);
+  kc->qkv = alloc(B * 3 * C * es);
+  kc->att = alloc(B * C * es);
+  kc->h = alloc(B * F * es);
+  kc->g = alloc(B * F * es);
+  kc->logits = alloc(B * (size_t)md->ld * es);
+  if (rc != TT_OK) {
+    ctx->offset = save;
+    kc->magic = 0;
+    delete kc;
+    return rc;
+  }
+  *out = kc;
+  return TT_OK;
+}
+
+extern "C" void tt_kvcache_destroy(tt_kvcache *kc) {
+  if (!kc || kc->magic != TT_KV_MAGIC) return;
+  kc->magic = 0;
+  delete kc;
+}
+
+namespace {
+
+int check_kv(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, const void *tok, int32_t *next) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "decode: bad model handle");
+  if (!kc || kc->magic != TT_KV_MAGIC) return tt_set_error(ctx, TT_ESTALE, "decode: stale cache");
+  TT_REQUIRE(ctx, md->ctx == ctx && kc->md == md, "decode: cache, model and context do not match");
+  TT_REQUIRE(ctx, B > 0 && B <= kc->B_max, "decode: B must be in [1, %d]", kc->B_max);
+  TT_REQUIRE(ctx, tok && next, "decode: NULL pointer");
+  return TT_OK;
+}
+
+// Logits of B rows of the final LayerNorm output (row stride ldf elements)
+// against the tied token table, their greedy choice, and (nullable) a copy
+// of the logits as [B, V].
+int logits_and_choice(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, const void *f, int ldf,
+                      void *logits_out, int32_t *next) {
+  const tt_model_cfg &c = md->cfg;
+  const size_t es = esize(c.mode);
+  GemmArgs g = gemm_args();
+  g.A = f; g.lda = ldf; g.a_kmajor = true;
+  g.B = mat(md, P_WTE); g.ldb = c.C; g.b_kmajor = true;
+  g.M = B; g.N = c.V; g.K = c.C;
+  g.epi = EPI_STORE; g.out = kc->logits; g.ldo = md->ld; g.out_bf16 = c.mode == TT_BF16;
+  TT_TRY(tt_gemm(ctx, c.mode, g));
+  TT_TRY(tt_argmax(ctx, c.mode, B, c.V, md->ld, kc->logits, next));
+  if (logits_out) {
+    hipError_t e = hipMemcpy2DAsync(logits_out, (size_t)c.V * es, kc->logits, (size_t)md->ld * es,
+                                    (size_t)c.V * es, B, hipMemcpyDeviceToDevice, ctx->stream);
+    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "decode: logits copy: %s", hipGetErrorString(e));
+  }
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" int tt_model_prefill(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, int T,
+                                const int32_t *tok, void *logits, int32_t *next) {
+  TT_TRY(check_kv(ctx, md, kc, B, tok, next));
+  const tt_model_cfg &c = md->cfg;
+  TT_REQUIRE(ctx, T >= 1 && T <= c.T_max, "prefill: T must be in [1, %d]", c.T_max);
+  const tt_mode mode = c.mode;
+  const int N = B * T, C = c.C;
+  TT_TRY(tt_embed_fwd(ctx, B, T, C, c.V, tok, md->w + md->off[P_WTE], md->w + md->off[P_WPE],
+                      md->xs[0]));
+  tt_block_w w;
+  LayerWT wt;
+  tt_block_g gr;
+  for (int l = 0; l < c.L; ++l) {
+    layer_views(md, l, w, wt, gr);
+    TT_TRY(layer_fwd(ctx, mode, B, T, C, c.NH, c.F, c.ln_eps, w, wt, md->xs[l], md->xs[l + 1],
+                     md->layers[l]));
+    TT_TRY(tt_kv_store(ctx, mode, B, T, C, c.T_max, md->layers[l].qkv, kc->kv[l]));
+  }
+  const int lf = p_lnf_g(md);
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, c.ln_eps, md->xs[c.L], md->w + md->off[lf],
+                               md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
+  // the last position of every sequence: rows b*T + T-1
+  const void *last = (const char *)md->lnf + (size_t)(T - 1) * C * esize(mode);
+  return logits_and_choice(ctx, md, kc, B, last, T * C, logits, next);
+}
+
+extern "C" int tt_model_decode(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, int pos,
+                               const int32_t *tok, void *logits, int32_t *next) {
+  TT_TRY(check_kv(ctx, md, kc, B, tok, next));
+  const tt_model_cfg &c = md->cfg;
+  TT_REQUIRE(ctx, pos >= 0 && pos < c.T_max, "decode: pos must be in [0, %d)", c.T_max);
+  const tt_mode mode = c.mode;
+  const bool lp = mode == TT_BF16;
+  const int C = c.C, F = c.F;
+  // x = wte[tok] + wpe[pos]
+  TT_TRY(tt_embed_fwd(ctx, B, 1, C, c.V, tok, md->w + md->off[P_WTE],
+                      md->w + md->off[P_WPE] + (size_t)pos * C, kc->x));
+  tt_block_w w;
+  LayerWT wt;
+  tt_block_g gr;
+  for (int l = 0; l < c.L; ++l) {
+    layer_views(md, l, w, wt, gr);
+    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, w.ln1_g, w.ln1_b, kc->ln,
+                                 kc->mean, kc->rstd));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, 3 * C, kc->ln, C, w.w_qkv, wt.w_qkv, w.b_qkv,
+                           EPI_STORE, kc->qkv, 3 * C, lp, nullptr, 0, nullptr, 0));
+    TT_TRY(tt_attn_decode(ctx, mode, B, c.NH, pos, c.T_max, kc->qkv, kc->kv[l], kc->att));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, C, kc->att, C, w.w_proj, wt.w_proj, w.b_proj,
+                           EPI_RESID, kc->x1, C, false, kc->x, C, nullptr, 0));
+    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x1, w.ln2_g, w.ln2_b, kc->ln,
+                                 kc->mean, kc->rstd));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, F, kc->ln, C, w.w_fc, wt.w_fc, w.b_fc, EPI_GELU,
+                           kc->g, F, lp, nullptr, 0, kc->h, F));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, F, C, kc->g, F, w.w_fcp, wt.w_fcp, w.b_fcp, EPI_RESID,
+                           kc->x, C, false, kc->x1, C, nullptr, 0));
+  }
+  const int lf = p_lnf_g(md);
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, md->w + md->off[lf],
+                               md->w + md->off[lf + 1], kc->ln, kc->mean, kc->rstd));
+  return logits_and_choice(ctx, md, kc, B, kc->ln, C, logits, next);
+}

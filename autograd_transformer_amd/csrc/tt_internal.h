@@ -17,6 +17,7 @@
 #define TT_CTX_MAGIC 0x54544358u    // "TTCX"
 #define TT_MODEL_MAGIC 0x54544d44u  // "TTMD"
 #define TT_SAVED_MAGIC 0x54545342u  // "TTSB"
+#define TT_KV_MAGIC 0x54544b56u     // "TTKV"
 
 // One timed kernel launch (profiling mode): HIP events on the context's
 // stream around the launch, tagged with the kernel name and its algorithmic
@@ -224,6 +225,13 @@ struct tt_tdesc {
 };
 // d_dev: device copy of the descriptor table, ordered by tile0.
 int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles, double elems);
+// Inference (decode.hip): copy a prefill's keys and values (qkv columns
+// C..3C of rows b*T + t) into the cache [B_max, T_max, 2C]; attention of one
+// new position pos over the cache, appending its key and value first.
+int tt_kv_store(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int T_max, const void *qkv,
+                void *kv);
+int tt_attn_decode(tt_ctx *ctx, tt_mode mode, int B, int NH, int pos, int T_max, const void *qkv,
+                   void *kv, void *att);
 int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      void *out, float *lse);
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,

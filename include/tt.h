@@ -314,6 +314,44 @@ int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *
 int tt_model_adamw(tt_ctx *ctx, tt_model *model, float lr, float beta1, float beta2,
                    float eps, float wd, int t);
 
+/* ---------------------------------------------------------------- inference
+ * Greedy generation with a key/value cache.  The Forge page's GPT-2 inference
+ * picks the most likely next token and names the missing KV cache as its main
+ * cost (sections "性能瓶颈与未来路线图", "瓶颈分析是否合理"): with causal
+ * attention the keys and values of earlier positions do not change, so they
+ * are kept and each new token computes only its own.  The result is the same
+ * as recomputing the whole sequence (up to rounding order). */
+
+/* Greedy choice: out[n] = index of the largest of logits[n, 0..V-1] (row
+ * stride ld >= V, mode dtype), the lowest index on ties and the first NaN if a
+ * row holds one.  out [N] int32 (written).  Exact: no rounding is involved. */
+int tt_argmax(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, const void *logits,
+              int32_t *out);
+
+typedef struct tt_kvcache tt_kvcache;
+/* A cache for up to B_max sequences of the model's T_max positions: per
+ * layer the keys and values of every processed position ([B_max, T_max, 2C],
+ * mode dtype) and the decode step's row buffers, carved from the context's
+ * arena (valid until it is reset below them or destroyed).  B_max <= the
+ * model's B_max. */
+int tt_kvcache_create(tt_ctx *ctx, tt_model *model, int B_max, tt_kvcache **out);
+void tt_kvcache_destroy(tt_kvcache *cache); /* NULL-safe */
+/* Prefill: the forward of the training step over tok [B,T] int32 (positions
+ * 0..T-1), keeping every layer's keys and values in the cache; then the
+ * logits of position T-1 and their greedy choice.  logits (nullable) [B,V]
+ * mode dtype (written); next [B] int32 (written).  Uses the model's
+ * activation buffers (a later training step overwrites them, not the cache).
+ * B <= cache B_max, 1 <= T <= T_max. */
+int tt_model_prefill(tt_ctx *ctx, tt_model *model, tt_kvcache *cache, int B, int T,
+                     const int32_t *tok, void *logits, int32_t *next);
+/* Decode one position: tok [B] int32 are the tokens at position pos of the B
+ * sequences, whose positions 0..pos-1 are in the cache (pos = the prefill's
+ * T for the first call, +1 per call).  Appends position pos to the cache and
+ * writes its logits (nullable, [B,V] mode dtype) and greedy choice next [B].
+ * pos < T_max. */
+int tt_model_decode(tt_ctx *ctx, tt_model *model, tt_kvcache *cache, int B, int pos,
+                    const int32_t *tok, void *logits, int32_t *next);
+
 #ifdef __cplusplus
 }
 #endif

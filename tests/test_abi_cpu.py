@@ -59,6 +59,7 @@ def test_null_and_stale_handles_without_gpu(lib):
     lib.tt_ctx_destroy(None)
     lib.tt_model_destroy(None)
     lib.tt_block_saved_destroy(None)
+    lib.tt_kvcache_destroy(None)
     assert lib.tt_ctx_sync(None) == -1
     fake = ctypes.create_string_buffer(512)   # zeroed memory: wrong magic word
     fp = ctypes.cast(fake, ctypes.c_void_p)
@@ -66,4 +67,6 @@ def test_null_and_stale_handles_without_gpu(lib):
     assert lib.tt_ctx_mark(fp) == -4
     assert lib.tt_linear_fwd(fp, 0, 1, 1, 1, None, None, None, None, 0, None, None) == -4
     assert lib.tt_model_refresh_shadow(fp) == -4
+    assert lib.tt_model_decode(fp, fp, fp, 1, 0, fp, None, fp) == -4
+    assert lib.tt_argmax(fp, 0, 1, 1, 1, fp, fp) == -4
     assert lib.tt_ctx_create(0, None, 1 << 20, None, None) == -1
