@@ -834,6 +834,13 @@ struct tt_kvcache {
   float *x = nullptr, *x1 = nullptr, *mean = nullptr, *rstd = nullptr;
   void *ln = nullptr, *qkv = nullptr, *att = nullptr, *h = nullptr, *g = nullptr;
   void *logits = nullptr;   // [B_max, md->ld]
+  float *part = nullptr;    // attention partials [B_max * NH * TT_DECODE_MAX_SPLITS * 66]
+  // The step reads its position and tokens from, and writes its choice to,
+  // device memory, so one captured graph of the step serves every position.
+  int32_t *pos_dev = nullptr, *tok_dev = nullptr, *next_dev = nullptr;
+  hipStream_t cap = nullptr;        // capture only (nothing runs on it)
+  hipGraphExec_t graph = nullptr;   // the captured step for graph_B sequences
+  int graph_B = 0;
 };
 
 extern "C" int tt_kvcache_create(tt_ctx *ctx, tt_model *md, int B_max, tt_kvcache **out) {
@@ -873,6 +880,14 @@ extern "C" int tt_kvcache_create(tt_ctx *ctx, tt_model *md, int B_max, tt_kvcach
   kc->h = alloc(B * F * es);
   kc->g = alloc(B * F * es);
   kc->logits = alloc(B * (size_t)md->ld * es);
+  kc->part = (float *)alloc(B * c.NH * (size_t)TT_DECODE_MAX_SPLITS * 66 * 4);
+  kc->pos_dev = (int32_t *)alloc(4);
+  kc->tok_dev = (int32_t *)alloc(B * 4);
+  kc->next_dev = (int32_t *)alloc(B * 4);
+  if (rc == TT_OK && hipStreamCreateWithFlags(&kc->cap, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipGetLastError();
+    rc = tt_set_error(ctx, TT_EHIP, "kvcache_create: stream creation failed");
+  }
   if (rc != TT_OK) {
     ctx->offset = save;
     kc->magic = 0;
@@ -886,6 +901,9 @@ extern "C" int tt_kvcache_create(tt_ctx *ctx, tt_model *md, int B_max, tt_kvcach
 extern "C" void tt_kvcache_destroy(tt_kvcache *kc) {
   if (!kc || kc->magic != TT_KV_MAGIC) return;
   kc->magic = 0;
+  (void)hipStreamSynchronize(kc->ctx->stream);
+  if (kc->graph) (void)hipGraphExecDestroy(kc->graph);
+  if (kc->cap) (void)hipStreamDestroy(kc->cap);
   delete kc;
 }
 
@@ -903,25 +921,98 @@ int check_kv(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, const void *tok, 
 }
 
 // Logits of B rows of the final LayerNorm output (row stride ldf elements)
-// against the tied token table, their greedy choice, and (nullable) a copy
-// of the logits as [B, V].
+// against the tied token table into the cache's [B, ld] buffer, and their
+// greedy choice.
 int logits_and_choice(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, const void *f, int ldf,
-                      void *logits_out, int32_t *next) {
+                      int32_t *next) {
   const tt_model_cfg &c = md->cfg;
-  const size_t es = esize(c.mode);
   GemmArgs g = gemm_args();
   g.A = f; g.lda = ldf; g.a_kmajor = true;
   g.B = mat(md, P_WTE); g.ldb = c.C; g.b_kmajor = true;
   g.M = B; g.N = c.V; g.K = c.C;
   g.epi = EPI_STORE; g.out = kc->logits; g.ldo = md->ld; g.out_bf16 = c.mode == TT_BF16;
   TT_TRY(tt_gemm(ctx, c.mode, g));
-  TT_TRY(tt_argmax(ctx, c.mode, B, c.V, md->ld, kc->logits, next));
-  if (logits_out) {
-    hipError_t e = hipMemcpy2DAsync(logits_out, (size_t)c.V * es, kc->logits, (size_t)md->ld * es,
-                                    (size_t)c.V * es, B, hipMemcpyDeviceToDevice, ctx->stream);
-    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "decode: logits copy: %s", hipGetErrorString(e));
-  }
+  return tt_argmax(ctx, c.mode, B, c.V, md->ld, kc->logits, next);
+}
+
+// (nullable) copy of the cache's logits as [B, V].
+int copy_logits(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, void *logits_out) {
+  if (!logits_out) return TT_OK;
+  const tt_model_cfg &c = md->cfg;
+  const size_t es = esize(c.mode);
+  hipError_t e = hipMemcpy2DAsync(logits_out, (size_t)c.V * es, kc->logits, (size_t)md->ld * es,
+                                  (size_t)c.V * es, B, hipMemcpyDeviceToDevice, ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "decode: logits copy: %s", hipGetErrorString(e));
   return TT_OK;
+}
+
+// One decode step on the cache's device-side position and tokens: embedding,
+// every block on B rows with attention over the cache, final LayerNorm,
+// logits and the greedy choice into kc->next_dev.  Only kernel launches with
+// fixed arguments for a given B (capturable).
+int decode_body(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, int pos_hint) {
+  const tt_model_cfg &c = md->cfg;
+  const tt_mode mode = c.mode;
+  const bool lp = mode == TT_BF16;
+  const int C = c.C, F = c.F;
+  const int S = tt_decode_splits(B, c.NH);
+  TT_TRY(tt_embed_decode(ctx, B, C, c.V, kc->tok_dev, kc->pos_dev, md->w + md->off[P_WTE],
+                         md->w + md->off[P_WPE], kc->x));
+  tt_block_w w;
+  LayerWT wt;
+  tt_block_g gr;
+  for (int l = 0; l < c.L; ++l) {
+    layer_views(md, l, w, wt, gr);
+    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, w.ln1_g, w.ln1_b, kc->ln,
+                                 kc->mean, kc->rstd));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, 3 * C, kc->ln, C, w.w_qkv, wt.w_qkv, w.b_qkv,
+                           EPI_STORE, kc->qkv, 3 * C, lp, nullptr, 0, nullptr, 0));
+    TT_TRY(tt_attn_decode(ctx, mode, B, c.NH, kc->pos_dev, pos_hint, c.T_max, kc->qkv, kc->kv[l],
+                          kc->att, kc->part, S));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, C, kc->att, C, w.w_proj, wt.w_proj, w.b_proj,
+                           EPI_RESID, kc->x1, C, false, kc->x, C, nullptr, 0));
+    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x1, w.ln2_g, w.ln2_b, kc->ln,
+                                 kc->mean, kc->rstd));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, F, kc->ln, C, w.w_fc, wt.w_fc, w.b_fc, EPI_GELU,
+                           kc->g, F, lp, nullptr, 0, kc->h, F));
+    TT_TRY(linear_fwd_gemm(ctx, mode, B, F, C, kc->g, F, w.w_fcp, wt.w_fcp, w.b_fcp, EPI_RESID,
+                           kc->x, C, false, kc->x1, C, nullptr, 0));
+  }
+  const int lf = p_lnf_g(md);
+  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, md->w + md->off[lf],
+                               md->w + md->off[lf + 1], kc->ln, kc->mean, kc->rstd));
+  return logits_and_choice(ctx, md, kc, B, kc->ln, C, kc->next_dev);
+}
+
+// Capture decode_body for B sequences into kc->graph (on the cache's own
+// stream: the context's stream may be the null stream, which cannot be
+// captured).  The graph holds kernel launches only.
+int capture_decode(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B) {
+  if (kc->graph) {
+    (void)hipGraphExecDestroy(kc->graph);
+    kc->graph = nullptr;
+    kc->graph_B = 0;
+  }
+  hipError_t e = hipStreamBeginCapture(kc->cap, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "decode capture: %s", hipGetErrorString(e));
+  hipStream_t saved = ctx->stream;
+  ctx->stream = kc->cap;
+  int rc = decode_body(ctx, md, kc, B, 0);
+  ctx->stream = saved;
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(kc->cap, &graph);
+  if (rc == TT_OK && e != hipSuccess)
+    rc = tt_set_error(ctx, TT_EHIP, "decode capture: %s", hipGetErrorString(e));
+  if (rc == TT_OK) {
+    e = hipGraphInstantiate(&kc->graph, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      kc->graph = nullptr;
+      rc = tt_set_error(ctx, TT_EHIP, "decode graph: %s", hipGetErrorString(e));
+    }
+  }
+  if (graph) (void)hipGraphDestroy(graph);
+  if (rc == TT_OK) kc->graph_B = B;
+  return rc;
 }
 
 }  // namespace
@@ -949,7 +1040,8 @@ extern "C" int tt_model_prefill(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B
                                md->w + md->off[lf + 1], md->lnf, md->meanf, md->rstdf));
   // the last position of every sequence: rows b*T + T-1
   const void *last = (const char *)md->lnf + (size_t)(T - 1) * C * esize(mode);
-  return logits_and_choice(ctx, md, kc, B, last, T * C, logits, next);
+  TT_TRY(logits_and_choice(ctx, md, kc, B, last, T * C, next));
+  return copy_logits(ctx, md, kc, B, logits);
 }
 
 extern "C" int tt_model_decode(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, int pos,
@@ -957,33 +1049,15 @@ extern "C" int tt_model_decode(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B,
   TT_TRY(check_kv(ctx, md, kc, B, tok, next));
   const tt_model_cfg &c = md->cfg;
   TT_REQUIRE(ctx, pos >= 0 && pos < c.T_max, "decode: pos must be in [0, %d)", c.T_max);
-  const tt_mode mode = c.mode;
-  const bool lp = mode == TT_BF16;
-  const int C = c.C, F = c.F;
-  // x = wte[tok] + wpe[pos]
-  TT_TRY(tt_embed_fwd(ctx, B, 1, C, c.V, tok, md->w + md->off[P_WTE],
-                      md->w + md->off[P_WPE] + (size_t)pos * C, kc->x));
-  tt_block_w w;
-  LayerWT wt;
-  tt_block_g gr;
-  for (int l = 0; l < c.L; ++l) {
-    layer_views(md, l, w, wt, gr);
-    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, w.ln1_g, w.ln1_b, kc->ln,
-                                 kc->mean, kc->rstd));
-    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, 3 * C, kc->ln, C, w.w_qkv, wt.w_qkv, w.b_qkv,
-                           EPI_STORE, kc->qkv, 3 * C, lp, nullptr, 0, nullptr, 0));
-    TT_TRY(tt_attn_decode(ctx, mode, B, c.NH, pos, c.T_max, kc->qkv, kc->kv[l], kc->att));
-    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, C, kc->att, C, w.w_proj, wt.w_proj, w.b_proj,
-                           EPI_RESID, kc->x1, C, false, kc->x, C, nullptr, 0));
-    TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x1, w.ln2_g, w.ln2_b, kc->ln,
-                                 kc->mean, kc->rstd));
-    TT_TRY(linear_fwd_gemm(ctx, mode, B, C, F, kc->ln, C, w.w_fc, wt.w_fc, w.b_fc, EPI_GELU,
-                           kc->g, F, lp, nullptr, 0, kc->h, F));
-    TT_TRY(linear_fwd_gemm(ctx, mode, B, F, C, kc->g, F, w.w_fcp, wt.w_fcp, w.b_fcp, EPI_RESID,
-                           kc->x, C, false, kc->x1, C, nullptr, 0));
+  TT_TRY(tt_decode_prep(ctx, B, pos, tok, kc->tok_dev, kc->pos_dev));
+  if (ctx->profiling) {
+    // per-kernel timing needs every launch on the context's stream
+    TT_TRY(decode_body(ctx, md, kc, B, pos));
+  } else {
+    if (!kc->graph || kc->graph_B != B) TT_TRY(capture_decode(ctx, md, kc, B));
+    hipError_t e = hipGraphLaunch(kc->graph, ctx->stream);
+    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "decode graph launch: %s", hipGetErrorString(e));
   }
-  const int lf = p_lnf_g(md);
-  TT_TRY(tt_layernorm_fwd_impl(ctx, mode, B, C, c.ln_eps, kc->x, md->w + md->off[lf],
-                               md->w + md->off[lf + 1], kc->ln, kc->mean, kc->rstd));
-  return logits_and_choice(ctx, md, kc, B, kc->ln, C, logits, next);
+  TT_TRY(tt_copy_i32(ctx, B, kc->next_dev, next));
+  return copy_logits(ctx, md, kc, B, logits);
 }

@@ -270,7 +270,7 @@ int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   if (!names[li][0])
     snprintf(names[li], sizeof names[li], "gemm_bf16_kernel<%d, %d, %d, %d, %s, %s>", BM, BN, WM, WN,
              g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
-  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, 0.0);
+  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
 #define TT_L(AK, BKM)                                                                          \
   if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                 \
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM>), grid, dim3(64 * WM * WN), 0, \
@@ -629,7 +629,7 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   if (!names[li][0])
     snprintf(names[li], sizeof names[li], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s>", BM,
              BN, BKV, WM, WN, NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
-  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, 0.0);
+  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
 #define TT_L3(AK, BKM)                                                                          \
   if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                  \
     if constexpr (DOp<BM, BKV, AK>::VALID && DOp<BN, BKV, BKM>::VALID) {                        \
@@ -678,6 +678,78 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ 
   }
 }
 
+// --------------------------------------------------------------------------
+// Skinny products (at most 16 rows, both operands k-major): the single-token
+// decode step, where every weight is read once per step and the product is
+// bound by that read.  One workgroup per 16 output columns; its 4 waves take
+// interleaved 32-wide slices of K, each accumulating the 16 x 16 tile with
+// v_mfma_f32_16x16x32_bf16 straight from global memory (rows past M and k
+// past K read zero through the buffer range checks); the 4 partial tiles
+// are added in LDS and the usual epilogue runs on 4-column groups.
+// --------------------------------------------------------------------------
+constexpr int SK_BATCH = 8;   // MFMA steps whose loads are issued together
+
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmParams p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+  const int m = lr, n = n0 + lr;
+  const bool mok = m < p.M, nok = n < p.N;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nsteps = (p.K + 31) / 32;
+  for (int s0 = wave; s0 < nsteps; s0 += 4 * SK_BATCH) {
+    uint4 fa[SK_BATCH], fb[SK_BATCH];
+#pragma unroll
+    for (int j = 0; j < SK_BATCH; ++j) {
+      const int k = (s0 + 4 * j) * 32 + 8 * lg;
+      const bool kok = s0 + 4 * j < nsteps && k < p.K;
+      const uint32_t oa = (mok && kok) ? (uint32_t)(((size_t)m * p.lda + k) * 2) : OOB;
+      const uint32_t ob = (nok && kok) ? (uint32_t)(((size_t)n * p.ldb + k) * 2) : OOB;
+      fa[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, oa, 0, 0));
+      fb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ob, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < SK_BATCH; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[j]),
+                                                     __builtin_bit_cast(bf16x8_t, fb[j]), acc,
+                                                     0, 0, 0);
+  }
+  __shared__ float part[4][16][17];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][lg * 4 + r][lr] = acc[r];
+  __syncthreads();
+  if (tid >= 64) return;
+  const int row = tid >> 2, cg = (tid & 3) * 4;
+  const int nn = n0 + cg, nv = p.n_valid;
+  if (row >= p.M || nn >= nv) return;
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = (part[0][row][cg + q] + part[1][row][cg + q]) + (part[2][row][cg + q] + part[3][row][cg + q]);
+    if (p.bias && nn + q < nv) v[q] += p.bias[nn + q];
+  }
+  epilogue4(p, row, nn, make_float4(v[0], v[1], v[2], v[3]), nv - nn);
+}
+
+int launch_skinny(tt_ctx *ctx, const GemmArgs &g) {
+  GemmParams p{};
+  p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
+  p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
+  p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
+  p.vec_out = gemm_vec_out(g) ? 1 : 0;
+  p.a_bytes = (uint32_t)gemm_extent_bytes(true, g.M, g.K, g.lda);
+  p.b_bytes = (uint32_t)gemm_extent_bytes(true, g.N, g.K, g.ldb);
+  tt_prof_scope prof(ctx, "gemm_skinny_kernel", 2.0 * g.M * g.N * g.K, gemm_bytes(g));
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((g.N + 15) / 16), dim3(256), 0, ctx->stream, p);
+  return tt_check_launch(ctx, "gemm_skinny");
+}
+
 }  // namespace
 
 // Host guard: the buffer-load path needs every operand extent below the OOB
@@ -714,6 +786,9 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 // least 256 of K per split.
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
+  if (g.M <= 16 && g.a_kmajor && g.b_kmajor && !g.colsum && g.K % 8 == 0 &&
+      (g.epi == EPI_STORE || g.epi == EPI_GELU || g.epi == EPI_RESID))
+    return launch_skinny(ctx, g);
   if (g.epi != EPI_ACCUM) {
     if (g.colsum && !(g.a_kmajor && g.b_kmajor))
       return tt_set_error(ctx, TT_EINVAL, "gemm_bf16: column sums need the k-major kernel");
@@ -789,7 +864,7 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
   TT_REQUIRE(ctx, entries && out && n > 0 && k_max > 0, "gemm_group: bad arguments");
   std::vector<GemmGroupEntry> t(entries, entries + n);
   int tiles = 0;
-  double mn2 = 0;
+  double mn2 = 0, bytes_k = 0, bytes_out = 0;
   for (auto &e : t) {
     TT_REQUIRE(ctx, e.A && e.B && e.out && e.M > 0 && e.N > 0, "gemm_group: bad entry");
     TT_REQUIRE(ctx, e.lda >= e.M && e.ldb >= e.N && e.ldo >= e.N, "gemm_group: bad leading dims");
@@ -804,6 +879,8 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
     e.vec_out = ((uintptr_t)e.out % 16 == 0 && e.ldo % 4 == 0) ? 1 : 0;
     tiles += e.tiles_m * e.tiles_n;
     mn2 += 2.0 * e.M * e.N;
+    bytes_k += 2.0 * (e.M + e.N);
+    bytes_out += 4.0 * e.M * e.N;
   }
   const int grid = (tiles + 7) / 8 * 8;
   TT_REQUIRE(ctx, grid < 0xffff && n < 0xffff, "gemm_group: too many tiles");
@@ -828,6 +905,8 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
   out->tiles = tiles;
   out->grid = grid;
   out->mn2 = mn2;
+  out->bytes_k = bytes_k;
+  out->bytes_out = bytes_out;
   return TT_OK;
 }
 
@@ -845,7 +924,7 @@ int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K) {
   if (!name[0])
     snprintf(name, sizeof name, "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, false, false, true>",
              GT::bm, GT::bn, GT::bk, GT::wm, GT::wn, GT::ns);
-  tt_prof_scope prof(ctx, name, g.mn2 * K, 0.0);
+  tt_prof_scope prof(ctx, name, g.mn2 * K, g.bytes_k * K + g.bytes_out);
   hipLaunchKernelGGL((gemm_bf16_v3_kernel<GBM, GBN, GBK, GT::wm, GT::wn, GT::ns, false, false, true>),
                      dim3(g.grid), dim3(64 * GT::wm * GT::wn), 0, ctx->stream, p);
   return tt_check_launch(ctx, "gemm_group");

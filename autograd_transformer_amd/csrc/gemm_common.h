@@ -156,6 +156,19 @@ inline bool gemm_vec_out(const GemmArgs &g) {
   return ok;
 }
 
+// Algorithmic HBM bytes of one product (bf16 operands read once, the output
+// written once, the epilogue's second input read once): with the FLOPs, the
+// arithmetic intensity that says which roofline bounds the launch.
+inline double gemm_bytes(const GemmArgs &g) {
+  const double mn = (double)g.M * g.N;
+  double b = 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + mn * (g.out_bf16 ? 2.0 : 4.0);
+  if (g.epi == EPI_GELU && g.aux) b += mn * (g.out_bf16 ? 2.0 : 4.0);
+  if (g.epi == EPI_GELU_BWD) b += mn * (g.out_bf16 ? 2.0 : 4.0);
+  if (g.epi == EPI_RESID || g.epi == EPI_STORE_ACC || (g.epi == EPI_ACCUM && !g.overwrite))
+    b += mn * 4.0;
+  return b;
+}
+
 // Bytes spanned by an operand: rows x reduction, k-major or row-major.
 inline size_t gemm_extent_bytes(bool kmajor, int rows, int K, int ld) {
   return kmajor ? ((size_t)(rows - 1) * ld + K) * 2 : ((size_t)(K - 1) * ld + rows) * 2;

@@ -192,6 +192,7 @@ struct GemmGroup {
   uint16_t *map = nullptr;           // device: workgroup -> entry (0xffff: padding)
   int n = 0, tiles = 0, grid = 0;
   double mn2 = 0;                    // sum of 2 M N (FLOPs per unit of K)
+  double bytes_k = 0, bytes_out = 0;  // operand bytes per unit of K; output bytes
 };
 // Plan a group (entries are copied; the device tables come from the arena
 // and stay valid as long as it does).  Every entry must satisfy the bf16
@@ -227,11 +228,24 @@ struct tt_tdesc {
 int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles, double elems);
 // Inference (decode.hip): copy a prefill's keys and values (qkv columns
 // C..3C of rows b*T + t) into the cache [B_max, T_max, 2C]; attention of one
-// new position pos over the cache, appending its key and value first.
+// new position pos over the cache, appending its key and value first, with
+// the keys split over up to max_splits workgroups per (sequence, head) whose
+// partials go to part (B * NH * max_splits * 66 floats).
 int tt_kv_store(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int T_max, const void *qkv,
                 void *kv);
-int tt_attn_decode(tt_ctx *ctx, tt_mode mode, int B, int NH, int pos, int T_max, const void *qkv,
-                   void *kv, void *att);
+// The position comes from device memory (pos_dev), so that one captured
+// decode step serves every position; pos_hint only sizes the timer's work.
+constexpr int TT_DECODE_MAX_SPLITS = 16;
+int tt_decode_splits(int B, int NH);
+int tt_attn_decode(tt_ctx *ctx, tt_mode mode, int B, int NH, const int32_t *pos_dev, int pos_hint,
+                   int T_max, const void *qkv, void *kv, void *att, float *part, int S);
+// pos_dev = pos, tok_dev[0..B) = tok[0..B) (one small launch).
+int tt_decode_prep(tt_ctx *ctx, int B, int pos, const int32_t *tok, int32_t *tok_dev,
+                   int32_t *pos_dev);
+// x[b] = wte[tok_dev[b]] + wpe[*pos_dev].
+int tt_embed_decode(tt_ctx *ctx, int B, int C, int V, const int32_t *tok_dev,
+                    const int32_t *pos_dev, const float *wte, const float *wpe, float *x);
+int tt_copy_i32(tt_ctx *ctx, int n, const int32_t *src, int32_t *dst);
 int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      void *out, float *lse);
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,

@@ -1,6 +1,7 @@
 """Benchmark: one GPT-2 training step (forward, backward, AdamW) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
+    python bench.py --decode             (greedy decoding with the KV cache, B=8)
     python bench.py --calibrate-copy     (1 GiB device copies, for HBM counter scaling)
 
 Workload (default): GPT-2 124M — 12 layers, d=768, 12 heads, vocab 50257
@@ -91,6 +92,135 @@ def measured_traffic(workload, B, T, kernel):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
+def bound_of(k):
+    """The roofline that bounds a kernel: MFMA when its algorithmic intensity
+    (FLOPs per HBM byte) reaches the ridge point of the two peaks, else HBM."""
+    if k["flops"] > 0 and (k["bytes"] <= 0 or
+                           k["flops"] / k["bytes"] >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)):
+        return "mfma"
+    return "hbm"
+
+
+def roofline(kernels, steps, ms):
+    """Roofline of the dominant kernel (largest total time in the profiled
+    pass): algorithmic FLOPs or bytes per launch over its average launch."""
+    dom = max(kernels, key=lambda k: k["ms"])
+    avg_ms = dom["ms"] / dom["calls"]
+    if bound_of(dom) == "mfma":
+        achieved = dom["flops"] / dom["calls"] / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        achieved = dom["bytes"] / dom["calls"] / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom["name"]
+    roof["calls_per_step"] = dom["calls"] / steps
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+    roof["share_of_step"] = round(dom["ms"] / steps / ms, 4)
+    return roof
+
+
+def log_kernels(kernels, steps, n=8):
+    for k in sorted(kernels, key=lambda k: -k["ms"])[:n]:
+        rate = (f"{k['flops'] / (k['ms'] / 1e3) / 1e12:7.1f} TFLOP/s" if bound_of(k) == "mfma" else
+                f"{k['bytes'] / (k['ms'] / 1e3) / 1e9:7.1f} GB/s")
+        log(f"[bench]   {k['ms'] / steps:7.3f} ms/step  {k['calls'] // steps:4d} calls  "
+            f"{rate}  {k['name']}")
+
+
+def cpu_decode_baseline(w, P):
+    """The oracle's greedy step as it stands (the whole sequence recomputed, no
+    cache), one sequence at context P, scaled to tokens/s."""
+    import numpy as np
+    import oracle  # noqa: F401  (test infrastructure: the baseline leg only)
+    from oracle import gpt2 as og
+    from autograd_transformer_amd import synthetic as syn
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
+    shape = syn.ModelShape(w["L"], w["C"], w["NH"], w["V"], w["T"])
+    cfg = og.GPTConfig(n_layer=w["L"], n_embd=w["C"], n_head=w["NH"], vocab=w["V"],
+                       block_size=w["T"])
+    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=3).items()}
+    tok, _ = syn.gpt2_tokens(1, P, w["V"], seed=5)
+    t0 = time.perf_counter()
+    og.greedy_generate(p, tok, 1, cfg, "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one greedy step of one sequence at context {P} (full forward recomputed, "
+                      f"float64 NumPy, bf16 storage rounding); {dt:.1f} s"}
+
+
+def decode_main(args, w):
+    """Greedy decoding with the KV cache: prefill P tokens per sequence, then
+    time single-token decode steps (logits, argmax) at growing positions."""
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+    L, C, NH, V, V_pad, T, B = (w[k] for k in ("L", "C", "NH", "V", "V_pad", "T", "B"))
+    P = T // 2
+    K = min(args.steps, (T - P - args.warmup) // 2)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    ctx = tt.Context(arena_bytes=(64 << 30) if L > 12 else (24 << 30), stream=stream)
+    model = tt.Model(ctx, L=L, C=C, NH=NH, V=V, T_max=T, B_max=B, mode="bf16", V_pad=V_pad)
+    model.load(syn.gpt2_params(syn.ModelShape(L, C, NH, V, T), seed=3))
+    cache = tt.KVCache(ctx, model, B)
+    prompt, _ = syn.gpt2_tokens(B, P, V, seed=5)
+    nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    tt.tt_model_prefill(ctx, model, cache, B, P, torch.from_numpy(prompt).cuda(), None, nxt)
+    cur = torch.zeros(B, dtype=torch.int32, device="cuda")
+    pos = P
+
+    def step():
+        nonlocal pos
+        cur.copy_(nxt)
+        tt.tt_model_decode(ctx, model, cache, B, pos, cur, None, nxt)
+        pos += 1
+
+    for _ in range(args.warmup):
+        step()
+    ctx.sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0 = pos
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    ctx.profile(True)
+    for _ in range(K):
+        step()
+    kernels = ctx.profile_report()
+    ctx.profile(False)
+    ctx.sync()
+    value = B / (ms / 1e3)
+    log(f"[bench] decode: {ms * 1e3:.1f} us/step  {value:,.0f} tokens/s  (B={B}, positions "
+        f"{p0}..{p0 + K - 1})")
+    out = {
+        "metric": "greedy decode tokens/sec with KV cache, GPT-2 124M at 1 GPU",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded uniform token ids, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload} greedy decode, KV cache, bf16", "batch": B,
+                   "prompt": P, "positions": [p0, p0 + K - 1], "parallelism": "single GPU"},
+        "roofline": roofline(kernels, K, ms),
+    }
+    log_kernels(kernels, K)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle's greedy step ...")
+        out["cpu_baseline"] = cpu_decode_baseline(w, P)
+    cache.close()
+    model.close()
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +228,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure greedy decoding with the KV cache instead of training")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -123,6 +255,9 @@ def main():
     from autograd_transformer_amd import synthetic as syn
 
     w = WORKLOADS[args.workload]
+    if args.decode:
+        decode_main(args, w)
+        return
     L, C, NH, V, V_pad, T, B = (w[k] for k in ("L", "C", "NH", "V", "V_pad", "T", "B"))
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -204,31 +339,9 @@ def main():
         "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "loss": round(last_loss, 5),
     }
-    dom = max(kernels, key=lambda k: k["ms"])
-    avg_ms = dom["ms"] / dom["calls"]
-    if dom["flops"] > 0:
-        per_launch = dom["flops"] / dom["calls"]
-        achieved = per_launch / (avg_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        per_launch = dom["bytes"] / dom["calls"]
-        achieved = per_launch / (avg_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = round(achieved / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, B, T, dom["name"])
-    roof["kernel"] = dom["name"]
-    roof["calls_per_step"] = dom["calls"] / args.steps
-    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
-    roof["share_of_step"] = round(dom["ms"] / args.steps / ms, 4)
-    out["roofline"] = roof
-    top = sorted(kernels, key=lambda k: -k["ms"])[:8]
-    for k in top:
-        rate = (f"{k['flops'] / (k['ms'] / 1e3) / 1e12:7.1f} TFLOP/s" if k["flops"] > 0 else
-                f"{k['bytes'] / (k['ms'] / 1e3) / 1e9:7.1f} GB/s")
-        log(f"[bench]   {k['ms'] / args.steps:7.3f} ms/step  {k['calls'] // args.steps:4d} calls  "
-            f"{rate}  {k['name']}")
+    out["roofline"] = roofline(kernels, args.steps, ms)
+    out["roofline"]["traffic"] = measured_traffic(args.workload, B, T, out["roofline"]["kernel"])
+    log_kernels(kernels, args.steps)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w)

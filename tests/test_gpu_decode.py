@@ -6,7 +6,9 @@
   against the oracle's full-sequence forward over the tokens the GPU chose
   (teacher forcing: causality makes the two the same computation), the GPU's
   token equal to the argmax of its own logits, and to the oracle's argmax
-  wherever the oracle's top-two margin exceeds the observed error;
+  wherever the oracle's top-two margin exceeds the observed error; the
+  decode steps replay one captured HIP graph, and the same steps run
+  eagerly match every replay bit for bit;
 * the full-size GPT-2 124M model (bf16): a decode step after a prefill gives
   the logits a prefill over the longer sequence gives (a property that holds
   at any size).
@@ -97,6 +99,21 @@ def test_prefill_and_decode_small_model_against_oracle(ctx, mode):
         top2 = np.sort(ref, axis=-1)[:, -2:]
         clear = (top2[:, 1] - top2[:, 0]) > 2 * err + 1e-12
         assert np.array_equal(toks[j][clear], oracle.argmax_rows(ref)[clear]), j
+    # The steps above replayed one captured graph; run them again eagerly
+    # (profiling mode launches every kernel on the context's stream) and
+    # compare every step bit for bit.
+    ctx.profile(True)
+    tt.tt_model_prefill(ctx, model, cache, B, T0, dev(prompt, "i32"), lg, nxt)
+    sync()
+    assert np.array_equal(host(lg), logits[0])
+    for j in range(steps):
+        tt.tt_model_decode(ctx, model, cache, B, T0 + j, dev(toks[j].astype(np.int32), "i32"), lg,
+                           nxt)
+        sync()
+        assert np.array_equal(host(lg), logits[j + 1]), j
+        assert np.array_equal(host(nxt).astype(np.int64), toks[j + 1]), j
+    ctx.profile_report()
+    ctx.profile(False)
     cache.close()
     model.close()
 
