@@ -301,5 +301,20 @@ def adamw_update(w, g, m, v, lr, beta1, beta2, eps, wd, t):
     return w_new, m_new, v_new
 
 
+def clip_grad_norm(grads, max_norm, eps=1e-6):
+    """Global-norm gradient clipping.  The C++/CUDA page (section 3.2) keeps
+    gradients in their own storage so that they can be clipped by their norm
+    before the update; it prints no formula.  Reading (PyTorch's
+    clip_grad_norm_): the L2 norm over every gradient entry of every tensor,
+    coefficient max_norm / (norm + eps), applied only when it is below 1.
+    Returns (clipped grads as float64, the norm before clipping)."""
+    g64 = {k: np.asarray(v, np.float64) for k, v in grads.items()}
+    total = math.sqrt(sum(float(np.sum(v * v)) for v in g64.values()))
+    coef = max_norm / (total + eps)
+    if coef < 1.0:
+        g64 = {k: v * coef for k, v in g64.items()}
+    return g64, total
+
+
 def sgd_update(w, g, lr):
     return np.asarray(w, np.float64) - lr * np.asarray(g, np.float64)

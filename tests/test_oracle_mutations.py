@@ -52,6 +52,9 @@ MUTANTS = {
     "argmax_highest_index_on_ties": ("ops.py",
                                      "return np.argmax(np.asarray(z), axis=-1).astype(np.int64)",
                                      "return (np.asarray(z).shape[-1] - 1 - np.argmax(np.asarray(z)[..., ::-1], axis=-1)).astype(np.int64)"),
+    "clip_norm_without_sqrt": ("ops.py",
+                               "total = math.sqrt(sum(float(np.sum(v * v)) for v in g64.values()))",
+                               "total = sum(float(np.sum(v * v)) for v in g64.values())"),
     "greedy_takes_first_position": ("gpt2.py",
                                     "z = model_logits(params, seq, cfg, mode)[:, -1, :]",
                                     "z = model_logits(params, seq, cfg, mode)[:, 0, :]"),

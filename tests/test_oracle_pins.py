@@ -436,3 +436,36 @@ def test_greedy_tokens_are_argmaxes_of_the_full_forward():
     for j in range(5):
         assert np.array_equal(seq[:, 2 + j], np.argmax(z[:, 1 + j], axis=-1))
         assert np.allclose(steps[j], z[:, 1 + j], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ gradient clipping
+
+def test_clip_grad_norm_three_four_five():
+    """Norm of (3, 4) is 5: above max_norm the gradients scale by
+    max_norm / (5 + 1e-6), below it they are unchanged."""
+    g = {"a": np.array([3.0]), "b": np.array([[4.0, 0.0]])}
+    out, n = oracle.clip_grad_norm(g, 1.0)
+    assert n == 5.0
+    c = 1.0 / (5.0 + 1e-6)
+    assert out["a"].tolist() == [3.0 * c] and out["b"].tolist() == [[4.0 * c, 0.0]]
+    out, n = oracle.clip_grad_norm(g, 10.0)
+    assert n == 5.0 and out["a"].tolist() == [3.0] and out["b"].tolist() == [[4.0, 0.0]]
+
+
+def test_clip_grad_norm_brute_force_and_torch():
+    rng = np.random.default_rng(12)
+    g = {f"t{i}": rng.standard_normal(rng.integers(1, 40, size=2)) for i in range(6)}
+    out, n = oracle.clip_grad_norm(g, 0.5)
+    s = 0.0
+    for v in g.values():
+        for x in v.reshape(-1):
+            s += float(x) * float(x)
+    assert abs(n - math.sqrt(s)) <= 1e-12 * n
+    import torch
+    ts = [torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in g.values()]
+    for t, v in zip(ts, g.values()):
+        t.grad = torch.tensor(v, dtype=torch.float64)
+    tn = torch.nn.utils.clip_grad_norm_(ts, 0.5)
+    assert abs(float(tn) - n) <= 1e-12 * n
+    for t, k in zip(ts, g):
+        assert np.allclose(t.grad.numpy(), out[k], rtol=1e-12, atol=0)
