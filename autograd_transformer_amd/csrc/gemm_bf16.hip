@@ -537,7 +537,7 @@ gemm_bf16_v3_kernel(GemmParams p) {
     p.tiles_m = q.tiles_m; p.tiles_n = q.tiles_n; p.vec_out = q.vec_out;
     p.a_bytes = (uint32_t)(((size_t)(p.K - 1) * q.lda + q.M) * 2);
     p.b_bytes = (uint32_t)(((size_t)(p.K - 1) * q.ldb + q.N) * 2);
-    tile_coords(bid - q.tile0, q.tiles_m * q.tiles_n, q.tiles_m, q.tiles_n, p.raster_n, tm, tn,
+    tile_coords(bid - q.tile0, q.tiles_m * q.tiles_n, q.tiles_m, q.tiles_n, q.raster_n, tm, tn,
                 false);
   } else {
     tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
@@ -627,8 +627,8 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   static char names[4][96];
   const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0);
   if (!names[li][0])
-    snprintf(names[li], sizeof names[li], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s>", BM,
-             BN, BKV, WM, WN, NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
+    snprintf(names[li], sizeof names[li], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s, false>",
+             BM, BN, BKV, WM, WN, NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
   tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
 #define TT_L3(AK, BKM)                                                                          \
   if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                  \
@@ -877,6 +877,10 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
     e.tiles_n = (e.N + GBN - 1) / GBN;
     e.tile0 = tiles;
     e.vec_out = ((uintptr_t)e.out % 16 == 0 && e.ldo % 4 == 0) ? 1 : 0;
+    // Tile order: neighbouring workgroups share the panel of the larger
+    // operand (n fastest when A has far more columns than B, as for the token
+    // table: its [tokens, vocabulary] gradient panel is then read once).
+    e.raster_n = e.M >= 4 * e.N ? 1 : 0;
     tiles += e.tiles_m * e.tiles_n;
     mn2 += 2.0 * e.M * e.N;
     bytes_k += 2.0 * (e.M + e.N);

@@ -180,12 +180,13 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
 // sum over k < K of A[k, m] B[k, n], both operands bf16 with the reduction
 // index as their row index (A[k * lda + m], B[k * ldb + n]) -- the shape of
 // every weight gradient (Xᵀ · dY).  K is shared by the group and given at run
-// time; tiles_m, tiles_n, tile0 and vec_out are filled in by the planner.
+// time; tiles_m, tiles_n, tile0, vec_out and raster_n are filled in by the
+// planner.
 struct GemmGroupEntry {
   const void *A; const void *B; float *out;
   int lda, ldb, ldo;
   int M, N;
-  int tiles_m, tiles_n, tile0, vec_out;
+  int tiles_m, tiles_n, tile0, vec_out, raster_n;
 };
 struct GemmGroup {
   GemmGroupEntry *table = nullptr;   // device copy of the entries
