@@ -9,6 +9,7 @@ was not built.
 """
 
 import ctypes as _C
+import os
 
 from . import _lib as _L
 
@@ -340,6 +341,33 @@ def tt_model_fwd_bwd(ctx, model, B, T, tok, targets, loss):
 
 def tt_model_adamw(ctx, model, lr, beta1, beta2, eps, wd, t):
     return ctx.check(lib().tt_model_adamw(ctx.handle, model.handle, lr, beta1, beta2, eps, wd, t))
+
+
+def tt_model_clip_grad_norm(ctx, model, max_norm, norm=None):
+    """Scale every gradient of the model by max_norm / (norm + 1e-6) when that
+    is below 1; norm (float32 [1] on the GPU, optional) receives the norm."""
+    return ctx.check(lib().tt_model_clip_grad_norm(ctx.handle, model.handle, max_norm,
+                                                   _ptr(norm)))
+
+
+def tt_clip_grad_norm(ctx, g, max_norm, norm=None):
+    """Global-norm clipping of one float32 gradient buffer in place."""
+    return ctx.check(lib().tt_clip_grad_norm(ctx.handle, _ptr(g), g.numel(), max_norm,
+                                             _ptr(norm)))
+
+
+def tt_model_save(ctx, model, path, step):
+    """Write weights, AdamW moments and the step count as a safetensors file."""
+    return ctx.check(lib().tt_model_save(ctx.handle, model.handle, os.fsencode(path), step))
+
+
+def tt_model_load_state(ctx, model, path):
+    """Read a checkpoint written by tt_model_save (or a weights-only
+    safetensors file with the same names); returns the stored step."""
+    step = _C.c_int64(0)
+    ctx.check(lib().tt_model_load_state(ctx.handle, model.handle, os.fsencode(path),
+                                        _C.byref(step)))
+    return step.value
 
 
 # ------------------------------------------------------------------ inference

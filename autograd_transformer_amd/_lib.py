@@ -14,6 +14,8 @@ vp = C.c_void_p
 i32 = C.c_int
 f32 = C.c_float
 sz = C.c_size_t
+i64 = C.c_int64
+cstr = C.c_char_p
 
 
 class tt_block_cfg(C.Structure):
@@ -90,6 +92,10 @@ SIGS = {
     "tt_train_step": (i32, [vp, vp, i32, i32, vp, vp, f32, f32, f32, f32, f32, i32, vp, vp]),
     "tt_model_fwd_bwd": (i32, [vp, vp, i32, i32, vp, vp, vp]),
     "tt_model_adamw": (i32, [vp, vp, f32, f32, f32, f32, f32, i32]),
+    "tt_model_clip_grad_norm": (i32, [vp, vp, f32, vp]),
+    "tt_clip_grad_norm": (i32, [vp, vp, sz, f32, vp]),
+    "tt_model_save": (i32, [vp, vp, cstr, i64]),
+    "tt_model_load_state": (i32, [vp, vp, cstr, P(i64)]),
     "tt_argmax": (i32, [vp, i32, i32, i32, i32, vp, vp]),
     "tt_kvcache_create": (i32, [vp, vp, i32, P(vp)]),
     "tt_kvcache_destroy": (None, [vp]),

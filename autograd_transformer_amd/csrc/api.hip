@@ -1061,3 +1061,292 @@ extern "C" int tt_model_decode(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B,
   TT_TRY(tt_copy_i32(ctx, B, kc->next_dev, next));
   return copy_logits(ctx, md, kc, B, logits);
 }
+
+// ------------------------------------------------------------ gradient clipping
+
+extern "C" int tt_model_clip_grad_norm(tt_ctx *ctx, tt_model *md, float max_norm, float *norm) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "clip_grad_norm: bad model handle");
+  TT_REQUIRE(ctx, md->ctx == ctx, "clip_grad_norm: model belongs to another context");
+  // every slot: padding slots hold zero gradients and add nothing to the norm
+  return tt_clip_grad_norm(ctx, md->g, md->n_slots, max_norm, norm);
+}
+
+// ------------------------------------------------------------ checkpoints
+// The Forge page (section "safetensors格式的安全性优势") reads and writes
+// safetensors: an 8-byte little-endian header length, a JSON header naming
+// each tensor's dtype, shape and byte range, then the raw data.  Here a
+// checkpoint holds the fp32 master weights under the names of the
+// HuggingFace GPT-2 files (wte.weight, h.0.attn.c_attn.weight, ...; the token
+// table's V rows, W as [in, out]), the AdamW moments as adam_m.<name> and
+// adam_v.<name>, and the step count as adam_step (I64 [1]).
+
+namespace {
+
+struct CkTensor {
+  std::string name;
+  std::vector<int64_t> shape;
+  size_t slot, n;
+};
+
+std::vector<CkTensor> ck_tensors(const tt_model *md) {
+  const tt_model_cfg &c = md->cfg;
+  const int64_t C = c.C, F = c.F;
+  std::vector<CkTensor> t;
+  auto add = [&](int idx, const std::string &name, std::vector<int64_t> shape) {
+    size_t n = 1;
+    for (int64_t d : shape) n *= (size_t)d;
+    t.push_back({name, shape, md->off[idx], n});
+  };
+  add(P_WTE, "wte.weight", {c.V, C});
+  add(P_WPE, "wpe.weight", {c.T_max, C});
+  static const char *ln[PER_LAYER] = {"ln_1.weight", "ln_1.bias", "attn.c_attn.weight",
+                                      "attn.c_attn.bias", "attn.c_proj.weight", "attn.c_proj.bias",
+                                      "ln_2.weight", "ln_2.bias", "mlp.c_fc.weight", "mlp.c_fc.bias",
+                                      "mlp.c_proj.weight", "mlp.c_proj.bias"};
+  const std::vector<int64_t> sh[PER_LAYER] = {{C}, {C}, {C, 3 * C}, {3 * C}, {C, C}, {C},
+                                              {C}, {C}, {C, F}, {F}, {F, C}, {C}};
+  for (int l = 0; l < c.L; ++l)
+    for (int i = 0; i < PER_LAYER; ++i)
+      add(P_LAYER0 + PER_LAYER * l + i, "h." + std::to_string(l) + "." + ln[i], sh[i]);
+  const int lf = p_lnf_g(md);
+  add(lf, "ln_f.weight", {C});
+  add(lf + 1, "ln_f.bias", {C});
+  return t;
+}
+
+std::string shape_json(const std::vector<int64_t> &s) {
+  std::string o = "[";
+  for (size_t i = 0; i < s.size(); ++i) o += (i ? "," : "") + std::to_string(s[i]);
+  return o + "]";
+}
+
+// A JSON reader for safetensors headers: objects, arrays, strings, integers,
+// true/false/null.  Values are kept as the tensor entries need them.
+struct JVal {
+  enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
+  double num = 0;
+  std::string str;
+  std::vector<JVal> arr;
+  std::vector<std::pair<std::string, JVal>> obj;
+};
+
+struct JParser {
+  const std::string &s;
+  size_t i = 0;
+  bool ok = true;
+  explicit JParser(const std::string &src) : s(src) {}
+  void ws() { while (i < s.size() && (s[i] == ' ' || s[i] == '\n' || s[i] == '\r' || s[i] == '\t')) ++i; }
+  bool eat(char c) { ws(); if (i < s.size() && s[i] == c) { ++i; return true; } return false; }
+  std::string string() {
+    std::string o;
+    if (!eat('"')) { ok = false; return o; }
+    while (i < s.size() && s[i] != '"') {
+      if (s[i] == '\\' && i + 1 < s.size()) {
+        const char e = s[++i];
+        o += e == 'n' ? '\n' : e == 't' ? '\t' : e;
+        ++i;
+      } else {
+        o += s[i++];
+      }
+    }
+    if (i >= s.size()) ok = false;
+    ++i;
+    return o;
+  }
+  JVal value(int depth = 0) {
+    JVal v;
+    ws();
+    if (!ok || i >= s.size() || depth > 16) { ok = false; return v; }
+    const char c = s[i];
+    if (c == '{') {
+      v.kind = JVal::OBJ; ++i;
+      if (eat('}')) return v;
+      do {
+        std::string k = string();
+        if (!eat(':')) { ok = false; return v; }
+        v.obj.emplace_back(k, value(depth + 1));
+      } while (ok && eat(','));
+      if (!eat('}')) ok = false;
+    } else if (c == '[') {
+      v.kind = JVal::ARR; ++i;
+      if (eat(']')) return v;
+      do v.arr.push_back(value(depth + 1)); while (ok && eat(','));
+      if (!eat(']')) ok = false;
+    } else if (c == '"') {
+      v.kind = JVal::STR; v.str = string();
+    } else if (s.compare(i, 4, "true") == 0) {
+      v.kind = JVal::BOOL; v.num = 1; i += 4;
+    } else if (s.compare(i, 5, "false") == 0) {
+      v.kind = JVal::BOOL; i += 5;
+    } else if (s.compare(i, 4, "null") == 0) {
+      i += 4;
+    } else {
+      size_t j = i;
+      while (j < s.size() && (isdigit((unsigned char)s[j]) || s[j] == '-' || s[j] == '+' ||
+                              s[j] == '.' || s[j] == 'e' || s[j] == 'E')) ++j;
+      if (j == i) { ok = false; return v; }
+      v.kind = JVal::NUM; v.num = strtod(s.substr(i, j - i).c_str(), nullptr); i = j;
+    }
+    return v;
+  }
+};
+
+struct CkEntry {
+  std::string dtype;
+  std::vector<int64_t> shape;
+  uint64_t begin = 0, end = 0;
+};
+
+struct FileCloser {
+  FILE *f;
+  ~FileCloser() { if (f) fclose(f); }
+};
+
+}  // namespace
+
+extern "C" int tt_model_save(tt_ctx *ctx, tt_model *md, const char *path, int64_t step) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "model_save: bad model handle");
+  TT_REQUIRE(ctx, md->ctx == ctx && path, "model_save: bad arguments");
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "model_save: %s", hipGetErrorString(e));
+  const std::vector<CkTensor> ts = ck_tensors(md);
+  struct Out { std::string name; const float *src; size_t n; std::vector<int64_t> shape; };
+  std::vector<Out> outs;
+  for (const char *kind : {"", "adam_m.", "adam_v."})
+    for (const CkTensor &t : ts) {
+      const float *base = kind[0] == 0 ? md->w : (kind[5] == 'm' ? md->m : md->v);
+      outs.push_back({std::string(kind) + t.name, base + t.slot, t.n, t.shape});
+    }
+  std::string hdr = "{\"__metadata__\":{\"format\":\"pt\"}";
+  uint64_t off = 0;
+  for (const Out &o : outs) {
+    hdr += ",\"" + o.name + "\":{\"dtype\":\"F32\",\"shape\":" + shape_json(o.shape) +
+           ",\"data_offsets\":[" + std::to_string(off) + "," + std::to_string(off + 4 * o.n) + "]}";
+    off += 4 * o.n;
+  }
+  hdr += ",\"adam_step\":{\"dtype\":\"I64\",\"shape\":[1],\"data_offsets\":[" +
+         std::to_string(off) + "," + std::to_string(off + 8) + "]}}";
+  while (hdr.size() % 8) hdr += ' ';
+  FileCloser fc{fopen(path, "wb")};
+  if (!fc.f) return tt_set_error(ctx, TT_EINVAL, "model_save: cannot open %s", path);
+  const uint64_t hl = hdr.size();   // little-endian host
+  bool ok = fwrite(&hl, 8, 1, fc.f) == 1 && fwrite(hdr.data(), 1, hl, fc.f) == hl;
+  std::vector<float> buf;
+  for (const Out &o : outs) {
+    if (!ok) break;
+    buf.resize(o.n);
+    e = hipMemcpy(buf.data(), o.src, o.n * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "model_save: %s", hipGetErrorString(e));
+    ok = fwrite(buf.data(), 4, o.n, fc.f) == o.n;
+  }
+  ok = ok && fwrite(&step, 8, 1, fc.f) == 1;
+  if (!ok) return tt_set_error(ctx, TT_EINVAL, "model_save: write to %s failed", path);
+  return TT_OK;
+}
+
+extern "C" int tt_model_load_state(tt_ctx *ctx, tt_model *md, const char *path, int64_t *step) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "model_load_state: bad model handle");
+  TT_REQUIRE(ctx, md->ctx == ctx && path, "model_load_state: bad arguments");
+  FileCloser fc{fopen(path, "rb")};
+  if (!fc.f) return tt_set_error(ctx, TT_EINVAL, "model_load_state: cannot open %s", path);
+  fseek(fc.f, 0, SEEK_END);
+  const long fsize = ftell(fc.f);
+  fseek(fc.f, 0, SEEK_SET);
+  uint64_t hl = 0;
+  if (fsize < 8 || fread(&hl, 8, 1, fc.f) != 1 || hl > (uint64_t)fsize - 8 || hl > (1u << 30))
+    return tt_set_error(ctx, TT_EINVAL, "model_load_state: %s is not a safetensors file", path);
+  std::string hdr(hl, ' ');
+  if (fread(&hdr[0], 1, hl, fc.f) != hl)
+    return tt_set_error(ctx, TT_EINVAL, "model_load_state: short header in %s", path);
+  JParser jp(hdr);
+  const JVal root = jp.value();
+  if (!jp.ok || root.kind != JVal::OBJ)
+    return tt_set_error(ctx, TT_EINVAL, "model_load_state: bad JSON header in %s", path);
+  const uint64_t data0 = 8 + hl, dsize = (uint64_t)fsize - data0;
+  std::vector<std::pair<std::string, CkEntry>> entries;
+  for (const auto &kv : root.obj) {
+    if (kv.first == "__metadata__") continue;
+    const JVal &v = kv.second;
+    CkEntry ce;
+    bool good = v.kind == JVal::OBJ;
+    for (const auto &f : v.obj) {
+      if (f.first == "dtype" && f.second.kind == JVal::STR) ce.dtype = f.second.str;
+      else if (f.first == "shape" && f.second.kind == JVal::ARR)
+        for (const JVal &d : f.second.arr) ce.shape.push_back((int64_t)d.num);
+      else if (f.first == "data_offsets" && f.second.kind == JVal::ARR && f.second.arr.size() == 2) {
+        ce.begin = (uint64_t)f.second.arr[0].num;
+        ce.end = (uint64_t)f.second.arr[1].num;
+      }
+    }
+    if (!good || ce.end < ce.begin || ce.end > dsize)
+      return tt_set_error(ctx, TT_EINVAL, "model_load_state: bad entry %s", kv.first.c_str());
+    entries.emplace_back(kv.first, ce);
+  }
+  auto find = [&](const std::string &name) -> const CkEntry * {
+    for (const auto &e : entries)
+      if (e.first == name) return &e.second;
+    return nullptr;
+  };
+  const tt_model_cfg &c = md->cfg;
+  std::vector<float> buf;
+  auto read_into = [&](const CkEntry &ce, float *dst, size_t n) -> int {
+    buf.resize(n);
+    if (fseek(fc.f, (long)(data0 + ce.begin), SEEK_SET) != 0 || fread(buf.data(), 4, n, fc.f) != n)
+      return tt_set_error(ctx, TT_EINVAL, "model_load_state: short data in %s", path);
+    hipError_t e = hipMemcpy(dst, buf.data(), n * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "model_load_state: %s", hipGetErrorString(e));
+    return TT_OK;
+  };
+  // everything runs after the stream's pending work, then the copies
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "model_load_state: %s", hipGetErrorString(e));
+  for (const CkTensor &t : ck_tensors(md)) {
+    const CkEntry *w = find(t.name);
+    if (!w) return tt_set_error(ctx, TT_EINVAL, "model_load_state: %s lacks %s", path, t.name.c_str());
+    std::vector<int64_t> want = t.shape;
+    size_t n = t.n;
+    if (t.name == "wte.weight" && w->shape.size() == 2 && w->shape[0] == c.V_pad) {
+      want[0] = c.V_pad;   // a padded table is accepted too
+      n = (size_t)c.V_pad * c.C;
+    }
+    for (const char *kind : {"", "adam_m.", "adam_v."}) {
+      const CkEntry *ce = kind[0] ? find(std::string(kind) + t.name) : w;
+      float *base = kind[0] == 0 ? md->w : (kind[5] == 'm' ? md->m : md->v);
+      float *dst = base + t.slot;
+      if (t.name == "wte.weight") {   // pad rows stay zero
+        const size_t all = (size_t)c.V_pad * c.C;
+        TT_TRY(tt_fill_f32(ctx, dst, all, 0.f));
+        e = hipStreamSynchronize(ctx->stream);
+        if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "model_load_state: %s", hipGetErrorString(e));
+      }
+      if (!ce) {
+        if (kind[0] == 0) return TT_EINVAL;
+        if (t.name != "wte.weight") TT_TRY(tt_fill_f32(ctx, dst, t.n, 0.f));
+        continue;   // a weights-only file: the moments start at zero
+      }
+      if (ce->dtype != "F32" || ce->shape != want || ce->end - ce->begin != 4 * n)
+        return tt_set_error(ctx, TT_EINVAL, "model_load_state: %s%s has dtype %s or shape "
+                            "other than F32 %s", kind, t.name.c_str(), ce->dtype.c_str(),
+                            shape_json(want).c_str());
+      TT_TRY(read_into(*ce, dst, n));
+    }
+  }
+  if (step) {
+    *step = 0;
+    const CkEntry *se = find("adam_step");
+    if (se) {
+      if (se->dtype != "I64" || se->end - se->begin != 8 ||
+          fseek(fc.f, (long)(data0 + se->begin), SEEK_SET) != 0 || fread(step, 8, 1, fc.f) != 1)
+        return tt_set_error(ctx, TT_EINVAL, "model_load_state: bad adam_step in %s", path);
+    }
+  }
+  // the bf16 shadow and its transposed copy follow the loaded weights
+  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp));
+  return refresh_transposed(md);
+}

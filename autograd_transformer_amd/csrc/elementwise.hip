@@ -201,6 +201,63 @@ __global__ void __launch_bounds__(256) finite_kernel(size_t n, const float *__re
   if (bad) atomicOr(flag, 1);
 }
 
+// Global-norm gradient clipping (the C++/CUDA page, section 3.2, clips the
+// separately stored gradients by their norm; coefficient max_norm / (norm +
+// 1e-6), applied when below 1 -- PyTorch's clip_grad_norm_).  Pass 1: each
+// workgroup's sum of squares in float64; pass 2: every workgroup adds the
+// CLIP_G partials in the same order (so all agree on the norm bit for bit)
+// and scales its share of the gradient.
+constexpr int CLIP_G = 1024;
+
+__global__ void __launch_bounds__(256) sumsq_kernel(size_t n, const float *__restrict__ g,
+                                                    double *__restrict__ part) {
+  double s = 0.0;
+  const size_t n4 = n / 4, stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 v = ((const float4 *)g)[i];
+    s += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  }
+  if (blockIdx.x == 0)
+    for (size_t i = n4 * 4 + threadIdx.x; i < n; i += 256) s += (double)g[i] * g[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  __shared__ double red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void __launch_bounds__(256) clip_scale_kernel(size_t n, float *__restrict__ g,
+                                                         const double *__restrict__ part,
+                                                         float max_norm, float *__restrict__ norm_out) {
+  static_assert(CLIP_G == 4 * 256, "four partials per thread");
+  __shared__ double red[4];
+  __shared__ double coef_s;
+  double t = (part[threadIdx.x] + part[threadIdx.x + 256]) +
+             (part[threadIdx.x + 512] + part[threadIdx.x + 768]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double nrm = sqrt((red[0] + red[1]) + (red[2] + red[3]));
+    coef_s = (double)max_norm / (nrm + 1e-6);
+    if (blockIdx.x == 0 && norm_out) *norm_out = (float)nrm;
+  }
+  __syncthreads();
+  const double c = coef_s;
+  if (c >= 1.0) return;
+  const float cf = (float)c;
+  const size_t n4 = n / 4, stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 v = ((float4 *)g)[i];
+    v.x *= cf; v.y *= cf; v.z *= cf; v.w *= cf;
+    ((float4 *)g)[i] = v;
+  }
+  if (blockIdx.x == 0)
+    for (size_t i = n4 * 4 + threadIdx.x; i < n; i += 256) g[i] *= cf;
+}
+
 }  // namespace
 
 int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v) {
@@ -339,4 +396,22 @@ extern "C" int tt_gelu_bwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, c
     hipLaunchKernelGGL(gelu_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
                        (const float *)x, (const float *)dy, (float *)dx);
   return tt_check_launch(ctx, "gelu_bwd");
+}
+
+extern "C" int tt_clip_grad_norm(tt_ctx *ctx, float *g, size_t n, float max_norm, float *norm) {
+  TT_TRY(tt_check_ctx(ctx));
+  TT_REQUIRE(ctx, g && n > 0 && tt_aligned16(g), "clip_grad_norm: bad gradient buffer");
+  TT_REQUIRE(ctx, max_norm > 0.f, "clip_grad_norm: max_norm must be positive");
+  tt_scratch_scope scope(ctx);
+  void *part;
+  TT_TRY(tt_arena_alloc(ctx, CLIP_G * sizeof(double), &part));
+  {
+    tt_prof_scope prof(ctx, "sumsq_kernel", 0.0, 4.0 * n);
+    hipLaunchKernelGGL(sumsq_kernel, dim3(CLIP_G), dim3(256), 0, ctx->stream, n, g, (double *)part);
+    TT_TRY(tt_check_launch(ctx, "sumsq"));
+  }
+  tt_prof_scope prof(ctx, "clip_scale_kernel", 0.0, 8.0 * n);
+  hipLaunchKernelGGL(clip_scale_kernel, dim3(CLIP_G), dim3(256), 0, ctx->stream, n, g,
+                     (const double *)part, max_norm, norm);
+  return tt_check_launch(ctx, "clip_scale");
 }

@@ -314,6 +314,34 @@ int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *
 int tt_model_adamw(tt_ctx *ctx, tt_model *model, float lr, float beta1, float beta2,
                    float eps, float wd, int t);
 
+/* Global-norm gradient clipping over every parameter gradient of the model
+ * (the C++/CUDA page, section 3.2, clips the separately stored gradients by
+ * their norm; reading: PyTorch's clip_grad_norm_): norm = sqrt(sum g^2) in
+ * float64 over all entries, then g *= max_norm / (norm + 1e-6) when that is
+ * below 1.  norm (nullable device float) receives the norm before clipping.
+ * Call between tt_model_fwd_bwd and tt_model_adamw.  max_norm > 0. */
+int tt_model_clip_grad_norm(tt_ctx *ctx, tt_model *model, float max_norm, float *norm);
+/* The same on one gradient buffer g [n] float32 (16-byte aligned). */
+int tt_clip_grad_norm(tt_ctx *ctx, float *g, size_t n, float max_norm, float *norm);
+
+/* Checkpoints in the safetensors layout the Forge page reads and writes
+ * (section "safetensors格式的安全性优势": 8-byte little-endian header length,
+ * JSON header with each tensor's dtype, shape and byte range, raw data).
+ * Tensors: the fp32 master weights under the HuggingFace GPT-2 names
+ * (wte.weight [V,C], wpe.weight, h.<l>.ln_1.weight, h.<l>.attn.c_attn.weight
+ * [C,3C], ..., ln_f.bias; W as [in, out]), the AdamW moments as
+ * adam_m.<name> / adam_v.<name>, and step as adam_step (I64 [1]).  save waits
+ * for the context's stream and writes path [host string].  load_state reads
+ * such a file (a weights-only file, e.g. without adam_* entries, leaves the
+ * moments zero; a [V_pad,C] token table is accepted), rebuilds the bf16
+ * shadow, and returns the step in *step (nullable; 0 if absent).  Shape or
+ * dtype mismatches and I/O errors return TT_EINVAL with the reason in
+ * tt_ctx_last_error; after a failed load the model's weights and moments may
+ * be partly overwritten (load again before training).  Both synchronise the
+ * host with the context's stream. */
+int tt_model_save(tt_ctx *ctx, tt_model *model, const char *path, int64_t step);
+int tt_model_load_state(tt_ctx *ctx, tt_model *model, const char *path, int64_t *step);
+
 /* ---------------------------------------------------------------- inference
  * Greedy generation with a key/value cache.  The Forge page's GPT-2 inference
  * picks the most likely next token and names the missing KV cache as its main
