@@ -36,7 +36,7 @@ from .ops import (
     layernorm_fwd, layernorm_bwd,
     gelu_fwd, gelu_bwd,
     attention_fwd, attention_bwd,
-    softmax_rows, cross_entropy_fwdbwd,
+    softmax_rows, softmax_bwd, cross_entropy_fwdbwd,
     lmhead_ce_fwdbwd,
     embed_fwd, embed_bwd,
     adamw_update, sgd_update,
@@ -51,7 +51,7 @@ __all__ = [
     "round_bf16",
     "linear_fwd", "linear_bwd", "layernorm_fwd", "layernorm_bwd",
     "gelu_fwd", "gelu_bwd", "attention_fwd", "attention_bwd",
-    "softmax_rows", "cross_entropy_fwdbwd", "lmhead_ce_fwdbwd",
+    "softmax_rows", "softmax_bwd", "cross_entropy_fwdbwd", "lmhead_ce_fwdbwd",
     "embed_fwd", "embed_bwd", "adamw_update", "sgd_update", "argmax_rows", "clip_grad_norm",
     "GPTConfig", "param_shapes", "param_count", "zero_grads",
     "block_fwd", "block_bwd", "model_fwd_bwd", "train_step", "mlp_step",

@@ -140,6 +140,16 @@ def softmax_rows(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def softmax_bwd(p, dp):
+    """Gradient through a row softmax p = softmax(z): dz_i = sum_j dp_j dp_j/dz_i
+    with dp_j/dz_i = p_j (delta_ij - p_i), i.e. dz = p * (dp - rowsum(dp * p)).
+    The tinytorch page (section 3 item 3) lists a Softmax node with its own
+    backward; this is that rule written out from the derivative."""
+    p = np.asarray(p, np.float64)
+    dp = np.asarray(dp, np.float64)
+    return p * (dp - (dp * p).sum(axis=-1, keepdims=True))
+
+
 def logsumexp_rows(z):
     z = np.asarray(z, np.float64)
     m = z.max(axis=-1)

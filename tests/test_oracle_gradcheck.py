@@ -247,3 +247,14 @@ def test_mlp_step_matches_torch():
     for k in P:
         assert np.allclose(grads[k], tp[k].grad.numpy(), atol=1e-14)
         assert np.allclose(new[k], P[k] - 0.1 * tp[k].grad.numpy(), atol=1e-14)
+
+
+def test_softmax_bwd_central_differences():
+    """The row-softmax backward against central differences of sum(r * softmax(z))."""
+    rng = np.random.default_rng(23)
+    z = rng.standard_normal((5, 7)) * 2.0
+    r = rng.standard_normal((5, 7))
+    dz = oracle.softmax_bwd(oracle.softmax_rows(z), r)
+    fd_check(lambda: float(np.sum(r * oracle.softmax_rows(z))), {"z": z}, {"z": dz}, n_coords=35)
+    # rows of the gradient sum to zero (softmax is shift invariant)
+    assert np.max(np.abs(dz.sum(axis=1))) < 1e-12

@@ -34,6 +34,9 @@ MUTANTS = {
                         "var = (xc * xc).sum(axis=-1) / (x.shape[-1] - 1)"),
     "ln_bwd_dropped_term": ("ops.py", "dx = rstd[..., None] * (g - mg - xhat * mgx)",
                             "dx = rstd[..., None] * (g - mg)"),
+    "softmax_bwd_dropped_rowsum": ("ops.py",
+                                   "return p * (dp - (dp * p).sum(axis=-1, keepdims=True))",
+                                   "return p * dp"),
     "ce_no_mean": ("ops.py", "grad_scale = 1.0 / n", "grad_scale = 1.0"),
     "adamw_no_bias_correction": ("ops.py", "v_hat = v_new / (1.0 - beta2 ** t)", "v_hat = v_new"),
     "adamw_decay_without_lr": ("ops.py",
