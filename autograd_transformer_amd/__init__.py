@@ -370,6 +370,87 @@ def tt_model_load_state(ctx, model, path):
     return step.value
 
 
+# ------------------------------------------------------------------ graph
+
+class Graph:
+    """Recorded-graph autograd (tt_graph): nodes are integer ids; leaves wrap
+    caller float32 tensors, computed nodes live in the context's arena."""
+
+    def __init__(self, ctx):
+        self.ctx = ctx
+        h = _C.c_void_p()
+        ctx.check(lib().tt_graph_create(ctx.handle, _C.byref(h)))
+        self.handle = h
+        self._keep = []   # tensors the graph reads (leaves, targets)
+
+    def _id(self, fn, *args):
+        out = _C.c_int(-1)
+        self.ctx.check(fn(self.handle, *args, _C.byref(out)))
+        return out.value
+
+    def leaf(self, data, grad=None):
+        rows, cols = (1, data.shape[0]) if data.dim() == 1 else tuple(data.shape)
+        self._keep += [data, grad]
+        return self._id(lib().tt_graph_leaf, rows, cols, _ptr(data), _ptr(grad))
+
+    def matmul(self, a, b):
+        return self._id(lib().tt_graph_matmul, a, b)
+
+    def add(self, a, b):
+        return self._id(lib().tt_graph_add, a, b)
+
+    def gelu(self, a):
+        return self._id(lib().tt_graph_gelu, a)
+
+    def softmax(self, a):
+        return self._id(lib().tt_graph_softmax, a)
+
+    def cross_entropy(self, logits, targets):
+        self._keep.append(targets)
+        return self._id(lib().tt_graph_cross_entropy, logits, _ptr(targets))
+
+    def forward(self, node):
+        return self.ctx.check(lib().tt_graph_forward(self.handle, node))
+
+    def backward(self, loss):
+        return self.ctx.check(lib().tt_graph_backward(self.handle, loss))
+
+    def zero_grad(self):
+        return self.ctx.check(lib().tt_graph_zero_grad(self.handle))
+
+    def capture_sgd_step(self, loss, lr):
+        """Record forward / zero_grad / backward / SGD as one HIP graph."""
+        return self.ctx.check(lib().tt_graph_capture_sgd_step(self.handle, loss, lr))
+
+    def step(self):
+        """Replay the captured training step on the context's stream."""
+        return self.ctx.check(lib().tt_graph_step(self.handle))
+
+    def _tensor(self, node, which):
+        import torch
+        v, g = _C.c_void_p(), _C.c_void_p()
+        r, c = _C.c_int(), _C.c_int()
+        self.ctx.check(lib().tt_graph_tensor(self.handle, node, _C.byref(v), _C.byref(g),
+                                             _C.byref(r), _C.byref(c)))
+        addr = v.value if which == "value" else g.value
+        if addr is None:
+            return None
+        return _tensor_view(addr, (r.value, c.value), torch.float32, self.ctx.device)
+
+    def value(self, node):
+        """A torch view of a node's value (valid while the arena holds it)."""
+        return self._tensor(node, "value")
+
+    def grad(self, node):
+        return self._tensor(node, "grad")
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().tt_graph_destroy(self.handle)
+            self.handle = None
+        self._keep = []
+
+
 # ------------------------------------------------------------------ inference
 
 def tt_argmax(ctx, mode, N, V, ld, logits, out):

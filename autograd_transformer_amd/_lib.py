@@ -96,6 +96,20 @@ SIGS = {
     "tt_clip_grad_norm": (i32, [vp, vp, sz, f32, vp]),
     "tt_model_save": (i32, [vp, vp, cstr, i64]),
     "tt_model_load_state": (i32, [vp, vp, cstr, P(i64)]),
+    "tt_graph_create": (i32, [vp, P(vp)]),
+    "tt_graph_destroy": (None, [vp]),
+    "tt_graph_leaf": (i32, [vp, i32, i32, vp, vp, P(i32)]),
+    "tt_graph_matmul": (i32, [vp, i32, i32, P(i32)]),
+    "tt_graph_add": (i32, [vp, i32, i32, P(i32)]),
+    "tt_graph_gelu": (i32, [vp, i32, P(i32)]),
+    "tt_graph_softmax": (i32, [vp, i32, P(i32)]),
+    "tt_graph_cross_entropy": (i32, [vp, i32, vp, P(i32)]),
+    "tt_graph_forward": (i32, [vp, i32]),
+    "tt_graph_backward": (i32, [vp, i32]),
+    "tt_graph_zero_grad": (i32, [vp]),
+    "tt_graph_capture_sgd_step": (i32, [vp, i32, f32]),
+    "tt_graph_step": (i32, [vp]),
+    "tt_graph_tensor": (i32, [vp, i32, P(vp), P(vp), P(i32), P(i32)]),
     "tt_argmax": (i32, [vp, i32, i32, i32, i32, vp, vp]),
     "tt_kvcache_create": (i32, [vp, vp, i32, P(vp)]),
     "tt_kvcache_destroy": (None, [vp]),

@@ -361,6 +361,7 @@ extern "C" int tt_sgd_step(tt_ctx *ctx, float *w, const float *g, size_t n, floa
   TT_TRY(tt_check_ctx(ctx));
   TT_REQUIRE(ctx, w && g, "sgd: NULL pointer");
   if (n == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "sgd_kernel", 0.0, 12.0 * n);
   hipLaunchKernelGGL(sgd_kernel, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n, w, g, lr);
   return tt_check_launch(ctx, "sgd");
 }

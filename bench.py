@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
     python bench.py --decode             (greedy decoding with the KV cache, B=8)
+    python bench.py --mlp                (the tiny classifier through the graph autograd)
     python bench.py --calibrate-copy     (1 GiB device copies, for HBM counter scaling)
 
 Workload (default): GPT-2 124M — 12 layers, d=768, 12 heads, vocab 50257
@@ -101,14 +102,14 @@ def bound_of(k):
     return "hbm"
 
 
-def roofline(kernels, steps, ms):
+def roofline(kernels, steps, ms, peak_mfma=PEAK_BF16_TFLOPS):
     """Roofline of the dominant kernel (largest total time in the profiled
     pass): algorithmic FLOPs or bytes per launch over its average launch."""
     dom = max(kernels, key=lambda k: k["ms"])
     avg_ms = dom["ms"] / dom["calls"]
     if bound_of(dom) == "mfma":
         achieved = dom["flops"] / dom["calls"] / (avg_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     else:
         achieved = dom["bytes"] / dom["calls"] / (avg_ms / 1e3) / 1e9
@@ -221,6 +222,92 @@ def decode_main(args, w):
     print(json.dumps(out), flush=True)
 
 
+def mlp_main(args):
+    """The tiny classifier (x [64,3] -> Linear 3->32 -> GELU -> Linear 32->4 ->
+    mean cross-entropy -> SGD lr 0.1) recorded as a tt_graph: per-step time of
+    the eager walk and of the step captured as one HIP graph."""
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    ctx = tt.Context(arena_bytes=1 << 26, stream=stream)
+    d = syn.mlp_inputs(seed=1)
+    P = {k: torch.from_numpy(d[k]).float().cuda() for k in ("W1", "b1", "W2", "b2")}
+    G = {k: torch.zeros_like(v) for k, v in P.items()}
+    g = tt.Graph(ctx)
+    x = g.leaf(torch.from_numpy(d["x"]).float().cuda())
+    ids = {k: g.leaf(P[k], G[k]) for k in P}
+    h = g.gelu(g.add(g.matmul(x, ids["W1"]), ids["b1"]))
+    loss = g.cross_entropy(g.add(g.matmul(h, ids["W2"]), ids["b2"]),
+                           torch.from_numpy(d["labels"]).int().cuda())
+
+    def eager():
+        g.forward(loss)
+        g.zero_grad()
+        g.backward(loss)
+        for k in P:
+            tt.tt_sgd_step(ctx, P[k], G[k], 0.1)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    K = max(args.steps, 200)
+    for _ in range(args.warmup):
+        eager()
+    us_eager = timed(eager, K)
+    ctx.profile(True)
+    for _ in range(K):
+        eager()
+    kernels = ctx.profile_report()
+    ctx.profile(False)
+    launches = sum(k["calls"] for k in kernels) / K
+    g.capture_sgd_step(loss, 0.1)
+    for _ in range(args.warmup):
+        g.step()
+    us_graph = timed(g.step, K)
+    final = float(g.value(loss).item())
+    log(f"[bench] tiny classifier: eager {us_eager:.1f} us/step ({launches:.0f} launches), "
+        f"captured {us_graph:.1f} us/step, loss {final:.4f}")
+    out = {
+        "metric": "tiny-classifier SGD step time (graph autograd; x[64,3], Linear 3->32, GELU, "
+                  "Linear 32->4, mean CE, SGD lr 0.1)",
+        "value": round(us_graph, 2), "unit": "us/step", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us_graph / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) inputs and weights, uniform labels)",
+        "config": {"workload": "tiny classifier step, 64 samples, captured HIP graph",
+                   "eager_us_per_step": round(us_eager, 2), "launches_per_step": launches,
+                   "parallelism": "single GPU"},
+        # float32 products: the fp32 peak (157.3 TFLOP/s) where a kernel is a
+        # contraction; at this size every kernel is launch-latency bound
+        "roofline": roofline(kernels, K, us_eager / 1e3, peak_mfma=157.3),
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import gpt2 as og  # test infrastructure: the baseline leg only
+        W = {k: d[k].astype(np.float64) for k in P}
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 2.0:
+            og.mlp_step(d["x"], W["W1"], W["b1"], W["W2"], W["b2"], d["labels"])
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        out["cpu_baseline"] = {"value": round(dt * 1e6, 2), "unit": "us/step", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} oracle steps of the same classifier (float64 "
+                                         f"NumPy) in {n * dt:.1f} s"}
+    g.close()
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +317,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="measure greedy decoding with the KV cache instead of training")
+    ap.add_argument("--mlp", action="store_true",
+                    help="measure the tiny classifier's step through the graph autograd")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -254,6 +343,9 @@ def main():
     import autograd_transformer_amd as tt
     from autograd_transformer_amd import synthetic as syn
 
+    if args.mlp:
+        mlp_main(args)
+        return
     w = WORKLOADS[args.workload]
     if args.decode:
         decode_main(args, w)

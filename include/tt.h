@@ -380,6 +380,61 @@ int tt_model_prefill(tt_ctx *ctx, tt_model *model, tt_kvcache *cache, int B, int
 int tt_model_decode(tt_ctx *ctx, tt_model *model, tt_kvcache *cache, int B, int pos,
                     const int32_t *tok, void *logits, int32_t *next);
 
+/* ---------------------------------------------------------------- graph
+ * Recorded-graph autograd over the library's float32 ops — the tinytorch
+ * page, section 3 item 3 (each op's result remembers its op and inputs;
+ * Backward walks from the loss to the inputs) with the non-recursive
+ * topological walk its comparison table recommends; gradients accumulate
+ * with += (C++/CUDA page, section 3.2).  Tensors are 2-D [rows, cols]
+ * row-major float32 and named by integer ids in creation order.  A node's
+ * inputs precede it, so creation order is topological.  Values and the
+ * gradients of computed nodes are carved from the context's arena (valid
+ * until it is reset below them or destroyed); leaves use caller memory.
+ * Every call validates on the host first (TT_EINVAL on a bad id or shape)
+ * and then enqueues kernels on the context's stream. */
+typedef struct tt_graph tt_graph;
+int tt_graph_create(tt_ctx *ctx, tt_graph **out);
+void tt_graph_destroy(tt_graph *graph); /* NULL-safe; arena memory stays */
+/* A leaf: data [rows, cols] float32 (caller-owned, read at each forward);
+ * grad (nullable) [rows, cols] float32 receiving += dloss/ddata at each
+ * backward (NULL: no gradient flows into this leaf).  16-byte aligned. */
+int tt_graph_leaf(tt_graph *graph, int rows, int cols, float *data, float *grad, int *id);
+/* c = a @ b ([M,K] x [K,N] -> [M,N]); backward dA += dC·bᵀ, dB += aᵀ·dC. */
+int tt_graph_matmul(tt_graph *graph, int a, int b, int *id);
+/* c = a + b, b of a's shape or one row [1, cols] added to every row (the
+ * bias of a linear layer; its gradient is the column sum). */
+int tt_graph_add(tt_graph *graph, int a, int b, int *id);
+/* c = tanh-form GELU(a) (tinytorch page, section 3 item 4). */
+int tt_graph_gelu(tt_graph *graph, int a, int *id);
+/* c = softmax of each row of a; backward dA += c∘(dC − rowsum(dC∘c)). */
+int tt_graph_softmax(tt_graph *graph, int a, int *id);
+/* [1,1] loss = mean over rows of logsumexp(z_r) − z_r[targets[r]] (fused
+ * log-softmax cross-entropy, tt_ce_fwdbwd); backward dz += dloss ·
+ * (softmax(z) − onehot)/rows.  targets [rows of z] int32 in [0, cols),
+ * device, read at each forward. */
+int tt_graph_cross_entropy(tt_graph *graph, int logits, const int32_t *targets, int *id);
+/* Compute node and every ancestor it needs, in creation order. */
+int tt_graph_forward(tt_graph *graph, int node);
+/* Seed dloss = 1 and apply every reachable node's gradient rule in reverse
+ * creation order, using the values of the last forward.  Gradients of
+ * computed nodes restart from zero on each call; leaf gradients accumulate
+ * (clear them with tt_graph_zero_grad).  loss: a computed [1,1] node. */
+int tt_graph_backward(tt_graph *graph, int loss);
+/* Zero every gradient buffer of the graph, the leaves' included. */
+int tt_graph_zero_grad(tt_graph *graph);
+/* One SGD training step — forward(loss), zero_grad, backward(loss), then
+ * w -= lr * grad on every leaf that has a gradient (tinytorch page, section
+ * 8: Forward, ZeroGrad, Backward, SGD) — recorded once as a HIP graph, so a
+ * step is one launch (tt_graph_step, on the context's stream).  The
+ * recording sees the graph's nodes and buffers as they are now: capture
+ * again after adding nodes.  Capturing again replaces the previous step.
+ * Not while profiling is on. */
+int tt_graph_capture_sgd_step(tt_graph *graph, int loss, float lr);
+int tt_graph_step(tt_graph *graph);
+/* A node's value and gradient (device pointers; grad NULL when no gradient
+ * flows through it) and shape; every output nullable. */
+int tt_graph_tensor(tt_graph *graph, int id, float **value, float **grad, int *rows, int *cols);
+
 #ifdef __cplusplus
 }
 #endif
