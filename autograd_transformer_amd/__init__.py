@@ -370,6 +370,18 @@ def tt_model_load_state(ctx, model, path):
     return step.value
 
 
+def tt_mlp_step(ctx, x, labels, W1, b1, W2, b2, lr, loss, grads=None):
+    """The tiny classifier's training step in one launch; weights updated in
+    place, grads (optional dict W1/b1/W2/b2 of tensors) receive gradients."""
+    N, I = x.shape
+    H, C = W1.shape[1], W2.shape[1]
+    g = grads or {}
+    return ctx.check(lib().tt_mlp_step(ctx.handle, N, I, H, C, _ptr(x), _ptr(labels), _ptr(W1),
+                                       _ptr(b1), _ptr(W2), _ptr(b2), lr, _ptr(loss),
+                                       _ptr(g.get("W1")), _ptr(g.get("b1")), _ptr(g.get("W2")),
+                                       _ptr(g.get("b2"))))
+
+
 # ------------------------------------------------------------------ graph
 
 class Graph:

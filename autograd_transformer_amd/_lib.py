@@ -96,6 +96,8 @@ SIGS = {
     "tt_clip_grad_norm": (i32, [vp, vp, sz, f32, vp]),
     "tt_model_save": (i32, [vp, vp, cstr, i64]),
     "tt_model_load_state": (i32, [vp, vp, cstr, P(i64)]),
+    "tt_mlp_step": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
+                          vp]),
     "tt_graph_create": (i32, [vp, P(vp)]),
     "tt_graph_destroy": (None, [vp]),
     "tt_graph_leaf": (i32, [vp, i32, i32, vp, vp, P(i32)]),

@@ -223,6 +223,19 @@ int tt_adamw_step(tt_ctx *ctx, const tt_param *params /* [host] */, int count, f
                   float beta1, float beta2, float eps, float wd, int t);
 /* SGD — tinytorch page §8 step 5: w -= lr * g. */
 int tt_sgd_step(tt_ctx *ctx, float *w, const float *g, size_t n, float lr);
+
+/* The tiny classifier's whole training step in ONE launch (tinytorch page,
+ * section 8 step 5: Linear -> tanh-GELU -> Linear -> softmax cross-entropy,
+ * backward, SGD): x [N,I], labels [N] int32 in [0,C), W1 [I,H], b1 [H],
+ * W2 [H,C], b2 [C] float32.  loss [1] receives the mean cross-entropy of the
+ * step's forward; the weights are updated in place (w -= lr * grad); gW1,
+ * gb1, gW2, gb2 (nullable) receive the gradients.  One workgroup holds
+ * everything in LDS: N*I + I*H + H + H*C + C + 2*N*H + N*C + N floats must
+ * fit in 16384 (TT_EINVAL otherwise).  Labels outside [0,C) give NaN and
+ * TT_ERANGE at the next tt_ctx_sync. */
+int tt_mlp_step(tt_ctx *ctx, int N, int I, int H, int C, const float *x, const int32_t *labels,
+                float *W1, float *b1, float *W2, float *b2, float lr, float *loss, float *gW1,
+                float *gb1, float *gW2, float *gb2);
 /* float32 -> bf16 (round to nearest even) copy of n values. */
 int tt_cast_bf16(tt_ctx *ctx, size_t n, const float *src, void *dst);
 

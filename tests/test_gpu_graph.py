@@ -233,3 +233,45 @@ def test_captured_step_replays_match_eager_and_oracle(ctx):
         W = new_ref
     gc.close()
     ge.close()
+
+
+# ------------------------------------------------ the step as one launch
+
+@pytest.mark.parametrize("N,I,H,C,seed", [(64, 3, 32, 4, 1), (100, 7, 50, 10, 3), (1, 3, 32, 4, 4)])
+def test_fused_mlp_step_against_oracle(ctx, N, I, H, C, seed):
+    """tt_mlp_step (forward, cross-entropy, backward, SGD in one kernel), five
+    steps, each against oracle.mlp_step."""
+    d = syn.mlp_inputs(seed=seed, batch=N, n_in=I, hidden=H, classes=C)
+    P = {k: dev(d[k]) for k in ("W1", "b1", "W2", "b2")}
+    G = {k: zeros(tuple(v.shape)) for k, v in P.items()}
+    xd, yd = dev(d["x"]), dev(d["labels"], "i32")
+    loss = zeros((1,))
+    W = {k: d[k].astype(np.float64) for k in P}
+    for step in range(5):
+        tt.tt_mlp_step(ctx, xd, yd, P["W1"], P["b1"], P["W2"], P["b2"], 0.1, loss, G)
+        sync()
+        l_ref, g_ref, new_ref, _ = og.mlp_step(d["x"], W["W1"], W["b1"], W["W2"], W["b2"],
+                                               d["labels"])
+        # (the N=1 case predicts its row confidently: loss ~1e-3, and the
+        # label's gradient entry p_y - 1 is that small too)
+        assert abs(host(loss)[0] - l_ref) <= TOL * abs(l_ref), step
+        for k in P:
+            assert rel_l2(host(G[k]), g_ref[k]) <= TOL, (step, k)
+            assert rel_l2(host(P[k]), new_ref[k]) <= TOL, (step, k)
+        W = new_ref
+
+
+def test_fused_mlp_step_limits(ctx):
+    d = syn.mlp_inputs(seed=1)
+    P = {k: dev(d[k]) for k in ("W1", "b1", "W2", "b2")}
+    loss = zeros((1,))
+    big = zeros((4096, 3))
+    with pytest.raises(tt.TTError, match="64 KB"):
+        tt.tt_mlp_step(ctx, big, dev(np.zeros(4096), "i32"), P["W1"], P["b1"], P["W2"], P["b2"],
+                       0.1, loss)
+    bad = d["labels"].copy()
+    bad[5] = 4                          # outside [0, C)
+    tt.tt_mlp_step(ctx, dev(d["x"]), dev(bad, "i32"), P["W1"], P["b1"], P["W2"], P["b2"], 0.1, loss)
+    with pytest.raises(tt.TTError, match="outside"):
+        ctx.sync()
+    assert np.isnan(host(loss)[0])
