@@ -30,7 +30,7 @@ finite differences and an independent PyTorch fp64 autograd cross-check).
 No function is "parity unpinned".
 """
 
-from .bf16 import round_bf16
+from .bf16 import round_bf16, round_fp16
 from .ops import (
     linear_fwd, linear_bwd,
     layernorm_fwd, layernorm_bwd,
@@ -45,14 +45,16 @@ from .ops import (
 from .gpt2 import (
     GPTConfig, param_shapes, param_count, zero_grads,
     block_fwd, block_bwd, model_fwd_bwd, train_step, mlp_step,
+    loss_scale_update, train_step_scaled,
 )
 
 __all__ = [
-    "round_bf16",
+    "round_bf16", "round_fp16",
     "linear_fwd", "linear_bwd", "layernorm_fwd", "layernorm_bwd",
     "gelu_fwd", "gelu_bwd", "attention_fwd", "attention_bwd",
     "softmax_rows", "softmax_bwd", "cross_entropy_fwdbwd", "lmhead_ce_fwdbwd",
     "embed_fwd", "embed_bwd", "adamw_update", "sgd_update", "argmax_rows", "clip_grad_norm",
     "GPTConfig", "param_shapes", "param_count", "zero_grads",
     "block_fwd", "block_bwd", "model_fwd_bwd", "train_step", "mlp_step",
+    "loss_scale_update", "train_step_scaled",
 ]

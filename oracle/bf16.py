@@ -1,4 +1,4 @@
-"""bfloat16 storage rounding for the oracle (test infrastructure only).
+"""bfloat16 and float16 storage rounding for the oracle (test infrastructure only).
 
 The pages never define a low-precision format; the C++/CUDA page (section 3.4,
 mixed precision) describes fp32 master weights with low-precision activations,
@@ -44,3 +44,18 @@ def round_bf16(x):
         if bad.any():
             r[bad] = a[bad]
     return r
+
+
+def round_fp16(x):
+    """Return float64 array holding the nearest-even IEEE binary16 value of ``x``.
+
+    The C++/CUDA page (section 3.4) runs activations and gradients in FP16 with
+    fp32 master weights.  binary16 keeps 11 significant bits, exponents down to
+    2**-14 (subnormal step 2**-24) and a largest finite value of 65504; values
+    at or past the midpoint 65520 become infinity.  NumPy's float64 -> float16
+    cast rounds the float64 value once, to nearest with ties to even (no
+    intermediate float32 rounding); it serves as the step here.
+    """
+    a = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return a.astype(np.float16).astype(np.float64)

@@ -14,7 +14,8 @@ where the page is silent or simplified:
 * AdamW decays every parameter (no exemption list on the pages).
 
 Precision modes.  ``mode="f32"``: no storage rounding (float64 maths
-throughout).  ``mode="bf16"`` (the C++/CUDA page, section 3.4: fp32 master
+throughout).  ``mode="fp16"``: as bf16 below with IEEE binary16 storage, used
+with loss scaling (``model_fwd_bwd(loss_scale=...)``, ``train_step_scaled``).  ``mode="bf16"`` (the C++/CUDA page, section 3.4: fp32 master
 weights, low-precision compute): the four block weight matrices and the tied
 LM-head matrix enter their products as bf16-rounded copies of the fp32 master
 values, and the tensors the training step stores as bf16 (LayerNorm outputs,
@@ -29,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .bf16 import round_bf16
+from .bf16 import round_bf16, round_fp16
 from .ops import (
     linear_fwd, linear_bwd, layernorm_fwd, layernorm_bwd, gelu_fwd, gelu_grad,
     attention_fwd, attention_bwd, lmhead_ce_fwdbwd, cross_entropy_fwdbwd,
@@ -88,6 +89,8 @@ def _store_fn(mode):
         return lambda a: a
     if mode == "bf16":
         return round_bf16
+    if mode == "fp16":
+        return round_fp16
     raise ValueError(f"unknown mode {mode!r}")
 
 
@@ -164,13 +167,26 @@ def _layer_w(params, l):
     return {k: params[f"h{l}.{k}"] for k in LAYER_PARAMS}
 
 
-def model_fwd_bwd(params, tokens, targets, cfg: GPTConfig, mode="f32"):
+def model_fwd_bwd(params, tokens, targets, cfg: GPTConfig, mode="f32", loss_scale=1.0):
     """Forward and backward of the mean next-token loss over all B*T positions.
 
     Sequences are processed one at a time with gradients accumulated (the
     result is the batched one: every per-position term carries the same
     1/(B*T) factor).  Returns (loss, grads) with grads keyed like params.
+
+    loss_scale (the C++/CUDA page, section 3.4, loss scaling for FP16): the
+    backward starts from loss_scale times the loss gradient, so every stored
+    activation gradient carries that factor (and may overflow the storage
+    format to infinity); the returned weight gradients are divided by it
+    again.  Non-finite values are left to propagate; the caller checks.
     """
+    if mode == "fp16":
+        with np.errstate(over="ignore", invalid="ignore"):
+            return _model_fwd_bwd(params, tokens, targets, cfg, mode, loss_scale)
+    return _model_fwd_bwd(params, tokens, targets, cfg, mode, loss_scale)
+
+
+def _model_fwd_bwd(params, tokens, targets, cfg, mode, loss_scale):
     S = _store_fn(mode)
     tokens = np.asarray(tokens, np.int64)
     targets = np.asarray(targets, np.int64)
@@ -192,7 +208,7 @@ def model_fwd_bwd(params, tokens, targets, cfg: GPTConfig, mode="f32"):
         f = S(f)
         lb, df, dwte_head, _ = lmhead_ce_fwdbwd(
             f.reshape(-1, C), wte_head, targets[b], store_logits=S,
-            store_dlogits=S, grad_scale=1.0 / N)
+            store_dlogits=S, grad_scale=loss_scale / N)
         loss += lb * T / N
         grads["wte"][:V] += dwte_head
         dx, dg, dbt = layernorm_bwd(x, muf, rsf, params["lnf_g"], df.reshape(1, T, C))
@@ -205,6 +221,8 @@ def model_fwd_bwd(params, tokens, targets, cfg: GPTConfig, mode="f32"):
         dwte_e, dwpe = embed_bwd(tok, dx, wte.shape[0], params["wpe"].shape[0])
         grads["wte"] += dwte_e
         grads["wpe"] += dwpe
+    if loss_scale != 1.0:
+        grads = {k: g / loss_scale for k, g in grads.items()}
     return loss, grads
 
 
@@ -242,6 +260,40 @@ def greedy_generate(params, prompt, n_new, cfg: GPTConfig, mode="f32"):
         steps.append(z)
         seq = np.concatenate([seq, argmax_rows(z)[:, None]], axis=1)
     return seq, np.stack(steps)
+
+
+def loss_scale_update(scale, good_steps, overflow, interval=1000, growth=1.001, backoff=0.5):
+    """Dynamic loss scaling (the C++/CUDA page, section 3.4): after a step whose
+    gradients hold inf or NaN the scale is halved and the step is dropped;
+    after `interval` consecutive clean steps it grows by the factor 1.001.
+    Reading: the clean-step count restarts after every change of the scale.
+    Returns (new_scale, new_good_steps)."""
+    if overflow:
+        return scale * backoff, 0
+    good_steps += 1
+    if good_steps >= interval:
+        return scale * growth, 0
+    return scale, good_steps
+
+
+def train_step_scaled(params, m, v, t, tokens, targets, cfg: GPTConfig, scale, good_steps,
+                      mode="fp16", lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1):
+    """One FP16 training step with dynamic loss scaling: the backward at the
+    current scale, then either AdamW on the unscaled gradients (all finite) or
+    no update (any inf or NaN), and the scale update.
+
+    Returns (loss, grads, new_params, new_m, new_v, new_scale, new_good_steps,
+    skipped); a skipped step returns the inputs unchanged."""
+    loss, grads = model_fwd_bwd(params, tokens, targets, cfg, mode, loss_scale=scale)
+    skipped = not all(np.all(np.isfinite(g)) for g in grads.values())
+    new_scale, new_good = loss_scale_update(scale, good_steps, skipped)
+    if skipped:
+        return loss, grads, params, m, v, new_scale, new_good, True
+    new_p, new_m, new_v = {}, {}, {}
+    for k in params:
+        new_p[k], new_m[k], new_v[k] = adamw_update(
+            params[k], grads[k], m[k], v[k], lr, beta1, beta2, eps, wd, t)
+    return loss, grads, new_p, new_m, new_v, new_scale, new_good, False
 
 
 def train_step(params, m, v, t, tokens, targets, cfg: GPTConfig, mode="f32",

@@ -37,6 +37,15 @@ MUTANTS = {
     "softmax_bwd_dropped_rowsum": ("ops.py",
                                    "return p * (dp - (dp * p).sum(axis=-1, keepdims=True))",
                                    "return p * dp"),
+    "loss_scale_not_undone": ("gpt2.py", "grads = {k: g / loss_scale for k, g in grads.items()}",
+                              "grads = {k: g for k, g in grads.items()}"),
+    "loss_scale_grows_every_step": ("gpt2.py", "if good_steps >= interval:",
+                                    "if good_steps >= 1:"),
+    "fp16_stored_as_bf16": ("gpt2.py", """    if mode == "fp16":
+        return round_fp16""", """    if mode == "fp16":
+        return round_bf16"""),
+    "fp16_double_rounding": ("bf16.py", "return a.astype(np.float16).astype(np.float64)",
+                             "return a.astype(np.float32).astype(np.float16).astype(np.float64)"),
     "ce_no_mean": ("ops.py", "grad_scale = 1.0 / n", "grad_scale = 1.0"),
     "adamw_no_bias_correction": ("ops.py", "v_hat = v_new / (1.0 - beta2 ** t)", "v_hat = v_new"),
     "adamw_decay_without_lr": ("ops.py",

@@ -469,3 +469,93 @@ def test_clip_grad_norm_brute_force_and_torch():
     assert abs(float(tn) - n) <= 1e-12 * n
     for t, k in zip(ts, g):
         assert np.allclose(t.grad.numpy(), out[k], rtol=1e-12, atol=0)
+
+
+# ------------------------------------------------ fp16 and loss scaling
+
+def test_round_fp16_ties_range_and_subnormals():
+    """binary16 by hand: 11 significant bits, ties to even, largest finite
+    65504 (65520 is the midpoint to 2**16 and rounds up to infinity),
+    subnormal step 2**-24 -- and one rounding of the float64 value (a detour
+    through float32 would turn 1 + 2**-11 + 2**-30 into the tie 1 + 2**-11
+    and then into 1)."""
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -30,
+                  65504.0, 65519.99, 65520.0, -70000.0, 2.0 ** -25, 3 * 2.0 ** -26,
+                  2.0 ** -25 + 2.0 ** -40, 2.0 ** -14, -0.0, 0.1])
+    want = np.array([1.0, 1 + 2.0 ** -9, 1 + 2.0 ** -10, 65504.0, 65504.0, np.inf, -np.inf,
+                     0.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -14, -0.0,
+                     1638 * 2.0 ** -14])   # 0.1 = 1.6 * 2**-4; 1.6 * 1024 = 1638.4 -> 1638
+    got = oracle.round_fp16(x)
+    assert np.array_equal(got, want)
+    assert np.signbit(got[11])
+    assert np.isnan(oracle.round_fp16(np.nan))
+
+
+def test_loss_scale_update_by_hand():
+    """Halve on overflow and restart the count; grow by 1.001 after 1000
+    consecutive clean steps."""
+    s, g = 65536.0, 0
+    s, g = oracle.loss_scale_update(s, g, True)
+    assert (s, g) == (32768.0, 0)
+    for _ in range(999):
+        s, g = oracle.loss_scale_update(s, g, False)
+    assert (s, g) == (32768.0, 999)
+    s, g = oracle.loss_scale_update(s, g, False)
+    assert s == 32768.0 * 1.001 and g == 0
+    s, g = oracle.loss_scale_update(s, g, False)
+    assert g == 1
+    s, g = oracle.loss_scale_update(s, 500, True)
+    assert s == 32768.0 * 1.001 / 2 and g == 0
+
+
+def _fp16_model():
+    from autograd_transformer_amd import synthetic as syn
+    cfg = og.GPTConfig(n_layer=2, n_embd=64, n_head=4, vocab=97, block_size=16)
+    shape = syn.ModelShape(2, 64, 4, 97, 16)
+    p = {k: v.astype(np.float64) for k, v in syn.gpt2_params(shape, seed=14, bias_std=0.02).items()}
+    tok, tgt = syn.gpt2_tokens(2, 16, 97, seed=14)
+    return cfg, p, tok, tgt
+
+
+def test_power_of_two_loss_scale_is_exact_without_storage_rounding():
+    """Scaling the loss gradient by 2**k and dividing the weight gradients by
+    it again changes no bit when nothing is rounded to a storage format."""
+    cfg, p, tok, tgt = _fp16_model()
+    l1, g1 = og.model_fwd_bwd(p, tok, tgt, cfg, "f32")
+    l2, g2 = og.model_fwd_bwd(p, tok, tgt, cfg, "f32", loss_scale=2.0 ** 10)
+    assert l1 == l2
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_fp16_mode_rounds_to_fp16():
+    """fp16 storage (11 significant bits) stays closer to the unrounded step
+    than bf16 storage (8 bits), and is not the unrounded step itself."""
+    cfg, p, tok, tgt = _fp16_model()
+    _, g32 = og.model_fwd_bwd(p, tok, tgt, cfg, "f32")
+    _, gh = og.model_fwd_bwd(p, tok, tgt, cfg, "fp16", loss_scale=1024.0)
+    _, gb = og.model_fwd_bwd(p, tok, tgt, cfg, "bf16")
+    eh = np.mean([rel_l2(gh[k], g32[k]) for k in g32])
+    eb = np.mean([rel_l2(gb[k], g32[k]) for k in g32])
+    assert 0 < eh < eb / 3, (eh, eb)
+    for k in g32:
+        assert rel_l2(gh[k], g32[k]) < 1e-2, k
+
+
+def test_fp16_step_overflow_is_skipped_and_scale_halves():
+    cfg, p, tok, tgt = _fp16_model()
+    zeros = {k: np.zeros_like(v) for k, v in p.items()}
+    hp = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1)
+    # 2**40 / N puts the label's dlogit far past 65504: infinity in fp16
+    out = og.train_step_scaled(p, zeros, dict(zeros), 1, tok, tgt, cfg, 2.0 ** 40, 7, **hp)
+    _, _, new_p, _, _, s, g, skipped = out
+    assert skipped and s == 2.0 ** 39 and g == 0
+    assert all(new_p[k] is p[k] for k in p)
+    # a representable scale: a normal AdamW step on the unscaled gradients
+    out = og.train_step_scaled(p, zeros, dict(zeros), 1, tok, tgt, cfg, 1024.0, 7, **hp)
+    loss, grads, new_p, new_m, _, s, g, skipped = out
+    assert not skipped and s == 1024.0 and g == 8
+    _, g_ref = og.model_fwd_bwd(p, tok, tgt, cfg, "fp16", loss_scale=1024.0)
+    for k in p:
+        w_ref, m_ref, _ = oracle.adamw_update(p[k], g_ref[k], 0, 0, t=1, **hp)
+        assert np.array_equal(new_p[k], w_ref) and np.array_equal(new_m[k], m_ref), k
