@@ -13,7 +13,7 @@ import os
 
 from . import _lib as _L
 
-TT_F32, TT_BF16 = 0, 1
+TT_F32, TT_BF16, TT_FP16 = 0, 1, 2
 TT_EPI_NONE, TT_EPI_GELU, TT_EPI_RESIDUAL = 0, 1, 2
 
 STATUS = {0: "TT_OK", -1: "TT_EINVAL", -2: "TT_ENOMEM", -3: "TT_EHIP", -4: "TT_ESTALE",
@@ -44,9 +44,9 @@ def _ptr(t):
 
 
 def _mode(m):
-    if m in (TT_F32, TT_BF16):
+    if m in (TT_F32, TT_BF16, TT_FP16):
         return m
-    return {"f32": TT_F32, "bf16": TT_BF16}[m]
+    return {"f32": TT_F32, "bf16": TT_BF16, "fp16": TT_FP16}[m]
 
 
 class Context:
@@ -283,7 +283,8 @@ class Model:
         i = self.names.index(name)
         p = self.table[i]
         addr = getattr(p, which)
-        dtype = torch.bfloat16 if which == "w_lowp" else torch.float32
+        lowp = torch.float16 if self.cfg.mode == TT_FP16 else torch.bfloat16
+        dtype = lowp if which == "w_lowp" else torch.float32
         return _tensor_view(addr, self.shapes[name], dtype, self.ctx.device)
 
     def load(self, params):
@@ -316,9 +317,11 @@ def _tensor_view(addr, shape, dtype, device):
         n *= s
     esz = torch.tensor([], dtype=dtype).element_size()
 
+    typestr = "<f4" if esz == 4 else ("<f2" if dtype == torch.float16 else "<u2")
+
     class _Arr:
         __cuda_array_interface__ = {
-            "shape": (n,), "typestr": "<f4" if esz == 4 else "<u2",
+            "shape": (n,), "typestr": typestr,
             "data": (addr, False), "version": 2, "strides": None,
         }
     t = torch.as_tensor(_Arr(), device=f"cuda:{device}")
@@ -341,6 +344,21 @@ def tt_model_fwd_bwd(ctx, model, B, T, tok, targets, loss):
 
 def tt_model_adamw(ctx, model, lr, beta1, beta2, eps, wd, t):
     return ctx.check(lib().tt_model_adamw(ctx.handle, model.handle, lr, beta1, beta2, eps, wd, t))
+
+
+def tt_model_loss_scale_set(ctx, model, scale, interval=1000, growth=1.001, backoff=0.5):
+    """Dynamic loss scaling policy and scale of a TT_FP16 model."""
+    return ctx.check(lib().tt_model_loss_scale_set(ctx.handle, model.handle, scale, interval,
+                                                   growth, backoff))
+
+
+def tt_model_loss_scale_get(ctx, model):
+    """(scale, clean steps since the last change, dropped steps) of a TT_FP16
+    model; synchronises with the context's stream."""
+    sc, good, skipped = _C.c_float(), _C.c_int(), _C.c_int()
+    ctx.check(lib().tt_model_loss_scale_get(ctx.handle, model.handle, _C.byref(sc),
+                                            _C.byref(good), _C.byref(skipped)))
+    return sc.value, good.value, skipped.value
 
 
 def tt_model_clip_grad_norm(ctx, model, max_norm, norm=None):

@@ -92,6 +92,8 @@ SIGS = {
     "tt_train_step": (i32, [vp, vp, i32, i32, vp, vp, f32, f32, f32, f32, f32, i32, vp, vp]),
     "tt_model_fwd_bwd": (i32, [vp, vp, i32, i32, vp, vp, vp]),
     "tt_model_adamw": (i32, [vp, vp, f32, f32, f32, f32, f32, i32]),
+    "tt_model_loss_scale_set": (i32, [vp, vp, f32, i32, f32, f32]),
+    "tt_model_loss_scale_get": (i32, [vp, vp, P(f32), P(i32), P(i32)]),
     "tt_model_clip_grad_norm": (i32, [vp, vp, f32, vp]),
     "tt_clip_grad_norm": (i32, [vp, vp, sz, f32, vp]),
     "tt_model_save": (i32, [vp, vp, cstr, i64]),

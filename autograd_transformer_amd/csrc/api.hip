@@ -10,8 +10,8 @@
 
 namespace {
 
-inline size_t esize(tt_mode m) { return m == TT_BF16 ? 2 : 4; }
-inline bool mode_ok(int m) { return m == TT_F32 || m == TT_BF16; }
+inline size_t esize(tt_mode m) { return tt_lowp(m) ? 2 : 4; }
+inline bool mode_ok(int m) { return m == TT_F32 || m == TT_BF16 || m == TT_FP16; }
 
 GemmArgs gemm_args() {
   GemmArgs g;
@@ -127,7 +127,7 @@ int layer_fwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F, flo
               const tt_block_w &w, const LayerWT &wt, const float *x, float *y,
               const LayerBufs &s) {
   const int N = B * T;
-  const bool lp = mode == TT_BF16;
+  const bool lp = tt_lowp(mode);
   TT_TRY(tt_layernorm_fwd_impl(ctx, mode, N, C, eps, x, w.ln1_g, w.ln1_b, s.ln1, s.mean1, s.rstd1));
   TT_TRY(linear_fwd_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, w.w_qkv, wt.w_qkv, w.b_qkv, EPI_STORE, s.qkv,
                          3 * C, lp, nullptr, 0, nullptr, 0));
@@ -168,14 +168,14 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
               const tt_block_g &gr, const BwdScratch &sc, bool fcp_bias_here, float *dsum_below,
               bool overwrite_dw) {
   const int N = B * T;
-  const bool lp = mode == TT_BF16;
+  const bool lp = tt_lowp(mode);
   // MLP down-projection: dh = (dy · W_fpᵀ) * gelu'(h), whose column sums are
   // the up-projection's bias gradient; dW_fp += gᵀ dy; db_fp.
   TT_TRY(linear_dx_gemm(ctx, mode, N, F, C, io.rl_in, C, w.w_fcp, EPI_GELU_BWD, io.dh, F, lp, s.h,
                         F, gr.b_fc));
   if (!io.defer_dw)
     TT_TRY(linear_dw_gemm(ctx, mode, N, F, C, s.g, F, io.rl_in, C, gr.w_fcp, overwrite_dw));
-  if (fcp_bias_here) TT_TRY(tt_colsum(ctx, lp, N, C, C, io.rl_in, gr.b_fcp));
+  if (fcp_bias_here) TT_TRY(tt_colsum(ctx, mode, N, C, C, io.rl_in, gr.b_fcp));
   // MLP up-projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, F, io.dh, F, w.w_fc, EPI_STORE, sc.dtmp, C, false,
                         nullptr, 0));
@@ -198,7 +198,7 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   if (!io.defer_dw)
     TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, io.dqkv, 3 * C, gr.w_qkv,
                           overwrite_dw));
-  TT_TRY(tt_colsum(ctx, lp, N, 3 * C, 3 * C, io.dqkv, gr.b_qkv));
+  TT_TRY(tt_colsum(ctx, mode, N, 3 * C, 3 * C, io.dqkv, gr.b_qkv));
   // LN1 backward + residual.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
                                lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b, dsum_below));
@@ -236,7 +236,7 @@ extern "C" int tt_linear_fwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, con
       break;
     default: return tt_set_error(ctx, TT_EINVAL, "linear_fwd: bad epilogue %d", epilogue);
   }
-  return linear_fwd_gemm(ctx, mode, M, K, N, X, K, W, nullptr, b, epi, Y, N, mode == TT_BF16, resid, N,
+  return linear_fwd_gemm(ctx, mode, M, K, N, X, K, W, nullptr, b, epi, Y, N, tt_lowp(mode), resid, N,
                          preact, N);
 }
 
@@ -253,7 +253,7 @@ extern "C" int tt_linear_bwd(tt_ctx *ctx, tt_mode mode, int M, int K, int N, con
     TT_TRY(linear_dx_gemm(ctx, mode, M, K, N, dY, N, W, accumulate_dX ? EPI_STORE_ACC : EPI_STORE,
                           dX, K, false, nullptr, 0));
   if (dW) TT_TRY(linear_dw_gemm(ctx, mode, M, K, N, X, K, dY, N, dW));
-  if (db) TT_TRY(tt_colsum(ctx, mode == TT_BF16, M, N, N, dY, db));
+  if (db) TT_TRY(tt_colsum(ctx, mode, M, N, N, dY, db));
   return TT_OK;
 }
 
@@ -323,8 +323,9 @@ extern "C" int tt_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, voi
 static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld, const void *h,
                           const void *wte, const void *wte_t, int V_pad, const int32_t *targets,
                           float *loss, float *dh, float *dwte, void *logits, float *row_loss,
-                          bool overwrite_dwte, bool skip_dwte = false) {
-  const bool lp = mode == TT_BF16;
+                          bool overwrite_dwte, bool skip_dwte = false,
+                          const float *scale_dev = nullptr) {
+  const bool lp = tt_lowp(mode);
   GemmArgs g = gemm_args();
   // z = h · wteᵀ
   g.A = h; g.lda = C; g.a_kmajor = true;
@@ -333,7 +334,8 @@ static int lmhead_ce_core(tt_ctx *ctx, tt_mode mode, int N, int C, int V, int ld
   g.epi = EPI_STORE; g.out = logits; g.ldo = ld; g.out_bf16 = lp;
   TT_TRY(tt_gemm(ctx, mode, g));
   // loss and dz = (softmax - onehot)/N in place
-  TT_TRY(tt_ce_impl(ctx, mode, N, V, ld, logits, targets, row_loss, loss, 1.0f / (float)N));
+  TT_TRY(tt_ce_impl(ctx, mode, N, V, ld, logits, targets, row_loss, loss, 1.0f / (float)N,
+                    scale_dev));
   // dh = dz · wte
   g = gemm_args();
   g.A = logits; g.lda = ld; g.a_kmajor = true;
@@ -450,9 +452,9 @@ extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
     if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_bwd copy: %s", hipGetErrorString(e));
   }
   void *Rl = dx;
-  if (mode == TT_BF16) {
+  if (tt_lowp(mode)) {
     TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * 2, &Rl));
-    TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl));
+    TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl, mode == TT_FP16));
   }
   const BwdIO io{Rl, Rl, Rl, sc.dh, sc.dqkv, false};
   return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, io,
@@ -502,6 +504,10 @@ struct tt_model {
   // table's included, run as one grouped GEMM after the backward.
   std::vector<BwdIO> lio;
   GemmGroup dw_group;
+  // TT_FP16: dynamic loss scaling (device state; host-side policy)
+  tt_loss_scale *ls = nullptr;
+  int ls_interval = 1000;
+  float ls_growth = 1.001f, ls_backoff = 0.5f;
 };
 
 namespace {
@@ -517,7 +523,7 @@ int check_model(tt_model *md) {
 }
 
 const void *mat(const tt_model *md, int idx) {
-  if (md->cfg.mode == TT_BF16) return md->lowp + md->off[idx];
+  if (tt_lowp(md->cfg.mode)) return md->lowp + md->off[idx];
   return md->w + md->off[idx];
 }
 
@@ -604,7 +610,7 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   md->g = (float *)alloc(md->n_slots * 4);
   md->m = (float *)alloc(md->n_slots * 4);
   md->v = (float *)alloc(md->n_slots * 4);
-  if (c.mode == TT_BF16) {
+  if (tt_lowp(c.mode)) {
     md->lowp = (bf16_t *)alloc(md->n_slots * 2);
     md->lowp_t = (bf16_t *)alloc(md->n_slots * 2);
     // transpose table: wte [V_pad, C], then per layer qkv, proj, fc, fcproj
@@ -644,9 +650,10 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
   md->logits = alloc((size_t)N * md->ld * es);
   md->row_loss = (float *)alloc((size_t)N * 4);
   md->R = (float *)alloc((size_t)N * C * 4);
-  md->Rl = c.mode == TT_BF16 ? alloc((size_t)N * C * 2) : (void *)md->R;
+  md->Rl = tt_lowp(c.mode) ? alloc((size_t)N * C * 2) : (void *)md->R;
+  if (c.mode == TT_FP16) md->ls = (tt_loss_scale *)alloc(sizeof(tt_loss_scale));
   if (rc == TT_OK) rc = alloc_bwd_scratch(ctx, c.mode, N, c.C, c.F, c.B_max, c.NH, c.T_max, md->sc);
-  if (rc == TT_OK && c.mode == TT_BF16) {
+  if (rc == TT_OK && tt_lowp(c.mode)) {
     md->lio.resize(c.L);
     for (int l = 0; l < c.L; ++l) {
       BwdIO &io = md->lio[l];
@@ -678,13 +685,16 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
         prod(s.att, c.C, c.C, io.rl_mid, c.C, c.C, md->g + md->off[b + 4]);
         prod(s.ln1, c.C, c.C, io.dqkv, 3 * c.C, 3 * c.C, md->g + md->off[b + 2]);
       }
-      rc = tt_gemm_group_plan(ctx, ent.data(), (int)ent.size(), N, &md->dw_group);
+      rc = tt_gemm_group_plan(ctx, ent.data(), (int)ent.size(), N, &md->dw_group,
+                              c.mode == TT_FP16);
     }
   }
   for (float *buf : {md->w, md->g, md->m, md->v})
     if (rc == TT_OK) rc = tt_fill_f32(ctx, buf, md->n_slots, 0.f);
-  if (rc == TT_OK && md->lowp) rc = tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp);
+  if (rc == TT_OK && md->lowp)
+    rc = tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp, c.mode == TT_FP16);
   if (rc == TT_OK) rc = refresh_transposed(md);
+  if (rc == TT_OK && md->ls) rc = tt_loss_scale_set(ctx, md->ls, 65536.f);
   if (rc != TT_OK) {
     ctx->offset = save;
     md->magic = 0;
@@ -732,7 +742,7 @@ extern "C" int tt_model_num_params(const tt_model *md, size_t *n_slots, size_t *
 extern "C" int tt_model_refresh_shadow(tt_model *md) {
   TT_TRY(check_model(md));
   tt_ctx *ctx = md->ctx;
-  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp));
+  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp, md->cfg.mode == TT_FP16));
   TT_TRY(refresh_transposed(md));
   TT_TRY(tt_fill_f32(ctx, md->m, md->n_slots, 0.f));
   return tt_fill_f32(ctx, md->v, md->n_slots, 0.f);
@@ -749,11 +759,13 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   TT_REQUIRE(ctx, tok && targets && loss, "fwd_bwd: NULL pointer");
   const tt_mode mode = c.mode;
   const int N = B * T, C = c.C;
-  const bool lp = mode == TT_BF16;
+  const bool lp = tt_lowp(mode);
 
   // Matrix gradients are overwritten by their GEMMs; clear the rest.  (The
   // token table's pad rows are never written and stay zero from creation.)
   TT_TRY(tt_fill_f32(ctx, md->g + md->small_begin, md->n_slots - md->small_begin, 0.f));
+  // TT_FP16: this step's overflow flag starts clear (its bits are float 0)
+  if (md->ls) TT_TRY(tt_fill_f32(ctx, (float *)&md->ls->overflow, 1, 0.f));
   TT_TRY(tt_embed_fwd(ctx, B, T, C, c.V, tok, md->w + md->off[P_WTE], md->w + md->off[P_WPE],
                       md->xs[0]));
   tt_block_w w;
@@ -770,7 +782,7 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   const bool grouped = !md->lio.empty();
   TT_TRY(lmhead_ce_core(ctx, mode, N, C, c.V, md->ld, md->lnf, mat(md, P_WTE), mat_t(md, P_WTE),
                         c.V_pad, targets, loss, md->sc.dtmp, md->g + md->off[P_WTE], md->logits,
-                        md->row_loss, true, grouped));
+                        md->row_loss, true, grouped, md->ls ? &md->ls->scale : nullptr));
   // Each LayerNorm backward also sums its output's columns into the
   // down-projection bias gradient of the block below it.
   auto fcp_bias = [&](int l) { return md->g + md->off[P_LAYER0 + PER_LAYER * l + 11]; };
@@ -789,19 +801,33 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   // Every weight-matrix gradient (stored, not accumulated) in one launch;
   // then the token rows of the embedding add into the token table's.
   if (grouped) TT_TRY(tt_gemm_group_run(ctx, md->dw_group, N));
-  return tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
-                      md->g + md->off[P_WPE]);
+  TT_TRY(tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
+                      md->g + md->off[P_WPE]));
+  // TT_FP16: the gradients carry the loss scale; divide it out and flag
+  // overflow (the update is then dropped and the scale halved)
+  if (md->ls) TT_TRY(tt_unscale_check(ctx, md->g, md->n_slots, md->ls));
+  return TT_OK;
 }
 
-extern "C" int tt_model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, float beta2,
-                              float eps, float wd, int t) {
+static int model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, float beta2, float eps,
+                       float wd, int t, int32_t *overflow_out) {
   TT_TRY(tt_check_ctx(ctx));
   int rc = check_model(md);
   if (rc != TT_OK) return tt_set_error(ctx, rc, "adamw: bad model handle");
   TT_REQUIRE(ctx, t >= 1, "adamw: t is 1-based");
+  const bool f16 = md->cfg.mode == TT_FP16;
   TT_TRY(tt_adamw_flat(ctx, md->w, md->g, md->m, md->v, md->lowp, md->n_slots, lr, beta1, beta2,
-                       eps, wd, t));
-  return refresh_transposed(md);
+                       eps, wd, t, f16, md->ls ? &md->ls->overflow : nullptr));
+  TT_TRY(refresh_transposed(md));
+  if (md->ls)
+    TT_TRY(tt_loss_scale_update(ctx, md->ls, md->ls_interval, md->ls_growth, md->ls_backoff,
+                                overflow_out));
+  return TT_OK;
+}
+
+extern "C" int tt_model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, float beta2,
+                              float eps, float wd, int t) {
+  return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nullptr);
 }
 
 extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int32_t *tok,
@@ -810,11 +836,43 @@ extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int3
   TT_TRY(tt_check_ctx(ctx));
   TT_REQUIRE(ctx, t >= 1, "train_step: t is 1-based");
   TT_TRY(tt_model_fwd_bwd(ctx, md, B, T, tok, targets, loss));
+  if (md->ls)   // TT_FP16: the flag is the step's gradient overflow (update dropped)
+    return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nonfinite);
   if (nonfinite) {
     TT_TRY(tt_fill_f32(ctx, (float *)nonfinite, 1, 0.f));
     TT_TRY(tt_check_finite(ctx, loss, 1, nonfinite));
   }
-  return tt_model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t);
+  return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nullptr);
+}
+
+extern "C" int tt_model_loss_scale_set(tt_ctx *ctx, tt_model *md, float scale, int interval,
+                                       float growth, float backoff) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "loss_scale_set: bad model handle");
+  TT_REQUIRE(ctx, md->ls != nullptr, "loss_scale_set: the model is not in TT_FP16 mode");
+  TT_REQUIRE(ctx, scale > 0.f && interval > 0 && growth >= 1.f && backoff > 0.f && backoff < 1.f,
+             "loss_scale_set: need scale > 0, interval > 0, growth >= 1, 0 < backoff < 1");
+  md->ls_interval = interval;
+  md->ls_growth = growth;
+  md->ls_backoff = backoff;
+  return tt_loss_scale_set(ctx, md->ls, scale);
+}
+
+extern "C" int tt_model_loss_scale_get(tt_ctx *ctx, tt_model *md, float *scale, int *good_steps,
+                                       int *skipped) {
+  TT_TRY(tt_check_ctx(ctx));
+  int rc = check_model(md);
+  if (rc != TT_OK) return tt_set_error(ctx, rc, "loss_scale_get: bad model handle");
+  TT_REQUIRE(ctx, md->ls != nullptr, "loss_scale_get: the model is not in TT_FP16 mode");
+  tt_loss_scale st;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e == hipSuccess) e = hipMemcpy(&st, md->ls, sizeof st, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "loss_scale_get: %s", hipGetErrorString(e));
+  if (scale) *scale = st.scale;
+  if (good_steps) *good_steps = st.good;
+  if (skipped) *skipped = st.skipped;
+  return TT_OK;
 }
 
 // ------------------------------------------------------------ inference
@@ -851,6 +909,8 @@ extern "C" int tt_kvcache_create(tt_ctx *ctx, tt_model *md, int B_max, tt_kvcach
   if (rc != TT_OK) return tt_set_error(ctx, rc, "kvcache_create: bad model handle");
   TT_REQUIRE(ctx, md->ctx == ctx, "kvcache_create: model belongs to another context");
   const tt_model_cfg &c = md->cfg;
+  if (c.mode == TT_FP16)
+    return tt_set_error(ctx, TT_EUNSUPPORTED, "kvcache_create: decoding runs in TT_F32 or TT_BF16");
   TT_REQUIRE(ctx, B_max > 0 && B_max <= c.B_max, "kvcache_create: B_max must be in [1, %d]",
              c.B_max);
   if (c.T_max > 16384)
@@ -953,7 +1013,7 @@ int copy_logits(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, void *logits_o
 int decode_body(tt_ctx *ctx, tt_model *md, tt_kvcache *kc, int B, int pos_hint) {
   const tt_model_cfg &c = md->cfg;
   const tt_mode mode = c.mode;
-  const bool lp = mode == TT_BF16;
+  const bool lp = tt_lowp(mode);
   const int C = c.C, F = c.F;
   const int S = tt_decode_splits(B, c.NH);
   TT_TRY(tt_embed_decode(ctx, B, C, c.V, kc->tok_dev, kc->pos_dev, md->w + md->off[P_WTE],
@@ -1347,6 +1407,6 @@ extern "C" int tt_model_load_state(tt_ctx *ctx, tt_model *md, const char *path, 
     }
   }
   // the bf16 shadow and its transposed copy follow the loaded weights
-  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp));
+  if (md->lowp) TT_TRY(tt_cast_f32_bf16(ctx, md->n_slots, md->w, md->lowp, md->cfg.mode == TT_FP16));
   return refresh_transposed(md);
 }

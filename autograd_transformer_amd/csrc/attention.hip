@@ -527,6 +527,11 @@ int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void
                      float *lse) {
   if (mode == TT_BF16 && tt_attn_bf16_ok(B, T, NH)) return tt_attn_fwd_bf16(ctx, B, T, NH, qkv, out, lse);
   if (mode == TT_BF16) return attn_fwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse);
+  if (mode == TT_FP16) {
+    if (!tt_attn_bf16_ok(B, T, NH))
+      return tt_set_error(ctx, TT_EUNSUPPORTED, "attention(fp16): qkv of 2 GB or more");
+    return tt_attn_fwd_bf16(ctx, B, T, NH, qkv, out, lse, true);
+  }
   return attn_fwd_t<float>(ctx, B, T, NH, qkv, out, lse);
 }
 
@@ -535,5 +540,10 @@ int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void
   if (mode == TT_BF16 && tt_attn_bf16_ok(B, T, NH))
     return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
   if (mode == TT_BF16) return attn_bwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
+  if (mode == TT_FP16) {
+    if (!tt_attn_bf16_ok(B, T, NH))
+      return tt_set_error(ctx, TT_EUNSUPPORTED, "attention(fp16): qkv of 2 GB or more");
+    return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv, true);
+  }
   return attn_bwd_t<float>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
 }

@@ -46,9 +46,10 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ bf16x8_t as_frag(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+template <bool F16>
 __device__ __forceinline__ bf16x8_t pack8(f32x4_t a, f32x4_t b) {
-  return as_frag(make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]),
-                            pack_bf2(b[2], b[3])));
+  return as_frag(make_uint4(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]),
+                            lp_pack2<F16>(b[0], b[1]), lp_pack2<F16>(b[2], b[3])));
 }
 
 // k-major fragment: token row rb + lane%16, head dims kk + 8*(lane/16) .. +7.
@@ -65,8 +66,9 @@ __device__ __forceinline__ bf16x8_t tr_frag(const bf16_t *tile, int rbase, int c
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+template <bool F16>
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  return lp_mfma<F16>(a, b, c);
 }
 
 // One 64 x 64 tile (token rows t0.., head columns col..col+63 of a [.., ld]
@@ -95,7 +97,7 @@ struct TileRegs {
 // 4 waves x 16 QS queries; K/V tiles of 64 keys; Sᵀ = K Qᵀ, Oᵀ += Vᵀ Pᵀ.
 // Workgroups run heaviest query blocks first across all heads (block index
 // outer, batch-head inner), so freed CU slots take the longest remaining work.
-template <int QS>
+template <int QS, bool F16>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out,
                      float *__restrict__ lse, int nqb, uint32_t qkv_bytes) {
@@ -152,7 +154,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
         const bf16x8_t k_0 = row_frag(ks, j * 16, 0, lr, lg), k_1 = row_frag(ks, j * 16, 32, lr, lg);
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs)
-          s[j][qs] = mfma(k_1, qf[qs][1], mfma(k_0, qf[qs][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          s[j][qs] = mfma<F16>(k_1, qf[qs][1], mfma<F16>(k_0, qf[qs][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
       }
       auto softmax = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -214,12 +216,12 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
       for (int t2 = 0; t2 < 2; ++t2) {
         bf16x8_t pb[QS];
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) pb[qs] = pack8(s[2 * t2][qs], s[2 * t2 + 1][qs]);
+        for (int qs = 0; qs < QS; ++qs) pb[qs] = pack8<F16>(s[2 * t2][qs], s[2 * t2 + 1][qs]);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const bf16x8_t va = tr_frag(vs, t2 * 32, d * 16, lr, lg);
 #pragma unroll
-          for (int qs = 0; qs < QS; ++qs) o[d][qs] = mfma(va, pb[qs], o[d][qs]);
+          for (int qs = 0; qs < QS; ++qs) o[d][qs] = mfma<F16>(va, pb[qs], o[d][qs]);
         }
       }
     }
@@ -242,8 +244,8 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
 #pragma unroll
     for (int d = 0; d < 4; ++d)
       *(uint2 *)(orow + d * 16 + lg * 4) =
-          make_uint2(pack_bf2(o[d][qs][0] * inv, o[d][qs][1] * inv),
-                     pack_bf2(o[d][qs][2] * inv, o[d][qs][3] * inv));
+          make_uint2(lp_pack2<F16>(o[d][qs][0] * inv, o[d][qs][1] * inv),
+                     lp_pack2<F16>(o[d][qs][2] * inv, o[d][qs][3] * inv));
     if (lg == 0) lse[((size_t)b * NH + h) * T + q] = (mrow[qs] + log2f(l)) / LOG2E;
   }
 }
@@ -252,6 +254,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
 // Workgroup: 64 keys (4 waves x 16) walking 64-query blocks from the
 // diagonal.  Rows = queries: S = Q Kᵀ, dP = dO Vᵀ, P = exp(S/8 - lse),
 // dS = P (dP - Dv); dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS (reductions over queries).
+template <bool F16>
 __global__ void __launch_bounds__(256, 2)
 attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
                       const float *__restrict__ lse, const float *__restrict__ Dv,
@@ -321,8 +324,8 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
       for (int qs = 0; qs < 4; ++qs) {
         const bf16x8_t a0 = row_frag(qs_t, qs * 16, 0, lr, lg), a1 = row_frag(qs_t, qs * 16, 32, lr, lg);
         const bf16x8_t o0 = row_frag(os_t, qs * 16, 0, lr, lg), o1 = row_frag(os_t, qs * 16, 32, lr, lg);
-        const f32x4_t sacc = mfma(a1, kf[1], mfma(a0, kf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-        const f32x4_t dpacc = mfma(o1, vf[1], mfma(o0, vf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t sacc = mfma<F16>(a1, kf[1], mfma<F16>(a0, kf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t dpacc = mfma<F16>(o1, vf[1], mfma<F16>(o0, vf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
         const float4 l4 = *(const float4 *)&ls[cur][qs * 16 + lg * 4];
         const float4 d4 = *(const float4 *)&ds[cur][qs * 16 + lg * 4];
         const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq4[4] = {d4.x, d4.y, d4.z, d4.w};
@@ -343,12 +346,12 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
       tile(std::false_type{});
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      const bf16x8_t pb = pack8(p[2 * t2], p[2 * t2 + 1]);
-      const bf16x8_t sb = pack8(dsv[2 * t2], dsv[2 * t2 + 1]);
+      const bf16x8_t pb = pack8<F16>(p[2 * t2], p[2 * t2 + 1]);
+      const bf16x8_t sb = pack8<F16>(dsv[2 * t2], dsv[2 * t2 + 1]);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        dv[d] = mfma(tr_frag(os_t, t2 * 32, d * 16, lr, lg), pb, dv[d]);
-        dk[d] = mfma(tr_frag(qs_t, t2 * 32, d * 16, lr, lg), sb, dk[d]);
+        dv[d] = mfma<F16>(tr_frag(os_t, t2 * 32, d * 16, lr, lg), pb, dv[d]);
+        dk[d] = mfma<F16>(tr_frag(qs_t, t2 * 32, d * 16, lr, lg), sb, dk[d]);
       }
     }
     if (qb + 1 < nqb) put(cur ^ 1);
@@ -359,16 +362,17 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int dd = d * 16 + lg * 4;
-    *(uint2 *)(drow + C + dd) = make_uint2(pack_bf2(dk[d][0] * 0.125f, dk[d][1] * 0.125f),
-                                           pack_bf2(dk[d][2] * 0.125f, dk[d][3] * 0.125f));
+    *(uint2 *)(drow + C + dd) = make_uint2(lp_pack2<F16>(dk[d][0] * 0.125f, dk[d][1] * 0.125f),
+                                           lp_pack2<F16>(dk[d][2] * 0.125f, dk[d][3] * 0.125f));
     *(uint2 *)(drow + 2 * C + dd) =
-        make_uint2(pack_bf2(dv[d][0], dv[d][1]), pack_bf2(dv[d][2], dv[d][3]));
+        make_uint2(lp_pack2<F16>(dv[d][0], dv[d][1]), lp_pack2<F16>(dv[d][2], dv[d][3]));
   }
 }
 
 // -------------------------------------------------------------------- dQ
 // Workgroup: 64 queries (4 waves x 16) walking key blocks up to the diagonal.
 // Rows = keys: Sᵀ = K Qᵀ, dPᵀ = V dOᵀ, dSᵀ = Pᵀ (dPᵀ - Dv); dQᵀ += Kᵀ dSᵀ.
+template <bool F16>
 __global__ void __launch_bounds__(256, 2)
 attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
                     const float *__restrict__ lse, const float *__restrict__ Dv,
@@ -423,10 +427,10 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4_t sacc = mfma(row_frag(ks, j * 16, 32, lr, lg), qf[1],
-                                    mfma(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-          const f32x4_t dpacc = mfma(row_frag(vs, j * 16, 32, lr, lg), of[1],
-                                     mfma(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          const f32x4_t sacc = mfma<F16>(row_frag(ks, j * 16, 32, lr, lg), qf[1],
+                                    mfma<F16>(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          const f32x4_t dpacc = mfma<F16>(row_frag(vs, j * 16, 32, lr, lg), of[1],
+                                     mfma<F16>(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float pv = ex2(fmaf(sacc[r], SL2, -lq));
@@ -443,9 +447,9 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
         tile(std::false_type{});
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8_t sb = pack8(dsv[2 * t2], dsv[2 * t2 + 1]);
+        const bf16x8_t sb = pack8<F16>(dsv[2 * t2], dsv[2 * t2 + 1]);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) dq[d] = mfma(tr_frag(ks, t2 * 32, d * 16, lr, lg), sb, dq[d]);
+        for (int d = 0; d < 4; ++d) dq[d] = mfma<F16>(tr_frag(ks, t2 * 32, d * 16, lr, lg), sb, dq[d]);
       }
     }
     if (kb + 1 < nkb) {
@@ -459,12 +463,13 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
 #pragma unroll
   for (int d = 0; d < 4; ++d)
     *(uint2 *)(drow + d * 16 + lg * 4) =
-        make_uint2(pack_bf2(dq[d][0] * 0.125f, dq[d][1] * 0.125f),
-                   pack_bf2(dq[d][2] * 0.125f, dq[d][3] * 0.125f));
+        make_uint2(lp_pack2<F16>(dq[d][0] * 0.125f, dq[d][1] * 0.125f),
+                   lp_pack2<F16>(dq[d][2] * 0.125f, dq[d][3] * 0.125f));
 }
 
 // Dv[b,h,t] = sum_d dO[t, h*64+d] * O[t, h*64+d]: one wave per (token, 4
 // heads), 16 lanes per head, 4 elements per lane.
+template <bool F16>
 __global__ void __launch_bounds__(256) attn_dot_bf16_kernel(int BT, int T, int NH,
                                                             const bf16_t *__restrict__ o,
                                                             const bf16_t *__restrict__ dO,
@@ -478,8 +483,8 @@ __global__ void __launch_bounds__(256) attn_dot_bf16_kernel(int BT, int T, int N
   if (ok) {
     const size_t off = (size_t)row * NH * HS + h * HS + l16 * 4;
     const uint2 a = *(const uint2 *)(o + off), c = *(const uint2 *)(dO + off);
-    s = bf2f(a.x & 0xffffu) * bf2f(c.x & 0xffffu) + bf2f(a.x >> 16) * bf2f(c.x >> 16) +
-        bf2f(a.y & 0xffffu) * bf2f(c.y & 0xffffu) + bf2f(a.y >> 16) * bf2f(c.y >> 16);
+    s = lp_to<F16>(a.x & 0xffffu) * lp_to<F16>(c.x & 0xffffu) + lp_to<F16>(a.x >> 16) * lp_to<F16>(c.x >> 16) +
+        lp_to<F16>(a.y & 0xffffu) * lp_to<F16>(c.y & 0xffffu) + lp_to<F16>(a.y >> 16) * lp_to<F16>(c.y >> 16);
   }
 #pragma unroll
   for (int w = 8; w > 0; w >>= 1) s += __shfl_xor(s, w, 64);
@@ -493,39 +498,60 @@ bool tt_attn_bf16_ok(int B, int T, int NH) {
   return qkv < OOB;
 }
 
-int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse) {
+int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse,
+                     bool f16) {
   constexpr int QS = 1;   // 64 queries per workgroup
   const int nqb = (T + 64 * QS - 1) / (64 * QS);
   const uint32_t qb = (uint32_t)((size_t)B * T * 3 * NH * HS * 2);
   const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
   tt_prof_scope prof(ctx, "attn_fwd_bf16_kernel", 2.0 * pass, 0.0);
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<QS>, dim3(B * NH * nqb), dim3(256), 0, ctx->stream, T,
-                     NH, (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
+  if (f16)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<QS, true>), dim3(B * NH * nqb), dim3(256), 0,
+                       ctx->stream, T, NH, (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<QS, false>), dim3(B * NH * nqb), dim3(256), 0,
+                       ctx->stream, T, NH, (const bf16_t *)qkv, (bf16_t *)out, lse, nqb, qb);
   return tt_check_launch(ctx, "attn_fwd_bf16");
 }
 
 int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
-                     const float *lse, const void *dout, void *dqkv, float *Dv) {
+                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16) {
   const int BT = B * T;
   const uint32_t qb = (uint32_t)((size_t)BT * 3 * NH * HS * 2);
   const uint32_t ob = (uint32_t)((size_t)BT * NH * HS * 2);
   const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
   {
     tt_prof_scope prof(ctx, "attn_dot_bf16_kernel", 0.0, 2.0 * ob + 4.0 * BT * NH);
-    hipLaunchKernelGGL(attn_dot_bf16_kernel, dim3((BT * NH * 16 + 255) / 256), dim3(256), 0,
-                       ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
+    if (f16)
+      hipLaunchKernelGGL(attn_dot_bf16_kernel<true>, dim3((BT * NH * 16 + 255) / 256), dim3(256),
+                         0, ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
+    else
+      hipLaunchKernelGGL(attn_dot_bf16_kernel<false>, dim3((BT * NH * 16 + 255) / 256), dim3(256),
+                         0, ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
   }
   TT_TRY(tt_check_launch(ctx, "attn_dot_bf16"));
   const int nb = (T + 63) / 64;
   {
   // algorithmic backward: dP, dV, dK here, dQ in the next kernel (4 products)
   tt_prof_scope prof(ctx, "attn_dkdv_bf16_kernel", 3.0 * pass, 0.0);
-  hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
-                     (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
+  if (f16)
+    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<true>, dim3(B * NH * nb), dim3(256), 0, ctx->stream,
+                       T, NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv,
+                       nb, qb, ob);
+  else
+    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<false>, dim3(B * NH * nb), dim3(256), 0, ctx->stream,
+                       T, NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv,
+                       nb, qb, ob);
   }
   TT_TRY(tt_check_launch(ctx, "attn_dkdv_bf16"));
   tt_prof_scope prof(ctx, "attn_dq_bf16_kernel", pass, 0.0);
-  hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T, NH,
-                     (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb, qb, ob);
+  if (f16)
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<true>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
+                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb,
+                       qb, ob);
+  else
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<false>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
+                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb,
+                       qb, ob);
   return tt_check_launch(ctx, "attn_dq_bf16");
 }

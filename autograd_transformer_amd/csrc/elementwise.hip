@@ -74,12 +74,16 @@ __device__ __forceinline__ void adamw_one(float &w, float g, float &m, float &v,
   w = w - lr * (mh / (sqrtf(vh) + eps) + wd * w);
 }
 
+// skip (nullable, device): when nonzero the step is dropped (a loss-scaled
+// step whose gradients overflowed) -- every thread reads it and returns.
+template <bool F16>
 __global__ void __launch_bounds__(256) adamw_kernel(size_t n, float *__restrict__ w,
                                                     const float *__restrict__ g,
                                                     float *__restrict__ m, float *__restrict__ v,
                                                     bf16_t *__restrict__ wl, float lr, float b1,
                                                     float b2, float eps, float wd, float rbc1,
-                                                    float rbc2) {
+                                                    float rbc2, const int32_t *__restrict__ skip) {
+  if (skip && *skip) return;
   const size_t n4 = n / 4;
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
@@ -92,14 +96,14 @@ __global__ void __launch_bounds__(256) adamw_kernel(size_t n, float *__restrict_
     ((float4 *)w)[i] = W;
     ((float4 *)m)[i] = Mv;
     ((float4 *)v)[i] = Vv;
-    if (wl) ((uint2 *)wl)[i] = make_uint2(pack_bf2(W.x, W.y), pack_bf2(W.z, W.w));
+    if (wl) ((uint2 *)wl)[i] = make_uint2(lp_pack2<F16>(W.x, W.y), lp_pack2<F16>(W.z, W.w));
   }
   // tail
   for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
     float W = w[i], Mv = m[i], Vv = v[i];
     adamw_one(W, g[i], Mv, Vv, lr, b1, b2, eps, wd, rbc1, rbc2);
     w[i] = W; m[i] = Mv; v[i] = Vv;
-    if (wl) wl[i] = f2bf(W);
+    if (wl) wl[i] = lp_from<F16>(W);
   }
 }
 
@@ -117,10 +121,61 @@ __global__ void __launch_bounds__(256) fill_kernel(size_t n, float *__restrict__
   for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = val;
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(256) cast_kernel(size_t n, const float *__restrict__ s,
                                                    bf16_t *__restrict__ d) {
   const size_t stride = (size_t)gridDim.x * 256;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) d[i] = f2bf(s[i]);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    d[i] = lp_from<F16>(s[i]);
+}
+
+// Dynamic loss scaling (the C++/CUDA page, section 3.4).  The backward of a
+// scaled step leaves scale * gradient in g: divide it out and raise the
+// overflow flag if any entry is inf or NaN.
+__global__ void __launch_bounds__(256) unscale_check_kernel(size_t n, float *__restrict__ g,
+                                                            tt_loss_scale *__restrict__ st) {
+  const float r = 1.0f / st->scale;
+  const size_t n4 = n / 4, stride = (size_t)gridDim.x * 256;
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 v = ((float4 *)g)[i];
+    bad |= !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+    v.x *= r; v.y *= r; v.z *= r; v.w *= r;
+    ((float4 *)g)[i] = v;
+  }
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    bad |= !isfinite(g[i]);
+    g[i] *= r;
+  }
+  if (bad) atomicOr(&st->overflow, 1);
+}
+
+// After the (possibly skipped) update: halve the scale on overflow and
+// restart the clean-step count, else count the step and grow the scale by
+// `growth` once `interval` clean steps have passed; report the step's
+// overflow flag (nullable out) and clear it for the next step.
+__global__ void ls_update_kernel(tt_loss_scale *st, int interval, float growth, float backoff,
+                                 int32_t *out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int32_t ov = st->overflow;
+  if (ov) {
+    st->scale *= backoff;
+    st->good = 0;
+    st->skipped += 1;
+  } else if (++st->good >= interval) {
+    st->scale *= growth;
+    st->good = 0;
+  }
+  if (out) *out = ov;
+  st->overflow = 0;
+}
+
+__global__ void ls_set_kernel(tt_loss_scale *st, float scale) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  st->scale = scale;
+  st->good = 0;
+  st->overflow = 0;
+  st->skipped = 0;
 }
 
 // Batched bf16 transpose: descriptor i maps src [rows, cols] (row pitch cols)
@@ -267,11 +322,36 @@ int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v) {
   return tt_check_launch(ctx, "fill");
 }
 
-int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst) {
+int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst, bool f16) {
   if (n == 0) return TT_OK;
   tt_prof_scope prof(ctx, "cast_kernel", 0.0, 6.0 * n);
-  hipLaunchKernelGGL(cast_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src, dst);
+  if (f16)
+    hipLaunchKernelGGL(cast_kernel<true>, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src,
+                       dst);
+  else
+    hipLaunchKernelGGL(cast_kernel<false>, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, src,
+                       dst);
   return tt_check_launch(ctx, "cast");
+}
+
+int tt_unscale_check(tt_ctx *ctx, float *g, size_t n, tt_loss_scale *st) {
+  if (n == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "unscale_check_kernel", 0.0, 8.0 * n);
+  hipLaunchKernelGGL(unscale_check_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, g,
+                     st);
+  return tt_check_launch(ctx, "unscale_check");
+}
+
+int tt_loss_scale_update(tt_ctx *ctx, tt_loss_scale *st, int interval, float growth,
+                         float backoff, int32_t *out) {
+  hipLaunchKernelGGL(ls_update_kernel, dim3(1), dim3(64), 0, ctx->stream, st, interval, growth,
+                     backoff, out);
+  return tt_check_launch(ctx, "loss_scale_update");
+}
+
+int tt_loss_scale_set(tt_ctx *ctx, tt_loss_scale *st, float scale) {
+  hipLaunchKernelGGL(ls_set_kernel, dim3(1), dim3(64), 0, ctx->stream, st, scale);
+  return tt_check_launch(ctx, "loss_scale_set");
 }
 
 int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles,
@@ -284,14 +364,19 @@ int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tile
 }
 
 int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,
-                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t) {
+                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t,
+                  bool f16, const int32_t *skip) {
   if (n == 0) return TT_OK;
   const float rbc1 = (float)(1.0 / (1.0 - pow((double)beta1, (double)t)));
   const float rbc2 = (float)(1.0 / (1.0 - pow((double)beta2, (double)t)));
   // w, g, m, v read; w, m, v written; optional bf16 copy: 28 (30) bytes per parameter
   tt_prof_scope prof(ctx, "adamw_kernel", 0.0, (28.0 + (w_lowp ? 2.0 : 0.0)) * n);
-  hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, w, g, m, v,
-                     w_lowp, lr, beta1, beta2, eps, wd, rbc1, rbc2);
+  if (f16)
+    hipLaunchKernelGGL(adamw_kernel<true>, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, w,
+                       g, m, v, w_lowp, lr, beta1, beta2, eps, wd, rbc1, rbc2, skip);
+  else
+    hipLaunchKernelGGL(adamw_kernel<false>, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, w,
+                       g, m, v, w_lowp, lr, beta1, beta2, eps, wd, rbc1, rbc2, skip);
   return tt_check_launch(ctx, "adamw");
 }
 
@@ -379,6 +464,9 @@ extern "C" int tt_gelu_fwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, v
   if (mode == TT_BF16)
     hipLaunchKernelGGL(gelu_fwd_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
                        (const bf16_t *)x, (bf16_t *)y);
+  else if (mode == TT_FP16)
+    hipLaunchKernelGGL(gelu_fwd_kernel<f16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const f16_t *)x, (f16_t *)y);
   else
     hipLaunchKernelGGL(gelu_fwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
                        (const float *)x, (float *)y);
@@ -393,6 +481,9 @@ extern "C" int tt_gelu_bwd(tt_ctx *ctx, tt_mode mode, size_t n, const void *x, c
   if (mode == TT_BF16)
     hipLaunchKernelGGL(gelu_bwd_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
                        (const bf16_t *)x, (const bf16_t *)dy, (bf16_t *)dx);
+  else if (mode == TT_FP16)
+    hipLaunchKernelGGL(gelu_bwd_kernel<f16_t>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
+                       (const f16_t *)x, (const f16_t *)dy, (f16_t *)dx);
   else
     hipLaunchKernelGGL(gelu_bwd_kernel<float>, dim3(grid_for(n)), dim3(256), 0, ctx->stream, n,
                        (const float *)x, (const float *)dy, (float *)dx);

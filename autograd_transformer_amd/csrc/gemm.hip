@@ -378,7 +378,7 @@ int dispatch_layout(tt_ctx *ctx, const GemmArgs &g, int split, bool vec) {
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
   TT_REQUIRE(ctx, g.M > 0 && g.N > 0 && g.K > 0, "gemm: empty shape %d %d %d", g.M, g.N, g.K);
   TT_REQUIRE(ctx, g.A && g.B && g.out, "gemm: NULL operand");
-  const int esz = mode == TT_BF16 ? 2 : 4;
+  const int esz = tt_lowp(mode) ? 2 : 4;
   const int vecn = 16 / esz;
   bool vec = tt_aligned16(g.A) && tt_aligned16(g.B) && (g.lda % vecn == 0) &&
              (g.ldb % vecn == 0);
@@ -394,7 +394,10 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
   }
   // Column sums of the output (g.colsum) are fused into the epilogue of the
   // direct-to-LDS bf16 kernel; every other path sums the stored output after.
-  const bool fast = mode == TT_BF16 && vec && tt_gemm_bf16_ok(g);
+  const bool fast = tt_lowp(mode) && vec && tt_gemm_bf16_ok(g);
+  if (mode == TT_FP16 && !fast)
+    return tt_set_error(ctx, TT_EUNSUPPORTED,
+                        "gemm(fp16): operands need 16-byte aligned rows (lda, ldb multiples of 8)");
   if (g.epi == EPI_ACCUM && g.overwrite && !fast) {
     // the generic kernels accumulate with atomics: clear the output first
     TT_REQUIRE(ctx, g.ldo == g.N, "gemm: overwrite needs a dense output");
@@ -402,6 +405,7 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
   }
   const bool fused_sum = fast && g.epi != EPI_ACCUM && g.a_kmajor && g.b_kmajor;
   GemmArgs h = g;
+  h.f16 = mode == TT_FP16;
   if (!fused_sum) h.colsum = nullptr;
   if (fast)
     TT_TRY(tt_gemm_bf16(ctx, h));
@@ -411,7 +415,7 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
     TT_TRY((dispatch_layout<float, 128, 128, 32, 2, 2>(ctx, h, split, vec)));
   if (g.colsum && !fused_sum) {
     TT_REQUIRE(ctx, g.epi == EPI_STORE || g.epi == EPI_GELU_BWD, "gemm: column sums of this epilogue");
-    return tt_colsum(ctx, g.out_bf16, g.M, g.N, g.ldo, g.out, g.colsum);
+    return tt_colsum(ctx, g.out_bf16 ? mode : TT_F32, g.M, g.N, g.ldo, g.out, g.colsum);
   }
   return TT_OK;
 }

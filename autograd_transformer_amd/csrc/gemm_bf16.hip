@@ -113,7 +113,7 @@ struct Cfg {
 // Occupancy target: two waves per SIMD (two 4-wave or one 8-wave workgroup
 // per CU, capping registers at 256 per lane), except the 256x256 tile whose
 // four waves each hold a 128x128 accumulator (one wave per SIMD).
-template <int BM, int BN, int WM, int WN, bool A_KM, bool B_KM>
+template <int BM, int BN, int WM, int WN, bool A_KM, bool B_KM, bool F16 = false>
 __global__ void __launch_bounds__(64 * WM * WN, (WM * WN == 4 && BM * BN < 256 * 256) ? 2 : 1)
 gemm_bf16_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, A_KM, B_KM>;
@@ -159,7 +159,7 @@ gemm_bf16_kernel(GemmParams p) {
         bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = lp_mfma<F16>(fa, fb[j], acc[i][j]);
       }
     }
   };
@@ -239,7 +239,7 @@ gemm_bf16_kernel(GemmParams p) {
       if (m >= p.M || n >= nv) continue;
       float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
       v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
-      epilogue4(p, m, n, v, nv - n);
+      epilogue4<F16>(p, m, n, v, nv - n);
     }
   }
 }
@@ -265,19 +265,22 @@ int launch(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   split = (kb + per - 1) / per;
   p.out_zstride = out_zstride;
   dim3 grid(p.tiles_m * p.tiles_n, 1, split);
-  static char names[4][80];
   const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0);
-  if (!names[li][0])
-    snprintf(names[li], sizeof names[li], "gemm_bf16_kernel<%d, %d, %d, %d, %s, %s>", BM, BN, WM, WN,
-             g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
-  tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
-#define TT_L(AK, BKM)                                                                          \
-  if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                 \
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM>), grid, dim3(64 * WM * WN), 0, \
-                       ctx->stream, p);                                                        \
+  static char names[8][80];
+  const int ni = li + (g.f16 ? 4 : 0);
+  if (!names[ni][0])
+    snprintf(names[ni], sizeof names[ni], "gemm_bf16_kernel<%d, %d, %d, %d, %s, %s, %s>", BM, BN, WM,
+             WN, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false",
+             g.f16 ? "true" : "false");
+  tt_prof_scope prof(ctx, names[ni], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
+#define TT_L(AK, BKM, H)                                                                       \
+  if (g.a_kmajor == AK && g.b_kmajor == BKM && g.f16 == H) {                                   \
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM, H>), grid, dim3(64 * WM * WN), \
+                       0, ctx->stream, p);                                                     \
     return tt_check_launch(ctx, "gemm_bf16");                                                  \
   }
-  TT_L(true, true) TT_L(true, false) TT_L(false, true) TT_L(false, false)
+  TT_L(true, true, false) TT_L(true, false, false) TT_L(false, true, false) TT_L(false, false, false)
+  TT_L(true, true, true) TT_L(true, false, true) TT_L(false, true, true) TT_L(false, false, true)
 #undef TT_L
   return TT_EINVAL;
 }
@@ -396,7 +399,7 @@ struct Cfg3 {
 // residual to 4 consecutive columns with row-coalesced accesses; optional
 // column sums of the stored values (bias gradients).  The caller has passed
 // a barrier after the last LDS read of the main loop.
-template <class C>
+template <class C, bool F16>
 __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM][C::FN], char *smem_raw,
                                             int m0, int n0) {
   constexpr int NT = C::NT, FM = C::FM, FN = C::FN, BN = C::BN_, WM = C::WM_, WN = C::WN_;
@@ -441,7 +444,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
           if (n + 2 < nv) v.z += p.bias[n + 2];
           if (n + 3 < nv) v.w += p.bias[n + 3];
         }
-        const float4 st = epilogue4(p, m, n, v, nv - n);
+        const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
         if (p.colsum) *cp = st;
       }
       if (p.colsum) {
@@ -486,7 +489,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
       if (m >= p.M || n >= nv) continue;
       float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
       v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
-      const float4 st = epilogue4(p, m, n, v, nv - n);
+      const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
       csum.x += st.x; csum.y += st.y; csum.z += st.z; csum.w += st.w;
     }
   }
@@ -506,7 +509,8 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
   }
 }
 
-template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM, bool GROUP = false>
+template <int BM, int BN, int BKV, int WM, int WN, int NS, bool A_KM, bool B_KM, bool GROUP = false,
+          bool F16 = false>
 __global__ void __launch_bounds__(64 * WM * WN,
                                   (Cfg3<BM, BN, BKV, WM, WN, NS, A_KM, B_KM>::WAVES_PER_EU))
 gemm_bf16_v3_kernel(GemmParams p) {
@@ -594,13 +598,13 @@ gemm_bf16_v3_kernel(GemmParams p) {
           const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = lp_mfma<F16>(fa, fb[j], acc[i][j]);
         }
       }
     }
   }
   __syncthreads();
-  v3_epilogue<C>(p, acc, smem_raw, m0, n0);
+  v3_epilogue<C, F16>(p, acc, smem_raw, m0, n0);
 }
 
 template <int BM, int BN, int BKV, int WM, int WN, int NS>
@@ -624,23 +628,27 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   p.k_chunk = per * BKV;
   split = (kb + per - 1) / per;
   dim3 grid(p.tiles_m * p.tiles_n, 1, split);
-  static char names[4][96];
-  const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0);
+  static char names[8][112];
+  const int li = (g.a_kmajor ? 2 : 0) + (g.b_kmajor ? 1 : 0) + (g.f16 ? 4 : 0);
   if (!names[li][0])
-    snprintf(names[li], sizeof names[li], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s, false>",
-             BM, BN, BKV, WM, WN, NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false");
+    snprintf(names[li], sizeof names[li],
+             "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, %s, %s, false, %s>", BM, BN, BKV, WM, WN,
+             NS, g.a_kmajor ? "true" : "false", g.b_kmajor ? "true" : "false",
+             g.f16 ? "true" : "false");
   tt_prof_scope prof(ctx, names[li], 2.0 * g.M * g.N * g.K, gemm_bytes(g));
-#define TT_L3(AK, BKM)                                                                          \
-  if (g.a_kmajor == AK && g.b_kmajor == BKM) {                                                  \
+#define TT_L3(AK, BKM, H)                                                                       \
+  if (g.a_kmajor == AK && g.b_kmajor == BKM && g.f16 == H) {                                    \
     if constexpr (DOp<BM, BKV, AK>::VALID && DOp<BN, BKV, BKM>::VALID) {                        \
-      hipLaunchKernelGGL((gemm_bf16_v3_kernel<BM, BN, BKV, WM, WN, NS, AK, BKM>), grid,         \
+      hipLaunchKernelGGL((gemm_bf16_v3_kernel<BM, BN, BKV, WM, WN, NS, AK, BKM, false, H>), grid, \
                          dim3(64 * WM * WN), 0, ctx->stream, p);                                \
       return tt_check_launch(ctx, "gemm_bf16_v3");                                              \
     } else {                                                                                    \
       return tt_set_error(ctx, TT_EUNSUPPORTED, "gemm_bf16_v3: tile/layout not supported");    \
     }                                                                                           \
   }
-  TT_L3(true, true) TT_L3(true, false) TT_L3(false, true) TT_L3(false, false)
+  TT_L3(true, true, false) TT_L3(true, false, false) TT_L3(false, true, false)
+  TT_L3(false, false, false) TT_L3(true, true, true) TT_L3(true, false, true)
+  TT_L3(false, true, true) TT_L3(false, false, true)
 #undef TT_L3
   return TT_EINVAL;
 }
@@ -786,7 +794,7 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 // least 256 of K per split.
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   const long tiles = (long)((g.M + 255) / 256) * ((g.N + 127) / 128);
-  if (g.M <= 16 && g.a_kmajor && g.b_kmajor && !g.colsum && g.K % 8 == 0 &&
+  if (g.M <= 16 && !g.f16 && g.a_kmajor && g.b_kmajor && !g.colsum && g.K % 8 == 0 &&
       (g.epi == EPI_STORE || g.epi == EPI_GELU || g.epi == EPI_RESID))
     return launch_skinny(ctx, g);
   if (g.epi != EPI_ACCUM) {
@@ -860,7 +868,7 @@ constexpr int GBM = GT::bm, GBN = GT::bn, GBK = GT::bk;
 }
 
 int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max,
-                       GemmGroup *out) {
+                       GemmGroup *out, bool f16) {
   TT_REQUIRE(ctx, entries && out && n > 0 && k_max > 0, "gemm_group: bad arguments");
   std::vector<GemmGroupEntry> t(entries, entries + n);
   int tiles = 0;
@@ -911,6 +919,7 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
   out->mn2 = mn2;
   out->bytes_k = bytes_k;
   out->bytes_out = bytes_out;
+  out->f16 = f16;
   return TT_OK;
 }
 
@@ -924,12 +933,19 @@ int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K) {
   p.raster_n = 0;
   p.group = g.table;
   p.group_map = g.map;
-  static char name[96];
+  static char names[2][112];
+  char *name = names[g.f16 ? 1 : 0];
   if (!name[0])
-    snprintf(name, sizeof name, "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, false, false, true>",
-             GT::bm, GT::bn, GT::bk, GT::wm, GT::wn, GT::ns);
+    snprintf(name, sizeof names[0], "gemm_bf16_v3_kernel<%d, %d, %d, %d, %d, %d, false, false, true, %s>",
+             GT::bm, GT::bn, GT::bk, GT::wm, GT::wn, GT::ns, g.f16 ? "true" : "false");
   tt_prof_scope prof(ctx, name, g.mn2 * K, g.bytes_k * K + g.bytes_out);
-  hipLaunchKernelGGL((gemm_bf16_v3_kernel<GBM, GBN, GBK, GT::wm, GT::wn, GT::ns, false, false, true>),
-                     dim3(g.grid), dim3(64 * GT::wm * GT::wn), 0, ctx->stream, p);
+  if (g.f16)
+    hipLaunchKernelGGL(
+        (gemm_bf16_v3_kernel<GBM, GBN, GBK, GT::wm, GT::wn, GT::ns, false, false, true, true>),
+        dim3(g.grid), dim3(64 * GT::wm * GT::wn), 0, ctx->stream, p);
+  else
+    hipLaunchKernelGGL(
+        (gemm_bf16_v3_kernel<GBM, GBN, GBK, GT::wm, GT::wn, GT::ns, false, false, true, false>),
+        dim3(g.grid), dim3(64 * GT::wm * GT::wn), 0, ctx->stream, p);
   return tt_check_launch(ctx, "gemm_group");
 }

@@ -26,9 +26,11 @@ struct GemmParams {
   const uint16_t *group_map;     // grouped launch: workgroup -> table entry
 };
 
+// out_bf16: the output is 16-bit (bf16, or binary16 when F16).
+template <bool F16 = false>
 __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
   if (out_bf16)
-    ((bf16_t *)out)[(size_t)m * ldo + n] = f2bf(v);
+    ((bf16_t *)out)[(size_t)m * ldo + n] = lp_from<F16>(v);
   else
     ((float *)out)[(size_t)m * ldo + n] = v;
 }
@@ -39,13 +41,16 @@ __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int 
 // (p.vec_out); otherwise elements are handled one by one.  Returns the values
 // as stored for EPI_STORE / EPI_GELU_BWD (bf16-rounded when the output is
 // bf16, 0 past cnt), for column sums.
+template <bool F16>
 __device__ __forceinline__ float4 round_stored(const GemmParams &p, const float *a, int lim) {
   float r[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] = q < lim ? (p.out_bf16 ? bf2f(f2bf(a[q])) : a[q]) : 0.f;
+  for (int q = 0; q < 4; ++q)
+    r[q] = q < lim ? (p.out_bf16 ? lp_to<F16>(lp_from<F16>(a[q])) : a[q]) : 0.f;
   return make_float4(r[0], r[1], r[2], r[3]);
 }
 
+template <bool F16 = false>
 __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, float4 v, int cnt) {
   const bool full = cnt >= 4 && p.vec_out;
   float a[4] = {v.x, v.y, v.z, v.w};
@@ -57,9 +62,9 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
         if (p.aux) {
           if (full && p.out_bf16)
             *(uint2 *)((bf16_t *)p.aux + (size_t)m * p.ldx + n) =
-                make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+                make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
           else
-            for (int q = 0; q < lim; ++q) store_out(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
+            for (int q = 0; q < lim; ++q) store_out<F16>(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) a[q] = gelu_f(a[q]);
@@ -67,13 +72,13 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
       if (full) {
         if (p.out_bf16)
           *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-              make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+              make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
         else
           *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) = make_float4(a[0], a[1], a[2], a[3]);
       } else {
-        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+        for (int q = 0; q < lim; ++q) store_out<F16>(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
       }
-      return round_stored(p, a, lim);
+      return round_stored<F16>(p, a, lim);
     }
     case EPI_RESID: {
       const float *rp = p.resid + (size_t)m * p.ldr + n;
@@ -92,10 +97,10 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
         const bf16_t *hp = (const bf16_t *)p.aux + (size_t)m * p.ldx + n;
         if (full) {
           uint2 u = *(const uint2 *)hp;
-          h[0] = __uint_as_float(u.x << 16); h[1] = __uint_as_float(u.x & 0xffff0000u);
-          h[2] = __uint_as_float(u.y << 16); h[3] = __uint_as_float(u.y & 0xffff0000u);
+          h[0] = lp_lo<F16>(u.x); h[1] = lp_hi<F16>(u.x);
+          h[2] = lp_lo<F16>(u.y); h[3] = lp_hi<F16>(u.y);
         } else {
-          for (int q = 0; q < 4; ++q) h[q] = q < lim ? bf2f(hp[q]) : 0.f;
+          for (int q = 0; q < 4; ++q) h[q] = q < lim ? lp_to<F16>(hp[q]) : 0.f;
         }
       } else {
         const float *hp = (const float *)p.aux + (size_t)m * p.ldx + n;
@@ -105,10 +110,10 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
       for (int q = 0; q < 4; ++q) a[q] *= gelu_grad_f(h[q]);
       if (full && p.out_bf16)
         *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-            make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+            make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
       else
-        for (int q = 0; q < lim; ++q) store_out(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
-      return round_stored(p, a, lim);
+        for (int q = 0; q < lim; ++q) store_out<F16>(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
+      return round_stored<F16>(p, a, lim);
     }
     case EPI_ACCUM: {
       float *op = (float *)p.out + (size_t)m * p.ldo + n;

@@ -10,7 +10,7 @@ namespace {
 // LayerNorm forward — tinytorch page §4 (subtract the mean, divide by the
 // standard deviation, scale by the weight, add the bias); biased variance,
 // eps inside the square root.  Two-pass statistics from registers.
-template <bool OUT_BF16, int LN_MAXV>
+template <bool OUT_BF16, int LN_MAXV, bool F16 = false>
 __global__ void __launch_bounds__(256) layernorm_fwd_kernel(int N, int C, float eps,
                                                             const float *__restrict__ x,
                                                             const float *__restrict__ g,
@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(int N, int C, float 
       float o2 = (v[i].z - mean) * rstd * gg.z + bb.z;
       float o3 = (v[i].w - mean) * rstd * gg.w + bb.w;
       if (OUT_BF16) {
-        uint2 pk = make_uint2(pack_bf2(o0, o1), pack_bf2(o2, o3));
+        uint2 pk = make_uint2(lp_pack2<F16>(o0, o1), lp_pack2<F16>(o2, o3));
         ((uint2 *)((bf16_t *)y + (size_t)row * C))[c] = pk;
       } else {
         ((float4 *)((float *)y + (size_t)row * C))[c] = make_float4(o0, o1, o2, o3);
@@ -101,7 +101,7 @@ __device__ __forceinline__ float4 ln_load4(__amdgpu_buffer_rsrc_t r, uint32_t of
 __host__ __device__ constexpr int lnb_waves(int nv) { return nv <= 4 ? 4 : (nv <= 8 ? 2 : 1); }
 __host__ __device__ constexpr int lnb_rpw(int nv) { return nv <= 3 ? 2 : 1; }
 
-template <int NV>
+template <int NV, bool F16 = false>
 __global__ void __launch_bounds__(64 * lnb_waves(NV)) layernorm_bwd_kernel(
     int N, int C, const float *__restrict__ x, const float *__restrict__ mean,
     const float *__restrict__ rstd, const float *__restrict__ gamma, const float *__restrict__ dy,
@@ -178,10 +178,9 @@ __global__ void __launch_bounds__(64 * lnb_waves(NV)) layernorm_bwd_kernel(
         o.w = rs[r] * (gg[i].w - m1 - xh[i].w * m2) + rv[r][i].w;
         ((float4 *)dx)[(size_t)row * nv + c] = o;
         if (dx_bf16) {
-          const uint32_t lo = pack_bf2(o.x, o.y), hi = pack_bf2(o.z, o.w);
+          const uint32_t lo = lp_pack2<F16>(o.x, o.y), hi = lp_pack2<F16>(o.z, o.w);
           ((uint2 *)dx_bf16)[(size_t)row * nv + c] = make_uint2(lo, hi);
-          o = make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+          o = make_float4(lp_lo<F16>(lo), lp_hi<F16>(lo), lp_lo<F16>(hi), lp_hi<F16>(hi));
         }
         ps[i].x += o.x; ps[i].y += o.y; ps[i].z += o.z; ps[i].w += o.w;
       }
@@ -249,7 +248,7 @@ __global__ void __launch_bounds__(256) layernorm_bwd_reduce_kernel(int G, int C,
 // 16-byte aligned rows (host-checked).
 constexpr int CS_ROWS = 128;   // rows per workgroup
 
-template <bool BF16>
+template <bool BF16, bool F16 = false>
 __global__ void __launch_bounds__(256) colsum_vec_kernel(int M, int N, int ld,
                                                          const void *__restrict__ src,
                                                          float *__restrict__ out) {
@@ -269,8 +268,8 @@ __global__ void __launch_bounds__(256) colsum_vec_kernel(int M, int N, int ld,
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += __uint_as_float(w[q] << 16);
-          acc[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+          acc[2 * q] += lp_lo<F16>(w[q]);
+          acc[2 * q + 1] += lp_hi<F16>(w[q]);
         }
       } else {
         const float4 f = *(const float4 *)((const float *)src + (size_t)m * ld + c0);
@@ -293,7 +292,7 @@ __global__ void __launch_bounds__(256) colsum_vec_kernel(int M, int N, int ld,
 
 // Column sums out[n] += sum_m src[m, n] (bias gradients).  Each block sums a
 // strip of 64 columns over a slice of rows, then one atomic per column.
-template <bool BF16>
+template <bool BF16, bool F16 = false>
 __global__ void __launch_bounds__(256) colsum_kernel(int M, int N, int ld, int rows_per_block,
                                                      const void *__restrict__ src,
                                                      float *__restrict__ out) {
@@ -304,7 +303,7 @@ __global__ void __launch_bounds__(256) colsum_kernel(int M, int N, int ld, int r
   float s = 0.f;
   if (col < N) {
     for (int m = m0 + part; m < m1; m += 4) {
-      s += BF16 ? bf2f(((const bf16_t *)src)[(size_t)m * ld + col])
+      s += BF16 ? lp_to<F16>(((const bf16_t *)src)[(size_t)m * ld + col])
                 : ((const float *)src)[(size_t)m * ld + col];
     }
   }
@@ -323,11 +322,13 @@ __global__ void __launch_bounds__(256) colsum_kernel(int M, int N, int ld, int r
 // the online form of the max-subtracted softmax — and merges them; pass 2
 // overwrites the row with dz = (exp(z - lse) - [v == y]) * scale and zeroes
 // the padding columns.
-template <bool BF16>
+template <bool BF16, bool F16 = false>
 __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *logits,
                                                  const int32_t *__restrict__ targets,
                                                  float *__restrict__ row_loss, float scale,
+                                                 const float *__restrict__ scale_dev,
                                                  int32_t *flags) {
+  if (scale_dev) scale *= *scale_dev;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int y = targets[row];
@@ -343,8 +344,8 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
       float v[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(w[q] << 16);
-        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        v[2 * q] = lp_lo<F16>(w[q]);
+        v[2 * q + 1] = lp_hi<F16>(w[q]);
       }
       float mx = v[0];
 #pragma unroll
@@ -357,7 +358,7 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
       m = nm;
     }
     for (int i = (nv8 << 3) + tid; i < V; i += 256) {
-      float v = bf2f(z[i]);
+      float v = lp_to<F16>(z[i]);
       float nm = fmaxf(m, v);
       s = s * __expf(m - nm) + __expf(v - nm);
       m = nm;
@@ -386,7 +387,7 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
   if (tid == 0) {
     float zy;
     if (BF16)
-      zy = y_ok ? bf2f(((const bf16_t *)logits)[(size_t)row * ld + y]) : NAN;
+      zy = y_ok ? lp_to<F16>(((const bf16_t *)logits)[(size_t)row * ld + y]) : NAN;
     else
       zy = y_ok ? ((const float *)logits)[(size_t)row * ld + y] : NAN;
     row_loss[row] = lse - zy;
@@ -403,10 +404,10 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         int c0 = i * 8 + 2 * q, c1 = c0 + 1;
-        float v0 = __uint_as_float(w[q] << 16), v1 = __uint_as_float(w[q] & 0xffff0000u);
+        float v0 = lp_lo<F16>(w[q]), v1 = lp_hi<F16>(w[q]);
         float d0 = c0 < V ? (__expf(v0 - lse) - (c0 == y ? 1.f : 0.f)) * scale : 0.f;
         float d1 = c1 < V ? (__expf(v1 - lse) - (c1 == y ? 1.f : 0.f)) * scale : 0.f;
-        o[q] = pack_bf2(d0, d1);
+        o[q] = lp_pack2<F16>(d0, d1);
       }
       ((uint4 *)z)[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -441,10 +442,14 @@ __device__ __forceinline__ float ce_block_reduce(float v, bool is_max, float *re
   return r;
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld, bf16_t *logits,
                                                             const int32_t *__restrict__ targets,
                                                             float *__restrict__ row_loss,
-                                                            float scale, int32_t *flags) {
+                                                            float scale,
+                                                            const float *__restrict__ scale_dev,
+                                                            int32_t *flags) {
+  if (scale_dev) scale *= *scale_dev;
   __shared__ float red[CE_THREADS / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int y = targets[row];
@@ -461,10 +466,10 @@ __global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld
         uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, idx < nv8 ? (uint32_t)idx * 16u : 0x7ffffff0u,
                                                      0, 0));
   }
-  const float zy = (tid == 0 && y_ok) ? bf2f(z[y]) : 0.f;   // read before any thread writes
+  const float zy = (tid == 0 && y_ok) ? lp_to<F16>(z[y]) : 0.f;   // read before any thread writes
   auto val = [&](int i, int q) {
     const uint32_t w = (&v[i].x)[q >> 1];
-    return __uint_as_float((q & 1) ? (w & 0xffff0000u) : (w << 16));
+    return (q & 1) ? lp_hi<F16>(w) : lp_lo<F16>(w);
   };
   float m = -INFINITY;
 #pragma unroll
@@ -490,7 +495,7 @@ __global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld
       const int c0 = idx * 8 + 2 * q, c1 = c0 + 1;
       const float d0 = c0 < V ? (__expf(val(i, 2 * q) - lse) - (c0 == y ? 1.f : 0.f)) * scale : 0.f;
       const float d1 = c1 < V ? (__expf(val(i, 2 * q + 1) - lse) - (c1 == y ? 1.f : 0.f)) * scale : 0.f;
-      o[q] = pack_bf2(d0, d1);
+      o[q] = lp_pack2<F16>(d0, d1);
     }
     ((uint4 *)z)[idx] = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -522,12 +527,15 @@ int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, co
   dim3 grid((N + 3) / 4);
   const int nv = (C / 4 + 63) / 64;
   tt_prof_scope prof(ctx, "layernorm_fwd_kernel", 0.0,
-                     (double)N * C * (4.0 + (mode == TT_BF16 ? 2.0 : 4.0)) + 8.0 * C + 8.0 * N);
+                     (double)N * C * (4.0 + (tt_lowp(mode) ? 2.0 : 4.0)) + 8.0 * C + 8.0 * N);
 #define TT_LNF(NV)                                                                              \
   if (nv <= NV) {                                                                               \
     if (mode == TT_BF16)                                                                        \
       hipLaunchKernelGGL((layernorm_fwd_kernel<true, NV>), grid, dim3(256), 0, ctx->stream, N, C, \
                          eps, x, g, b, y, mean, rstd);                                          \
+    else if (mode == TT_FP16)                                                                   \
+      hipLaunchKernelGGL((layernorm_fwd_kernel<true, NV, true>), grid, dim3(256), 0, ctx->stream, \
+                         N, C, eps, x, g, b, y, mean, rstd);                                    \
     else                                                                                        \
       hipLaunchKernelGGL((layernorm_fwd_kernel<false, NV>), grid, dim3(256), 0, ctx->stream, N,   \
                          C, eps, x, g, b, y, mean, rstd);                                       \
@@ -542,7 +550,6 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                           const float *mean, const float *rstd, const float *g, const float *dy,
                           const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
                           float *dsum) {
-  (void)mode;
   TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
   TT_REQUIRE(ctx, x && mean && rstd && g && dy && dx, "layernorm_bwd: NULL pointer");
   if (N == 0) return TT_OK;
@@ -560,9 +567,14 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                            8.0 * N + 12.0 * G * C);
 #define TT_LNB(NV)                                                                        \
     if (nv <= NV) {                                                                       \
-      hipLaunchKernelGGL((layernorm_bwd_kernel<NV>), dim3(G), dim3(64 * lnb_waves(NV)), 0, \
-                         ctx->stream, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,      \
-                         (float *)part);                                                  \
+      if (mode == TT_FP16)                                                              \
+        hipLaunchKernelGGL((layernorm_bwd_kernel<NV, true>), dim3(G), dim3(64 * lnb_waves(NV)), \
+                           0, ctx->stream, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16, \
+                           (float *)part);                                                \
+      else                                                                                \
+        hipLaunchKernelGGL((layernorm_bwd_kernel<NV>), dim3(G), dim3(64 * lnb_waves(NV)), 0, \
+                           ctx->stream, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,    \
+                           (float *)part);                                                \
     } else
     TT_LNB(1) TT_LNB(2) TT_LNB(3) TT_LNB(4) TT_LNB(8) TT_LNB(16) return TT_EUNSUPPORTED;
 #undef TT_LNB
@@ -576,13 +588,17 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
   return tt_check_launch(ctx, "layernorm_bwd_reduce");
 }
 
-int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out) {
+int tt_colsum(tt_ctx *ctx, int fmt, int M, int N, int ld, const void *src, float *out) {
   if (M == 0 || N == 0) return TT_OK;
+  const bool src_bf16 = tt_lowp(fmt), f16 = fmt == TT_FP16;
   tt_prof_scope prof(ctx, "colsum_kernel", 0.0, (double)M * N * (src_bf16 ? 2.0 : 4.0) + 4.0 * N);
   const int vec = src_bf16 ? 8 : 4;
   if (tt_aligned16(src) && N % vec == 0 && ld % vec == 0) {
     dim3 grid((N / vec + 31) / 32, (M + CS_ROWS - 1) / CS_ROWS);
-    if (src_bf16)
+    if (f16)
+      hipLaunchKernelGGL((colsum_vec_kernel<true, true>), grid, dim3(256), 0, ctx->stream, M, N, ld,
+                         src, out);
+    else if (src_bf16)
       hipLaunchKernelGGL(colsum_vec_kernel<true>, grid, dim3(256), 0, ctx->stream, M, N, ld, src, out);
     else
       hipLaunchKernelGGL(colsum_vec_kernel<false>, grid, dim3(256), 0, ctx->stream, M, N, ld, src, out);
@@ -593,7 +609,10 @@ int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src,
   while (colblocks * rowsplit < 1024 && rowsplit * 64 < M) rowsplit *= 2;
   int rpb = (M + rowsplit - 1) / rowsplit;
   dim3 grid(colblocks, (M + rpb - 1) / rpb);
-  if (src_bf16)
+  if (f16)
+    hipLaunchKernelGGL((colsum_kernel<true, true>), grid, dim3(256), 0, ctx->stream, M, N, ld, rpb,
+                       src, out);
+  else if (src_bf16)
     hipLaunchKernelGGL(colsum_kernel<true>, grid, dim3(256), 0, ctx->stream, M, N, ld, rpb, src, out);
   else
     hipLaunchKernelGGL(colsum_kernel<false>, grid, dim3(256), 0, ctx->stream, M, N, ld, rpb, src, out);
@@ -601,23 +620,35 @@ int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src,
 }
 
 int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
-               const int32_t *targets, float *per_row_loss, float *loss, float grad_scale) {
+               const int32_t *targets, float *per_row_loss, float *loss, float grad_scale,
+               const float *scale_dev) {
   TT_REQUIRE(ctx, N > 0 && V > 0 && ld >= V, "ce: bad shape N=%d V=%d ld=%d", N, V, ld);
   TT_REQUIRE(ctx, logits && targets && per_row_loss && loss, "ce: NULL pointer");
   {
   // algorithmic: one read and one write of the logits
-  tt_prof_scope prof(ctx, "ce_kernel", 0.0, 2.0 * N * (double)ld * (mode == TT_BF16 ? 2.0 : 4.0) + 8.0 * N);
-  if (mode == TT_BF16) {
-    TT_REQUIRE(ctx, ld % 8 == 0 && tt_aligned16(logits), "ce(bf16): ld %% 8 and 16-byte alignment required");
-    if (ld <= CE_VPT * 8 * CE_THREADS)
-      hipLaunchKernelGGL(ce_reg_kernel, dim3(N), dim3(CE_THREADS), 0, ctx->stream, N, V, ld,
-                         (bf16_t *)logits, targets, per_row_loss, grad_scale, ctx->dev_flags);
-    else
+  tt_prof_scope prof(ctx, "ce_kernel", 0.0, 2.0 * N * (double)ld * (tt_lowp(mode) ? 2.0 : 4.0) + 8.0 * N);
+  if (tt_lowp(mode)) {
+    TT_REQUIRE(ctx, ld % 8 == 0 && tt_aligned16(logits), "ce(16-bit): ld %% 8 and 16-byte alignment required");
+    const bool f16 = mode == TT_FP16;
+    if (ld <= CE_VPT * 8 * CE_THREADS) {
+      if (f16)
+        hipLaunchKernelGGL(ce_reg_kernel<true>, dim3(N), dim3(CE_THREADS), 0, ctx->stream, N, V, ld,
+                           (bf16_t *)logits, targets, per_row_loss, grad_scale, scale_dev,
+                           ctx->dev_flags);
+      else
+        hipLaunchKernelGGL(ce_reg_kernel<false>, dim3(N), dim3(CE_THREADS), 0, ctx->stream, N, V, ld,
+                           (bf16_t *)logits, targets, per_row_loss, grad_scale, scale_dev,
+                           ctx->dev_flags);
+    } else if (f16) {
+      hipLaunchKernelGGL((ce_kernel<true, true>), dim3(N), dim3(256), 0, ctx->stream, N, V, ld,
+                         logits, targets, per_row_loss, grad_scale, scale_dev, ctx->dev_flags);
+    } else {
       hipLaunchKernelGGL(ce_kernel<true>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
-                         targets, per_row_loss, grad_scale, ctx->dev_flags);
+                         targets, per_row_loss, grad_scale, scale_dev, ctx->dev_flags);
+    }
   } else {
     hipLaunchKernelGGL(ce_kernel<false>, dim3(N), dim3(256), 0, ctx->stream, N, V, ld, logits,
-                       targets, per_row_loss, grad_scale, ctx->dev_flags);
+                       targets, per_row_loss, grad_scale, scale_dev, ctx->dev_flags);
   }
   }
   TT_TRY(tt_check_launch(ctx, "ce"));

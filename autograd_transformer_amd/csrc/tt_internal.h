@@ -100,6 +100,56 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 __device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack_bf2(f, 0.f) & 0xffffu); }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
+// IEEE binary16 (TT_FP16).  Kernels that move 16-bit tensors as raw bits
+// keep bf16_t pointers and take a compile-time F16 flag that selects the
+// conversions and the MFMA; element-typed kernels use f16_t.
+typedef _Float16 f16_t;
+typedef _Float16 tt_h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  tt_f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, tt_h2));
+}
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// 16-bit storage format F16 ? binary16 : bf16.
+template <bool F16>
+__device__ __forceinline__ uint32_t lp_pack2(float a, float b) {
+  if constexpr (F16) return pack_h2(a, b);
+  else return pack_bf2(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ uint16_t lp_from(float f) {
+  return (uint16_t)(lp_pack2<F16>(f, 0.f) & 0xffffu);
+}
+template <bool F16>
+__device__ __forceinline__ float lp_to(uint16_t h) {
+  if constexpr (F16) return h2f(h);
+  else return bf2f(h);
+}
+// low / high half of a packed pair
+template <bool F16>
+__device__ __forceinline__ float lp_lo(uint32_t u) {
+  if constexpr (F16) return h2f((uint16_t)(u & 0xffffu));
+  else return __uint_as_float(u << 16);
+}
+template <bool F16>
+__device__ __forceinline__ float lp_hi(uint32_t u) {
+  if constexpr (F16) return h2f((uint16_t)(u >> 16));
+  else return __uint_as_float(u & 0xffff0000u);
+}
+// 16x16x32 MFMA on eight 16-bit values per lane (bits in a bf16x8_t).
+template <bool F16>
+__device__ __forceinline__ f32x4_t lp_mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+inline bool tt_lowp(int mode) { return mode == TT_BF16 || mode == TT_FP16; }
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
@@ -108,6 +158,10 @@ template <> struct Elem<float> {
 template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static float load(const bf16_t *p, size_t i) { return bf2f(p[i]); }
   __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) { p[i] = f2bf(v); }
+};
+template <> struct Elem<f16_t> {
+  __device__ __forceinline__ static float load(const f16_t *p, size_t i) { return (float)p[i]; }
+  __device__ __forceinline__ static void store(f16_t *p, size_t i, float v) { p[i] = (f16_t)v; }
 };
 
 // Wave64 reductions (butterfly over all 64 lanes).
@@ -173,6 +227,7 @@ struct GemmArgs {
   float *colsum;               // nullable: colsum[n] += sum over rows of the stored output
   int raster;                  // tile order: 0 auto, 1 m fastest, 2 n fastest
   bool overwrite;              // EPI_ACCUM only: store the product instead of adding it
+  bool f16;                    // 16-bit operands / output are binary16 (set by tt_gemm)
 };
 int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g);
 
@@ -194,11 +249,13 @@ struct GemmGroup {
   int n = 0, tiles = 0, grid = 0;
   double mn2 = 0;                    // sum of 2 M N (FLOPs per unit of K)
   double bytes_k = 0, bytes_out = 0;  // operand bytes per unit of K; output bytes
+  bool f16 = false;                  // operands are binary16 (else bf16)
 };
 // Plan a group (entries are copied; the device tables come from the arena
 // and stay valid as long as it does).  Every entry must satisfy the bf16
 // kernel's layout rules for K up to k_max.
-int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max, GemmGroup *out);
+int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max, GemmGroup *out,
+                       bool f16 = false);
 // Run every product of the group in one launch with reduction length K.
 int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K);
 // bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
@@ -214,9 +271,25 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                           const float *mean, const float *rstd, const float *g, const float *dy,
                           const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
                           float *dsum = nullptr);
-int tt_colsum(tt_ctx *ctx, bool src_bf16, int M, int N, int ld, const void *src, float *out);
+// Column sums out[n] += sum_m src[m, n]; fmt: the source's tt_mode (float32,
+// bf16 or binary16).
+int tt_colsum(tt_ctx *ctx, int fmt, int M, int N, int ld, const void *src, float *out);
 int tt_fill_f32(tt_ctx *ctx, float *p, size_t n, float v);
-int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst);
+// float32 -> 16-bit (bf16, or binary16 when f16), round to nearest even.
+int tt_cast_f32_bf16(tt_ctx *ctx, size_t n, const float *src, bf16_t *dst, bool f16 = false);
+// Dynamic loss scaling state (device memory).
+struct tt_loss_scale {
+  float scale;       // current loss scale
+  int32_t good;      // clean steps since the scale last changed
+  int32_t overflow;  // this step's gradients held inf / NaN
+  int32_t skipped;   // steps dropped so far
+};
+// g *= 1 / scale over n entries; st->overflow |= any entry non-finite.
+int tt_unscale_check(tt_ctx *ctx, float *g, size_t n, tt_loss_scale *st);
+// Scale update after a step; *out (nullable, device) = the step's overflow.
+int tt_loss_scale_update(tt_ctx *ctx, tt_loss_scale *st, int interval, float growth,
+                         float backoff, int32_t *out);
+int tt_loss_scale_set(tt_ctx *ctx, tt_loss_scale *st, float scale);
 // One 64 x 64 tile range of a batched bf16 transpose (src [rows, cols] ->
 // dst [cols, rows]); tile0 is the first workgroup of this matrix, tiles are
 // numbered row-major with tiles_c = ceil(cols / 64) per tile row.
@@ -255,12 +328,20 @@ int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void
 // bf16 attention kernels (buffer loads, LDS transpose reads); *_ok says
 // whether the tensors fit their 32-bit buffer offsets.
 bool tt_attn_bf16_ok(int B, int T, int NH);
-int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse);
+// f16: the 16-bit tensors are binary16 (else bf16).
+int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse,
+                     bool f16 = false);
 int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
-                     const float *lse, const void *dout, void *dqkv, float *Dv);
+                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16 = false);
 // In-place CE over logits; per_row_loss [N] scratch; loss = mean.
+// grad_scale is multiplied by *scale_dev when that is given (the dynamic
+// loss scale, kept on the device).
 int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
-               const int32_t *targets, float *per_row_loss, float *loss, float grad_scale);
+               const int32_t *targets, float *per_row_loss, float *loss, float grad_scale,
+               const float *scale_dev = nullptr);
+// w_lowp (nullable) receives the 16-bit copy (binary16 when f16); skip
+// (nullable, device): a nonzero value drops the update.
 int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,
-                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t);
+                  size_t n, float lr, float beta1, float beta2, float eps, float wd, int t,
+                  bool f16 = false, const int32_t *skip = nullptr);
 int tt_check_finite(tt_ctx *ctx, const float *x, size_t n, int32_t *flag);

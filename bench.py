@@ -1,6 +1,7 @@
 """Benchmark: one GPT-2 training step (forward, backward, AdamW) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
+    python bench.py --dtype fp16         (the same step in fp16 with dynamic loss scaling)
     python bench.py --decode             (greedy decoding with the KV cache, B=8)
     python bench.py --mlp                (the tiny classifier through the graph autograd)
     python bench.py --calibrate-copy     (1 GiB device copies, for HBM counter scaling)
@@ -48,7 +49,7 @@ def step_flops(L, C, V, T, B, F=None, **_):
     return 3.0 * (L * (linear + attn) + head)
 
 
-def cpu_baseline(w):
+def cpu_baseline(w, dtype="bf16"):
     """Time the CPU oracle (float64 NumPy, as it stands) on a bounded sample of
     the same workload: one training step of the same model on one sequence of
     a reduced length, scaled to tokens/s."""
@@ -66,10 +67,13 @@ def cpu_baseline(w):
     T = w["T"]
     tok, tgt = syn.gpt2_tokens(1, T, w["V"], seed=3)
     t0 = time.perf_counter()
-    og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16")
+    if dtype == "fp16":
+        og.train_step_scaled(p, zeros, dict(zeros), 1, tok, tgt, cfg, 65536.0, 0)
+    else:
+        og.train_step(p, zeros, dict(zeros), 1, tok, tgt, cfg, "bf16")
     dt = time.perf_counter() - t0
     return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one full {w['L']}-layer training step (fwd+bwd+AdamW, bf16 storage "
+            "sample": f"one full {w['L']}-layer training step (fwd+bwd+AdamW, {dtype} storage "
                       f"rounding, float64 NumPy) on 1 sequence of {T} tokens; {dt:.1f} s"}
 
 
@@ -335,6 +339,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="16-bit format of the training step (fp16: dynamic loss scaling)")
     ap.add_argument("--decode", action="store_true",
                     help="measure greedy decoding with the KV cache instead of training")
     ap.add_argument("--mlp", action="store_true",
@@ -379,7 +385,7 @@ def main():
     tok, tgt = syn.gpt2_tokens(B, T, V, seed=3)
     arena = 64 << 30 if L > 12 else 24 << 30
     ctx = tt.Context(arena_bytes=arena, stream=stream)
-    model = tt.Model(ctx, L=L, C=C, NH=NH, V=V, T_max=T, B_max=B, mode="bf16", V_pad=V_pad)
+    model = tt.Model(ctx, L=L, C=C, NH=NH, V=V, T_max=T, B_max=B, mode=args.dtype, V_pad=V_pad)
     model.load(params)
     del params
     tok_d = torch.from_numpy(tok).cuda()
@@ -412,7 +418,7 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     last_loss = float(loss.item())
     if not math.isfinite(last_loss) or int(flag.item()) != 0:
-        log(f"[bench] WARNING: non-finite loss {last_loss}")
+        log(f"[bench] WARNING: non-finite loss {last_loss} or a dropped (overflowed) step")
     # Second pass over the same number of steps with every kernel launch
     # bracketed by HIP events on the context stream: per-kernel durations for
     # the roofline of the dominant kernel (events add small gaps between
@@ -442,9 +448,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded uniform token ids, N(0,0.02) weights)",
-        "config": {"workload": f"{args.workload} train step (fwd+bwd+AdamW), bf16 MFMA / fp32 master",
+        "config": {"workload": f"{args.workload} train step (fwd+bwd+AdamW), {args.dtype} MFMA / "
+                               f"fp32 master" + (", dynamic loss scaling" if args.dtype == "fp16"
+                                                 else ""),
                    "global_batch": B, "seq_len": T, "layers": L, "d_model": C, "heads": NH,
                    "vocab": V, "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
@@ -452,11 +460,12 @@ def main():
         "loss": round(last_loss, 5),
     }
     out["roofline"] = roofline(kernels, args.steps, ms)
-    out["roofline"]["traffic"] = measured_traffic(args.workload, B, T, out["roofline"]["kernel"])
+    out["roofline"]["traffic"] = (measured_traffic(args.workload, B, T, out["roofline"]["kernel"])
+                                  if args.dtype == "bf16" else None)
     log_kernels(kernels, args.steps)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.dtype)
     model.close()
     ctx.close()
     print(json.dumps(out), flush=True)

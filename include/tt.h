@@ -31,7 +31,9 @@
  *     LayerNorm statistics and the loss stay float32 (C++/CUDA page §3.4:
  *     fp32 master weights with low-precision compute).  A "mode tensor" below
  *     is float32 in TT_F32 and bf16 (uint16 storage, round to nearest even)
- *     in TT_BF16.
+ *     in TT_BF16.  TT_FP16: as TT_BF16 with IEEE binary16 in place of bf16
+ *     (the same page's FP16 variant); the whole-model step then scales its
+ *     loss gradient dynamically (tt_model_loss_scale_*).
  *   - Alignment: device pointers must be 16-byte aligned; row lengths need not
  *     be tile multiples (ragged edges are handled).
  *   - One context per stream; a context is not thread-safe.
@@ -57,7 +59,7 @@ typedef enum {
   TT_ERANGE = -7        /* a token id or target was outside [0, V) (device check)*/
 } tt_status;
 
-typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_mode;
+typedef enum { TT_F32 = 0, TT_BF16 = 1, TT_FP16 = 2 } tt_mode;
 
 typedef struct tt_ctx tt_ctx;
 typedef struct tt_model tt_model;
@@ -326,6 +328,26 @@ int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *
 /* AdamW over every model parameter in one launch (weight decay on all). */
 int tt_model_adamw(tt_ctx *ctx, tt_model *model, float lr, float beta1, float beta2,
                    float eps, float wd, int t);
+
+/* Dynamic loss scaling of a TT_FP16 model (C++/CUDA page, section 3.4: fp16
+ * activations and gradients with fp32 master weights; the loss is scaled so
+ * that small gradients survive in fp16, and the scale adapts).  Every
+ * tt_model_fwd_bwd of a TT_FP16 model multiplies the loss gradient by the
+ * current scale, so all stored activation gradients carry it, then divides
+ * the float32 parameter gradients by it again and flags any inf / NaN.  The
+ * next tt_model_adamw (or the update inside tt_train_step) is then dropped,
+ * the scale is multiplied by backoff and the clean-step count restarts;
+ * after interval consecutive clean steps the scale is multiplied by growth.
+ * tt_train_step's nonfinite flag reports the dropped step.  The state lives
+ * on the device (no host synchronisation in the step).  Defaults at
+ * creation: scale 65536, interval 1000, growth 1.001, backoff 0.5.
+ * set: new policy and scale (the counters restart).  get: synchronises with
+ * the context's stream and reads the state (host outputs, nullable).
+ * TT_EINVAL for a model not in TT_FP16. */
+int tt_model_loss_scale_set(tt_ctx *ctx, tt_model *model, float scale, int interval, float growth,
+                            float backoff);
+int tt_model_loss_scale_get(tt_ctx *ctx, tt_model *model, float *scale, int *good_steps,
+                            int *skipped);
 
 /* Global-norm gradient clipping over every parameter gradient of the model
  * (the C++/CUDA page, section 3.2, clips the separately stored gradients by

@@ -11,11 +11,14 @@ def torch_mod():
 
 
 def dev(a, dtype="f32"):
-    """numpy -> contiguous GPU tensor (float32, bf16 or int32)."""
+    """numpy -> contiguous GPU tensor (float32, bf16, fp16 or int32)."""
     torch = torch_mod()
     a = np.ascontiguousarray(a)
     if dtype == "i32":
         return torch.from_numpy(a.astype(np.int32)).cuda()
+    if dtype == "fp16":
+        # numpy rounds float64 -> float16 once (torch would go through float32)
+        return torch.from_numpy(a.astype(np.float16)).cuda().contiguous()
     t = torch.from_numpy(a.astype(np.float32))
     if dtype == "bf16":
         t = t.to(torch.bfloat16)
@@ -33,28 +36,44 @@ def host(t):
 
 def empty(shape, dtype="f32"):
     torch = torch_mod()
-    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[dtype]
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16,
+          "i32": torch.int32}[dtype]
     return torch.empty(shape, dtype=dt, device="cuda")
 
 
 def zeros(shape, dtype="f32"):
     torch = torch_mod()
-    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[dtype]
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16,
+          "i32": torch.int32}[dtype]
     return torch.zeros(shape, dtype=dt, device="cuda")
 
 
 def lowp(mode):
-    return "bf16" if mode == "bf16" else "f32"
+    return mode if mode in ("bf16", "fp16") else "f32"
 
 
 def store(mode):
     """Storage rounding the oracle applies in a mode."""
-    return oracle.round_bf16 if mode == "bf16" else (lambda a: a)
+    if mode == "bf16":
+        return oracle.round_bf16
+    if mode == "fp16":
+        return oracle.round_fp16
+    return lambda a: a
 
 
 def tol(mode):
-    """The parity bar: rel-L2 <= 1e-5 in fp32 mode, <= 2e-2 in bf16 mode."""
-    return 1e-5 if mode == "f32" else 2e-2
+    """The parity bar: rel-L2 <= 1e-5 in fp32 mode, <= 2e-2 in bf16 mode,
+    <= 1e-2 in fp16 mode (11 significant bits against bf16's 8)."""
+    return {"f32": 1e-5, "bf16": 2e-2, "fp16": 1e-2}[mode]
+
+
+def exact_in(mode, a):
+    """Inputs exactly representable in the mode's storage format."""
+    if mode == "bf16":
+        return oracle.round_bf16(a)
+    if mode == "fp16":
+        return oracle.round_fp16(a)
+    return a
 
 
 def sync():
@@ -73,7 +92,7 @@ def split_key_bias(name, got, ref, C):
     return got[rest], ref[rest], got[C:2 * C]
 
 
-KEY_BIAS_NOISE = {"f32": 1e-3, "bf16": 5e-2}
+KEY_BIAS_NOISE = {"f32": 1e-3, "bf16": 5e-2, "fp16": 2e-2}
 
 
 def check_post_adamw(w_gpu, w0, g_ref, w_ref, lr, wd, bar, grad_rms):
