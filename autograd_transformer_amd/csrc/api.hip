@@ -191,14 +191,15 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   if (!io.defer_dw)
     TT_TRY(linear_dw_gemm(ctx, mode, N, C, C, s.att, C, io.rl_mid, C, gr.w_proj, overwrite_dw));
   // Attention.
-  TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, io.dqkv, sc.Dv));
+  // (its kernels also add the column sums of dqkv into the qkv bias gradient)
+  TT_TRY(tt_attn_bwd_impl(ctx, mode, B, T, NH, s.qkv, s.att, s.lse, sc.datt, io.dqkv, sc.Dv,
+                          gr.b_qkv));
   // QKV projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, 3 * C, io.dqkv, 3 * C, w.w_qkv, EPI_STORE, sc.dtmp, C,
                         false, nullptr, 0));
   if (!io.defer_dw)
     TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, io.dqkv, 3 * C, gr.w_qkv,
                           overwrite_dw));
-  TT_TRY(tt_colsum(ctx, mode, N, 3 * C, 3 * C, io.dqkv, gr.b_qkv));
   // LN1 backward + residual.
   TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
                                lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b, dsum_below));

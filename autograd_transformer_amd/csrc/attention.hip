@@ -536,14 +536,16 @@ int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void
 }
 
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
-                     const void *out, const float *lse, const void *dout, void *dqkv, float *Dv) {
-  if (mode == TT_BF16 && tt_attn_bf16_ok(B, T, NH))
-    return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
-  if (mode == TT_BF16) return attn_bwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
-  if (mode == TT_FP16) {
-    if (!tt_attn_bf16_ok(B, T, NH))
-      return tt_set_error(ctx, TT_EUNSUPPORTED, "attention(fp16): qkv of 2 GB or more");
-    return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv, true);
-  }
-  return attn_bwd_t<float>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv);
+                     const void *out, const float *lse, const void *dout, void *dqkv, float *Dv,
+                     float *dbias) {
+  if (tt_lowp(mode) && tt_attn_bf16_ok(B, T, NH))
+    return tt_attn_bwd_bf16(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv, mode == TT_FP16, dbias);
+  if (mode == TT_FP16)
+    return tt_set_error(ctx, TT_EUNSUPPORTED, "attention(fp16): qkv of 2 GB or more");
+  if (mode == TT_BF16)
+    TT_TRY(attn_bwd_t<bf16_t>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv));
+  else
+    TT_TRY(attn_bwd_t<float>(ctx, B, T, NH, qkv, out, lse, dout, dqkv, Dv));
+  const int C3 = 3 * NH * 64;
+  return dbias ? tt_colsum(ctx, mode, B * T, C3, C3, dqkv, dbias) : TT_OK;
 }

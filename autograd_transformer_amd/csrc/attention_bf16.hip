@@ -71,6 +71,31 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return lp_mfma<F16>(a, b, c);
 }
 
+// Bias gradients (the qkv bias's gradient is the column sum of dqkv as
+// stored): lane (lr, lg) of each wave holds the values of one token row
+// (lr) for head dims d*16 + lg*4 + r.  Sum over the 16 rows of the wave with
+// shuffles, over the 4 waves through LDS, then one atomic per column and
+// workgroup.  `red` is [4][64] floats of LDS.
+template <bool F16>
+__device__ __forceinline__ void colsum_atomic(const f32x4_t (&v)[4], float scale, bool row_ok,
+                                              float *red, float *dst, int lr, int lg, int wave,
+                                              int tid) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = row_ok ? lp_to<F16>(lp_from<F16>(v[d][r] * scale)) : 0.f;
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      x += __shfl_xor(x, 8, 64);
+      if (lr == 0) red[wave * 64 + d * 16 + lg * 4 + r] = x;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) unsafeAtomicAdd(dst + tid, (red[tid] + red[64 + tid]) + (red[128 + tid] + red[192 + tid]));
+}
+
 // One 64 x 64 tile (token rows t0.., head columns col..col+63 of a [.., ld]
 // tensor), 2 vectors per thread of a 256-thread block.
 struct TileRegs {
@@ -258,7 +283,8 @@ template <bool F16>
 __global__ void __launch_bounds__(256, 2)
 attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
                       const float *__restrict__ lse, const float *__restrict__ Dv,
-                      bf16_t *__restrict__ dqkv, int nkb, uint32_t qkv_bytes, uint32_t do_bytes) {
+                      bf16_t *__restrict__ dqkv, int nkb, uint32_t qkv_bytes, uint32_t do_bytes,
+                      float *__restrict__ dbias) {
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][64 * LDT];
   __shared__ __attribute__((aligned(16))) bf16_t Os[2][64 * LDT];
   __shared__ __attribute__((aligned(16))) float ls[2][64], ds[2][64];
@@ -357,6 +383,12 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
     if (qb + 1 < nqb) put(cur ^ 1);
     __syncthreads();
   }
+  if (dbias) {   // key and value bias gradients (LDS reused after the loop's last barrier)
+    float *red = (float *)&Qs[0][0];
+    colsum_atomic<F16>(dk, 0.125f, key < T, red, dbias + C + h * HS, lr, lg, wave, tid);
+    __syncthreads();
+    colsum_atomic<F16>(dv, 1.f, key < T, red, dbias + 2 * C + h * HS, lr, lg, wave, tid);
+  }
   if (key >= T) return;
   bf16_t *drow = dqkv + (row0 + key) * ld + h * HS;
 #pragma unroll
@@ -375,8 +407,9 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
 template <bool F16>
 __global__ void __launch_bounds__(256, 2)
 attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dO,
-                    const float *__restrict__ lse, const float *__restrict__ Dv,
-                    bf16_t *__restrict__ dqkv, int nqb, uint32_t qkv_bytes, uint32_t do_bytes) {
+                    const bf16_t *__restrict__ O, const float *__restrict__ lse,
+                    float *__restrict__ Dv, bf16_t *__restrict__ dqkv, int nqb, uint32_t qkv_bytes,
+                    uint32_t do_bytes, float *__restrict__ dbias) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * LDT];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][64 * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -386,18 +419,32 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
   const int bh = blockIdx.x % nbh, b = bh / NH, h = bh % NH;
   const int C = NH * HS, ld = 3 * C;
   const size_t row0 = (size_t)b * T;
-  const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qkv, qkv_bytes), ro = rsrc(dO, do_bytes),
+                               rout = rsrc(O, do_bytes);
 
   const int q = qb * 64 + wave * 16 + lr;   // this lane's query column
   bf16x8_t qf[2], of[2];
+  // D = rowsum(dO o O) for this query: each lane has 16 of the 64 head dims
+  // of dO and O, the 4 lanes of a query add theirs up; the dK/dV kernel,
+  // which runs next, reads it back.
+  float dsum = 0.f;
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const bool ok = q < T;
+    const uint32_t off_o = ok ? (uint32_t)(((row0 + q) * C + h * HS + st * 32 + lg * 8) * 2) : OOB;
     qf[st] = as_frag(bload(rq, ok ? (uint32_t)(((row0 + q) * ld + h * HS + st * 32 + lg * 8) * 2) : OOB));
-    of[st] = as_frag(bload(ro, ok ? (uint32_t)(((row0 + q) * C + h * HS + st * 32 + lg * 8) * 2) : OOB));
+    const uint4 dov = bload(ro, off_o), ov = bload(rout, off_o);
+    of[st] = as_frag(dov);
+    const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w}, c[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dsum += lp_lo<F16>(a[i]) * lp_lo<F16>(c[i]) + lp_hi<F16>(a[i]) * lp_hi<F16>(c[i]);
   }
+  dsum += __shfl_xor(dsum, 16, 64);
+  dsum += __shfl_xor(dsum, 32, 64);
   const float lq = q < T ? lse[((size_t)b * NH + h) * T + q] * LOG2E : 0.f;
-  const float Dq = q < T ? Dv[((size_t)b * NH + h) * T + q] : 0.f;
+  const float Dq = q < T ? dsum : 0.f;
+  if (q < T && lg == 0) Dv[((size_t)b * NH + h) * T + q] = dsum;
   f32x4_t dq[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) dq[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -458,6 +505,10 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
     }
     __syncthreads();
   }
+  if (dbias) {   // query bias gradient (LDS reused after the loop's last barrier)
+    float *red = (float *)&Ks[0][0];
+    colsum_atomic<F16>(dq, 0.125f, q < T, red, dbias + h * HS, lr, lg, wave, tid);
+  }
   if (q >= T) return;
   bf16_t *drow = dqkv + (row0 + q) * ld + h * HS;
 #pragma unroll
@@ -465,30 +516,6 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
     *(uint2 *)(drow + d * 16 + lg * 4) =
         make_uint2(lp_pack2<F16>(dq[d][0] * 0.125f, dq[d][1] * 0.125f),
                    lp_pack2<F16>(dq[d][2] * 0.125f, dq[d][3] * 0.125f));
-}
-
-// Dv[b,h,t] = sum_d dO[t, h*64+d] * O[t, h*64+d]: one wave per (token, 4
-// heads), 16 lanes per head, 4 elements per lane.
-template <bool F16>
-__global__ void __launch_bounds__(256) attn_dot_bf16_kernel(int BT, int T, int NH,
-                                                            const bf16_t *__restrict__ o,
-                                                            const bf16_t *__restrict__ dO,
-                                                            float *__restrict__ Dv) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int seg = gid >> 4;           // (token, head) pair
-  const int l16 = threadIdx.x & 15;
-  const bool ok = seg < BT * NH;
-  float s = 0.f;
-  const int row = ok ? seg / NH : 0, h = ok ? seg % NH : 0;
-  if (ok) {
-    const size_t off = (size_t)row * NH * HS + h * HS + l16 * 4;
-    const uint2 a = *(const uint2 *)(o + off), c = *(const uint2 *)(dO + off);
-    s = lp_to<F16>(a.x & 0xffffu) * lp_to<F16>(c.x & 0xffffu) + lp_to<F16>(a.x >> 16) * lp_to<F16>(c.x >> 16) +
-        lp_to<F16>(a.y & 0xffffu) * lp_to<F16>(c.y & 0xffffu) + lp_to<F16>(a.y >> 16) * lp_to<F16>(c.y >> 16);
-  }
-#pragma unroll
-  for (int w = 8; w > 0; w >>= 1) s += __shfl_xor(s, w, 64);
-  if (ok && l16 == 0) Dv[((size_t)(row / T) * NH + h) * T + row % T] = s;
 }
 
 }  // namespace
@@ -515,43 +542,35 @@ int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *o
 }
 
 int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
-                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16) {
+                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16,
+                     float *dbias) {
   const int BT = B * T;
   const uint32_t qb = (uint32_t)((size_t)BT * 3 * NH * HS * 2);
   const uint32_t ob = (uint32_t)((size_t)BT * NH * HS * 2);
   const double pass = 2.0 * B * NH * HS * (double)T * (T + 1) / 2.0;   // one causal product
-  {
-    tt_prof_scope prof(ctx, "attn_dot_bf16_kernel", 0.0, 2.0 * ob + 4.0 * BT * NH);
-    if (f16)
-      hipLaunchKernelGGL(attn_dot_bf16_kernel<true>, dim3((BT * NH * 16 + 255) / 256), dim3(256),
-                         0, ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
-    else
-      hipLaunchKernelGGL(attn_dot_bf16_kernel<false>, dim3((BT * NH * 16 + 255) / 256), dim3(256),
-                         0, ctx->stream, BT, T, NH, (const bf16_t *)out, (const bf16_t *)dout, Dv);
-  }
-  TT_TRY(tt_check_launch(ctx, "attn_dot_bf16"));
   const int nb = (T + 63) / 64;
   {
-  // algorithmic backward: dP, dV, dK here, dQ in the next kernel (4 products)
+  // dQ first: it also forms D = rowsum(dO o O), which the dK/dV kernel reads
+  tt_prof_scope prof(ctx, "attn_dq_bf16_kernel", pass, 0.0);
+  if (f16)
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<true>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
+                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, (const bf16_t *)out, lse, Dv,
+                       (bf16_t *)dqkv, nb, qb, ob, dbias);
+  else
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<false>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
+                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, (const bf16_t *)out, lse, Dv,
+                       (bf16_t *)dqkv, nb, qb, ob, dbias);
+  }
+  TT_TRY(tt_check_launch(ctx, "attn_dq_bf16"));
+  // algorithmic backward: dP, dV, dK here, dQ in the other kernel (4 products)
   tt_prof_scope prof(ctx, "attn_dkdv_bf16_kernel", 3.0 * pass, 0.0);
   if (f16)
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<true>, dim3(B * NH * nb), dim3(256), 0, ctx->stream,
                        T, NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv,
-                       nb, qb, ob);
+                       nb, qb, ob, dbias);
   else
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<false>, dim3(B * NH * nb), dim3(256), 0, ctx->stream,
                        T, NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv,
-                       nb, qb, ob);
-  }
-  TT_TRY(tt_check_launch(ctx, "attn_dkdv_bf16"));
-  tt_prof_scope prof(ctx, "attn_dq_bf16_kernel", pass, 0.0);
-  if (f16)
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<true>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
-                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb,
-                       qb, ob);
-  else
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<false>, dim3(B * NH * nb), dim3(256), 0, ctx->stream, T,
-                       NH, (const bf16_t *)qkv, (const bf16_t *)dout, lse, Dv, (bf16_t *)dqkv, nb,
-                       qb, ob);
-  return tt_check_launch(ctx, "attn_dq_bf16");
+                       nb, qb, ob, dbias);
+  return tt_check_launch(ctx, "attn_dkdv_bf16");
 }

@@ -322,17 +322,21 @@ int tt_embed_decode(tt_ctx *ctx, int B, int C, int V, const int32_t *tok_dev,
 int tt_copy_i32(tt_ctx *ctx, int n, const int32_t *src, int32_t *dst);
 int tt_attn_fwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      void *out, float *lse);
+// dbias (nullable) += column sums of dqkv as stored (the qkv bias gradient).
 int tt_attn_bwd_impl(tt_ctx *ctx, tt_mode mode, int B, int T, int NH, const void *qkv,
                      const void *out, const float *lse, const void *dout, void *dqkv,
-                     float *scratch_D);
+                     float *scratch_D, float *dbias = nullptr);
 // bf16 attention kernels (buffer loads, LDS transpose reads); *_ok says
 // whether the tensors fit their 32-bit buffer offsets.
 bool tt_attn_bf16_ok(int B, int T, int NH);
 // f16: the 16-bit tensors are binary16 (else bf16).
 int tt_attn_fwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, void *out, float *lse,
                      bool f16 = false);
+// dbias (nullable) += the column sums of dqkv as stored (the qkv bias
+// gradient, [3C] float32).  Dv: [B, NH, T] scratch.
 int tt_attn_bwd_bf16(tt_ctx *ctx, int B, int T, int NH, const void *qkv, const void *out,
-                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16 = false);
+                     const float *lse, const void *dout, void *dqkv, float *Dv, bool f16 = false,
+                     float *dbias = nullptr);
 // In-place CE over logits; per_row_loss [N] scratch; loss = mean.
 // grad_scale is multiplied by *scale_dev when that is given (the dynamic
 // loss scale, kept on the device).
