@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int MLP_THREADS = 256;
+constexpr int MLP_THREADS = 1024;
 constexpr size_t MLP_LDS_FLOATS = 16384;   // 64 KB of dynamic LDS
 
 struct MlpArgs {
@@ -28,6 +28,19 @@ struct MlpArgs {
   int32_t *range_flag;
 };
 
+// Sum over the G consecutive lanes that share one output (G a power of two
+// dividing 64): butterfly within the group.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Every phase spreads its outputs over all 1024 threads; the reductions over
+// rows (logits, weight gradients) give each output a group of lanes that
+// split the rows and meet in a butterfly, so no thread walks a long serial
+// chain of LDS reads.
 __global__ void __launch_bounds__(MLP_THREADS) mlp_step_kernel(MlpArgs a) {
   extern __shared__ float lds[];
   const int N = a.N, I = a.I, H = a.H, C = a.C, tid = threadIdx.x;
@@ -46,20 +59,29 @@ __global__ void __launch_bounds__(MLP_THREADS) mlp_step_kernel(MlpArgs a) {
   for (int i = tid; i < H * C; i += MLP_THREADS) w2[i] = a.W2[i];
   for (int i = tid; i < C; i += MLP_THREADS) b2[i] = a.b2[i];
   __syncthreads();
-  // forward: hp = x W1 + b1, h = GELU(hp), z = h W2 + b2
+  // forward: hp = x W1 + b1, h = GELU(hp)
   for (int e = tid; e < N * H; e += MLP_THREADS) {
-    const int n = e / H, j = e % H;
+    const int n = e / H, j = e - n * H;
     float s = b1[j];
     for (int i = 0; i < I; ++i) s += x[n * I + i] * w1[i * H + j];
     hp[e] = s;
     h[e] = gelu_f(s);
   }
   __syncthreads();
-  for (int e = tid; e < N * C; e += MLP_THREADS) {
-    const int n = e / C, c = e % C;
-    float s = b2[c];
-    for (int j = 0; j < H; ++j) s += h[n * H + j] * w2[j * C + c];
-    z[e] = s;
+  // z = h W2 + b2: 4 lanes per logit, each over a quarter of the hidden units
+  {
+    constexpr int G = 4;
+    const int sub = tid & (G - 1);
+    for (int base = tid - sub; base < N * C * G; base += MLP_THREADS) {
+      const int e = base / G;
+      float s = 0.f;
+      if (e < N * C) {
+        const int n = e / C, c = e - n * C;
+        for (int j = sub; j < H; j += G) s += h[n * H + j] * w2[j * C + c];
+      }
+      s = group_sum<G>(s);
+      if (sub == 0 && e < N * C) z[e] = s + b2[e % C];
+    }
   }
   __syncthreads();
   // cross-entropy per row: loss_n = logsumexp(z_n) - z_n[y_n];
@@ -91,47 +113,69 @@ __global__ void __launch_bounds__(MLP_THREADS) mlp_step_kernel(MlpArgs a) {
     for (int c = 0; c < C; ++c) zr[c] = c == y ? -r * inv : __expf(zr[c] - m) * inv;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {   // mean loss: one wave adds the row losses
     float t = 0.f;
-    for (int n = 0; n < N; ++n) t += rl[n];
-    *a.loss = t * invN;
+    for (int n = tid; n < N; n += 64) t += rl[n];
+    t = wave_sum(t);
+    if (tid == 0) *a.loss = t * invN;
   }
-  // dW2 = hᵀ dz, db2 = column sums of dz (old W2 still in LDS)
-  for (int e = tid; e < H * C + C; e += MLP_THREADS) {
-    float s = 0.f;
-    if (e < H * C) {
-      const int j = e / C, c = e % C;
-      for (int n = 0; n < N; ++n) s += h[n * H + j] * z[n * C + c];
-      if (a.gW2) a.gW2[e] = s;
-      a.W2[e] = w2[e] - a.lr * s;
-    } else {
-      const int c = e - H * C;
-      for (int n = 0; n < N; ++n) s += z[n * C + c];
-      if (a.gb2) a.gb2[c] = s;
-      a.b2[c] = b2[c] - a.lr * s;
+  // dW2 = hᵀ dz, db2 = column sums of dz (old W2 still in LDS): 8 lanes per
+  // output, each over every 8th row
+  {
+    constexpr int G = 8;
+    const int sub = tid & (G - 1);
+    for (int base = tid - sub; base < (H * C + C) * G; base += MLP_THREADS) {
+      const int e = base / G;
+      float s = 0.f;
+      if (e < H * C) {
+        const int j = e / C, c = e - j * C;
+        for (int n = sub; n < N; n += G) s += h[n * H + j] * z[n * C + c];
+      } else if (e < H * C + C) {
+        const int c = e - H * C;
+        for (int n = sub; n < N; n += G) s += z[n * C + c];
+      }
+      s = group_sum<G>(s);
+      if (sub == 0 && e < H * C) {
+        if (a.gW2) a.gW2[e] = s;
+        a.W2[e] = w2[e] - a.lr * s;
+      } else if (sub == 0 && e < H * C + C) {
+        const int c = e - H * C;
+        if (a.gb2) a.gb2[c] = s;
+        a.b2[c] = b2[c] - a.lr * s;
+      }
     }
   }
   // dhp = (dz W2ᵀ) * GELU'(hp), written over hp
   for (int e = tid; e < N * H; e += MLP_THREADS) {
-    const int n = e / H, j = e % H;
+    const int n = e / H, j = e - n * H;
     float s = 0.f;
     for (int c = 0; c < C; ++c) s += z[n * C + c] * w2[j * C + c];
     hp[e] = s * gelu_grad_f(hp[e]);
   }
   __syncthreads();
-  // dW1 = xᵀ dhp, db1 = column sums of dhp
-  for (int e = tid; e < I * H + H; e += MLP_THREADS) {
-    float s = 0.f;
-    if (e < I * H) {
-      const int i = e / H, j = e % H;
-      for (int n = 0; n < N; ++n) s += x[n * I + i] * hp[n * H + j];
-      if (a.gW1) a.gW1[e] = s;
-      a.W1[e] = w1[e] - a.lr * s;
-    } else {
-      const int j = e - I * H;
-      for (int n = 0; n < N; ++n) s += hp[n * H + j];
-      if (a.gb1) a.gb1[j] = s;
-      a.b1[j] = b1[j] - a.lr * s;
+  // dW1 = xᵀ dhp, db1 = column sums of dhp: 8 lanes per output
+  {
+    constexpr int G = 8;
+    const int sub = tid & (G - 1);
+    for (int base = tid - sub; base < (I * H + H) * G; base += MLP_THREADS) {
+      const int e = base / G;
+      float s = 0.f;
+      if (e < I * H) {
+        const int i = e / H, j = e - i * H;
+        for (int n = sub; n < N; n += G) s += x[n * I + i] * hp[n * H + j];
+      } else if (e < I * H + H) {
+        const int j = e - I * H;
+        for (int n = sub; n < N; n += G) s += hp[n * H + j];
+      }
+      s = group_sum<G>(s);
+      if (sub == 0 && e < I * H) {
+        if (a.gW1) a.gW1[e] = s;
+        a.W1[e] = w1[e] - a.lr * s;
+      } else if (sub == 0 && e < I * H + H) {
+        const int j = e - I * H;
+        if (a.gb1) a.gb1[j] = s;
+        a.b1[j] = b1[j] - a.lr * s;
+      }
     }
   }
 }
