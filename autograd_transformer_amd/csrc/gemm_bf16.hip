@@ -588,17 +588,54 @@ gemm_bf16_v3_kernel(GemmParams p) {
       asm volatile("" ::: "memory");
       if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
       const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
+      if constexpr (A_KM && B_KM) {
+        // Every fragment of the stage is read into registers of its own; the
+        // scheduling barriers then fix the order: the first k step's reads,
+        // its MFMAs with the next step's reads spread between them, the
+        // remaining MFMAs.  Left to itself the compiler reads each fragment
+        // just before its first MFMA and waits for it there.
+        constexpr int KS = BKV / 32;
+        constexpr int RD = FM + FN;   // LDS reads per k step
+        constexpr int MF = FM * FN;   // MFMAs per k step
+        constexpr int PER = MF / RD > 0 ? MF / RD : 1;
+        bf16x8_t fa[KS][FM], fb[KS][FN];
 #pragma unroll
-      for (int kk = 0; kk < BKV; kk += 32) {
-        bf16x8_t fb[FN];
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+          for (int j = 0; j < FN; ++j) fb[s][j] = OB::frag(bs, wn * C::WTN + j * 16, s * 32, lr, lg);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+          for (int i = 0; i < FM; ++i) fa[s][i] = OA::frag(as, wm * C::WTM + i * 16, s * 32, lr, lg);
+        }
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = lp_mfma<F16>(fa, fb[j], acc[i][j]);
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = lp_mfma<F16>(fa[s][i], fb[s][j], acc[i][j]);
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);       // DS reads
+#pragma unroll
+        for (int s = 1; s < KS; ++s) {
+#pragma unroll
+          for (int q = 0; q < RD; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (MF - PER * RD > 0) __builtin_amdgcn_sched_group_barrier(0x008, MF - PER * RD, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < BKV; kk += 32) {
+          bf16x8_t fb[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = lp_mfma<F16>(fa, fb[j], acc[i][j]);
+          }
         }
       }
     }
