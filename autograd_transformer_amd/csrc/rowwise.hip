@@ -427,8 +427,22 @@ __global__ void __launch_bounds__(256) ce_kernel(int N, int V, int ld, void *log
 // (max, sum exp) over the workgroup, then overwrites the row with
 // (softmax - onehot) * scale; pad columns (>= V) become 0.  One read and one
 // write of the logits instead of two reads and a write.
+// Two workgroups share a CU (8 waves per SIMD, at most 64 VGPRs), so one
+// row's reductions and stores overlap another's loads.  That fits only if
+// the three passes each re-derive their unpacked values and indexes from the
+// packed row: between passes the row and the thread index go through
+// ce_opaque, which the compiler cannot see through (left alone it keeps 56
+// unpacked floats and 7 store offsets live across the passes: 105 VGPRs, one
+// workgroup per CU).
 constexpr int CE_VPT = 7;
 constexpr int CE_THREADS = 1024;
+
+// An empty asm statement that claims to change x: values computed from the
+// old x are not reused after it.  It emits no instruction.
+__device__ __forceinline__ void ce_opaque(int &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void ce_opaque(uint4 &x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
 
 __device__ __forceinline__ float ce_block_reduce(float v, bool is_max, float *red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -443,7 +457,7 @@ __device__ __forceinline__ float ce_block_reduce(float v, bool is_max, float *re
 }
 
 template <bool F16>
-__global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld, bf16_t *logits,
+__global__ void __launch_bounds__(CE_THREADS, 8) ce_reg_kernel(int N, int V, int ld, bf16_t *logits,
                                                             const int32_t *__restrict__ targets,
                                                             float *__restrict__ row_loss,
                                                             float scale,
@@ -471,23 +485,31 @@ __global__ void __launch_bounds__(CE_THREADS) ce_reg_kernel(int N, int V, int ld
     const uint32_t w = (&v[i].x)[q >> 1];
     return (q & 1) ? lp_hi<F16>(w) : lp_lo<F16>(w);
   };
+  int tq = tid;
+  ce_opaque(tq);
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < CE_VPT; ++i)
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if ((tid + i * CE_THREADS) * 8 + q < V) m = fmaxf(m, val(i, q));
+      if ((tq + i * CE_THREADS) * 8 + q < V) m = fmaxf(m, val(i, q));
   const float gm = ce_block_reduce(m, true, red);
+#pragma unroll
+  for (int i = 0; i < CE_VPT; ++i) ce_opaque(v[i]);
+  ce_opaque(tq);
   float sacc = 0.f;
 #pragma unroll
   for (int i = 0; i < CE_VPT; ++i)
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if ((tid + i * CE_THREADS) * 8 + q < V) sacc += __expf(val(i, q) - gm);
+      if ((tq + i * CE_THREADS) * 8 + q < V) sacc += __expf(val(i, q) - gm);
   const float lse = gm + __logf(ce_block_reduce(sacc, false, red));
 #pragma unroll
+  for (int i = 0; i < CE_VPT; ++i) ce_opaque(v[i]);
+  ce_opaque(tq);
+#pragma unroll
   for (int i = 0; i < CE_VPT; ++i) {
-    const int idx = tid + i * CE_THREADS;
+    const int idx = tq + i * CE_THREADS;
     if (idx >= nv8) continue;
     uint32_t o[4];
 #pragma unroll
