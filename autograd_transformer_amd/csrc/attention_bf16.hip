@@ -38,6 +38,14 @@ constexpr float RESCALE = 8.0f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every outstanding vector-memory load of this wave (vmcnt(0); the
+// other counters untouched, gfx9 encoding).  Placed before a main loop whose
+// body uses registers loaded in the prologue: without it the compiler's wait
+// analysis sees those loads as possibly in flight on loop entry and, inside
+// the loop, waits for everything issued before their first use -- including
+// the next tile's prefetch, which then no longer overlaps anything.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)bytes, 0x00020000);
 }
@@ -163,6 +171,7 @@ attn_fwd_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, bf16_t *__re
   vr.load(rs, row0, 0, T, ld, 2 * C + h * HS, tid);
   kr.store(Ks[0], tid);
   vr.store(Vs[0], tid);
+  wait_all_loads();
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
@@ -315,26 +324,32 @@ attn_dkdv_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_
   }
   const int nqb = (T + 63) / 64;
   TileRegs qr, orr;
+  // The row statistics are loaded raw (clamped row, no arithmetic on the
+  // value) and finished in put(): a use right after the load would make the
+  // wave wait for the whole prefetch there.
   float lv = 0.f, dvv = 0.f;
+  bool qok = false;
   auto fetch = [&](int q0) {
     qr.load(rq, row0, q0, T, ld, h * HS, tid);
     orr.load(ro, row0, q0, T, C, h * HS, tid);
     if (tid < 64) {
       const int q = q0 + tid;
-      lv = q < T ? lseg[q] * LOG2E : INFINITY;
-      dvv = q < T ? Dg[q] : 0.f;
+      qok = q < T;
+      lv = lseg[min(q, T - 1)];
+      dvv = Dg[min(q, T - 1)];
     }
   };
   auto put = [&](int buf) {
     qr.store(Qs[buf], tid);
     orr.store(Os[buf], tid);
     if (tid < 64) {
-      ls[buf][tid] = lv;
-      ds[buf][tid] = dvv;
+      ls[buf][tid] = qok ? lv * LOG2E : INFINITY;
+      ds[buf][tid] = qok ? dvv : 0.f;
     }
   };
   fetch(kb * 64);
   put(0);
+  wait_all_loads();
   __syncthreads();
   for (int qb = kb; qb < nqb; ++qb) {
     const int cur = (qb - kb) & 1;
@@ -457,6 +472,7 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
   vr.load(rq, row0, 0, T, ld, 2 * C + h * HS, tid);
   kr.store(Ks[0], tid);
   vr.store(Vs[0], tid);
+  wait_all_loads();
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
