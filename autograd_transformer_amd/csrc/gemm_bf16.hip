@@ -586,9 +586,9 @@ gemm_bf16_v3_kernel(GemmParams p) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
       const bf16_t *as = At(it % NS), *bs = Bt(it % NS);
       if constexpr (A_KM && B_KM) {
+        if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
         // Every fragment of the stage is read into registers of its own; the
         // scheduling barriers then fix the order: the first k step's reads,
         // its MFMAs with the next step's reads spread between them, the
@@ -624,19 +624,29 @@ gemm_bf16_v3_kernel(GemmParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
       } else {
+        // A transposed operand: the compiler puts a full vmcnt(0) wait in
+        // front of the first ds_read_b64_tr_b16 after any buffer-to-LDS load
+        // (it cannot tell that they touch different stages).  So the stage's
+        // fragments are all read first and only then is the next stage's
+        // load issued -- issued before the reads, it would be waited for
+        // right there and overlap none of the MFMAs.
+        constexpr int KS = BKV / 32;
+        bf16x8_t fa[KS][FM], fb[KS][FN];
 #pragma unroll
-        for (int kk = 0; kk < BKV; kk += 32) {
-          bf16x8_t fb[FN];
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) fb[j] = OB::frag(bs, wn * C::WTN + j * 16, kk, lr, lg);
+          for (int j = 0; j < FN; ++j) fb[s][j] = OB::frag(bs, wn * C::WTN + j * 16, s * 32, lr, lg);
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const bf16x8_t fa = OA::frag(as, wm * C::WTM + i * 16, kk, lr, lg);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = lp_mfma<F16>(fa, fb[j], acc[i][j]);
-          }
+          for (int i = 0; i < FM; ++i) fa[s][i] = OA::frag(as, wm * C::WTM + i * 16, s * 32, lr, lg);
         }
+        asm volatile("" ::: "memory");
+        if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = lp_mfma<F16>(fa[s][i], fb[s][j], acc[i][j]);
       }
     }
   }
