@@ -356,14 +356,38 @@ struct DOp {
       const int kr0 = kk + 8 * lg + (lr >> 2);
       const int kr1 = kr0 + 4;
       const int pc0 = (c >> 3) ^ rswz(kr0), pc1 = (c >> 3) ^ rswz(kr1);
-      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7)));
-      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr1 * ROWS + pc1 * 8 + (c & 7)));
+      // Issued as inline assembly: through the builtin, the compiler puts a
+      // full vmcnt(0) wait in front of the read whenever a buffer-to-LDS load
+      // is in flight (it cannot tell the stages apart), which would drain the
+      // operand ring every stage.  The caller waits for these reads itself
+      // (lds_frags_ready) before using the fragments.
+      const uint32_t a0 = (uint32_t)(uintptr_t)(lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7));
+      const uint32_t a1 = (uint32_t)(uintptr_t)(lds_v4s *)(t + kr1 * ROWS + pc1 * 8 + (c & 7));
+      v4s lo, hi;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
       typedef short v8s __attribute__((ext_vector_type(8)));
       v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(bf16x8_t, v);
     }
   }
 };
+
+// Wait for every LDS read this wave has issued (lgkmcnt(0)) and tie the
+// fragments to that wait: each passes through an empty asm statement after
+// it, so no use of a fragment can be scheduled above the wait.  Needed after
+// the inline-assembly transpose reads, which the compiler does not track.
+template <int KS, int FM, int FN>
+__device__ __forceinline__ void lds_frags_ready(bf16x8_t (&fa)[KS][FM], bf16x8_t (&fb)[KS][FN]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[s][i]));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[s][j]));
+  }
+}
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 template <int N>
@@ -624,12 +648,9 @@ gemm_bf16_v3_kernel(GemmParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
       } else {
-        // A transposed operand: the compiler puts a full vmcnt(0) wait in
-        // front of the first ds_read_b64_tr_b16 after any buffer-to-LDS load
-        // (it cannot tell that they touch different stages).  So the stage's
-        // fragments are all read first and only then is the next stage's
-        // load issued -- issued before the reads, it would be waited for
-        // right there and overlap none of the MFMAs.
+        // A transposed operand: the stage's fragments are read, the next
+        // stage's loads issued, then the reads waited for (lds_frags_ready)
+        // and the MFMAs run while those loads are in flight.
         constexpr int KS = BKV / 32;
         bf16x8_t fa[KS][FM], fb[KS][FN];
 #pragma unroll
@@ -641,6 +662,7 @@ gemm_bf16_v3_kernel(GemmParams p) {
         }
         asm volatile("" ::: "memory");
         if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+        lds_frags_ready<KS, FM, FN>(fa, fb);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -829,7 +851,8 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 //    (ranked with operands arriving cold from HBM, as in the step; with
 //    cache-resident operands the ranking differs)
 //  * one row-major operand: the register-prefetch v2 kernel, 256 x 128;
-//  * weight gradients: 256 x 128, BK 32, 2 stages (below).
+//  * weight gradients: 256 x 128, BK 32, 3 stages (below; two workgroups
+//    per CU).
 // Tile order within an XCD: m fastest (neighbouring workgroups share B
 // panels) except on the 256 x 128 BK-32 path, where n fastest (shared A
 // panels) measured faster inside the step.
@@ -871,7 +894,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
     h.epi = g.overwrite ? EPI_STORE : EPI_STORE_ACC;
     h.out_bf16 = false;
     h.bias = nullptr;
-    return launch3<256, 128, 32, 4, 2, 2>(ctx, h, 1);
+    return launch3<256, 128, 32, 4, 2, 3>(ctx, h, 1);
   }
   tt_scratch_scope scope(ctx);
   void *ws;
@@ -883,7 +906,7 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
   h.bias = nullptr;
   // split is already what launch3 runs (whole k-blocks per split), so the
   // reduction sums exactly the partials written.
-  TT_TRY((launch3<256, 128, 32, 4, 2, 2>(ctx, h, split, (size_t)g.M * g.N)));
+  TT_TRY((launch3<256, 128, 32, 4, 2, 3>(ctx, h, split, (size_t)g.M * g.N)));
   const size_t work = (size_t)g.M * g.N / 4;
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
   tt_prof_scope prof(ctx, "splitk_reduce_kernel", 0.0,
@@ -895,15 +918,16 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
 
 // ------------------------------------------------------------ grouped launch
 // The products of a group share one kernel configuration (the weight-gradient
-// tile: 256 x 128, BK 32, 2 stages, both operands read with the LDS transpose)
+// tile: 256 x 128, BK 32, 3 stages, both operands read with the LDS transpose)
 // and one reduction length; each workgroup owns one output tile of one
 // product.  Run as one launch, the 48 weight gradients of a 12-layer model
 // and the token-table gradient fill the machine without splitting K.
 // Tile of the grouped launch (BM, BN, BK, waves along M, along N, stages);
 // measured inside the GPT-2 124M step against 256x128 BK 32/64 with 2-3
-// stages, 256x256 and 128x256.
+// stages, 256x256 and 128x256 (3 stages gain once the transpose reads no
+// longer drain the ring).
 #ifndef TT_GROUP_TILE
-#define TT_GROUP_TILE 256, 128, 32, 4, 2, 2
+#define TT_GROUP_TILE 256, 128, 32, 4, 2, 3
 #endif
 namespace {
 template <int BM, int BN, int BKV, int WM, int WN, int NS>
