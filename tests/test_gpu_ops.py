@@ -85,8 +85,10 @@ def test_gradient_accumulation_2_plus_3(ctx, mode, golden):
 
 # ------------------------------------------------------------------ linear
 
+# (17, 96, 48) and (40, 64, 64): weight gradients whose token reduction is one
+# and two 32-deep stages, shorter than the operand ring
 SHAPES = [(64, 3, 32), (300, 200, 130), (256, 256, 384), (129, 64, 17), (1000, 768, 2304),
-          (4160, 768, 768)]
+          (4160, 768, 768), (17, 96, 48), (40, 64, 64)]
 
 
 @pytest.mark.parametrize("mode", MODES)
