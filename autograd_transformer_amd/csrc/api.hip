@@ -153,6 +153,9 @@ struct BwdIO {
   void *rl_in, *rl_mid, *rl_out;
   void *dh, *dqkv;
   bool defer_dw;   // leave the four weight-matrix gradients to the caller
+  // non-NULL: the LayerNorm backward leaves its column partials here and the
+  // caller adds them up later (tt_layernorm_bwd_reduce_batch)
+  float *ln2_part = nullptr, *ln1_part = nullptr;
 };
 
 // Block backward, in place on the residual gradient R (fp32): on entry R
@@ -183,8 +186,12 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
     TT_TRY(linear_dw_gemm(ctx, mode, N, C, F, s.ln2, C, io.dh, F, gr.w_fc, overwrite_dw));
   // LN2 backward + residual: R = R + LN2_bwd(dtmp); its column sums are the
   // attention projection's bias gradient.
-  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
-                               lp ? (bf16_t *)io.rl_mid : nullptr, gr.ln2_g, gr.ln2_b, gr.b_proj));
+  if (io.ln2_part)
+    TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
+                                 lp ? (bf16_t *)io.rl_mid : nullptr, io.ln2_part));
+  else
+    TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
+                                 lp ? (bf16_t *)io.rl_mid : nullptr, gr.ln2_g, gr.ln2_b, gr.b_proj));
   // Attention projection.
   TT_TRY(linear_dx_gemm(ctx, mode, N, C, C, io.rl_mid, C, w.w_proj, EPI_STORE, sc.datt, C, lp,
                         nullptr, 0));
@@ -201,8 +208,13 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
     TT_TRY(linear_dw_gemm(ctx, mode, N, C, 3 * C, s.ln1, C, io.dqkv, 3 * C, gr.w_qkv,
                           overwrite_dw));
   // LN1 backward + residual.
-  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
-                               lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b, dsum_below));
+  if (io.ln1_part)
+    TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
+                                 lp ? (bf16_t *)io.rl_out : nullptr, io.ln1_part));
+  else
+    TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
+                                 lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b,
+                                 dsum_below));
   return TT_OK;
 }
 
@@ -505,6 +517,11 @@ struct tt_model {
   // table's included, run as one grouped GEMM after the backward.
   std::vector<BwdIO> lio;
   GemmGroup dw_group;
+  // ... and leaves the column partials of its 2L+1 LayerNorm backwards in
+  // buffers of their own, added up by one launch after the backward
+  float *lnf_part = nullptr;
+  LnReduceEntry *ln_table = nullptr;   // device, 2L+1 entries
+  int n_ln = 0;
   // TT_FP16: dynamic loss scaling (device state; host-side policy)
   tt_loss_scale *ls = nullptr;
   int ls_interval = 1000;
@@ -689,6 +706,35 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
       rc = tt_gemm_group_plan(ctx, ent.data(), (int)ent.size(), N, &md->dw_group,
                               c.mode == TT_FP16);
     }
+    // LayerNorm partials: LN_f, then each layer's LN2 and LN1 from the top
+    // (the order the backward runs them; the table's order does not matter).
+    const size_t part_floats = (size_t)tt_layernorm_bwd_groups(N, c.C) * 3 * c.C;
+    std::vector<LnReduceEntry> lt;
+    const int lf = p_lnf_g(md);
+    md->lnf_part = (float *)alloc(part_floats * 4);
+    lt.push_back({md->lnf_part, md->g + md->off[lf], md->g + md->off[lf + 1],
+                  md->g + md->off[P_LAYER0 + PER_LAYER * (c.L - 1) + 11]});
+    for (int l = c.L - 1; l >= 0; --l) {
+      const int b = P_LAYER0 + PER_LAYER * l;
+      BwdIO &io = md->lio[l];
+      io.ln2_part = (float *)alloc(part_floats * 4);
+      io.ln1_part = (float *)alloc(part_floats * 4);
+      // LN2: gamma, beta, and the projection bias (column sums of its output)
+      lt.push_back({io.ln2_part, md->g + md->off[b + 6], md->g + md->off[b + 7],
+                    md->g + md->off[b + 5]});
+      // LN1: gamma, beta, and the down-projection bias of the block below
+      lt.push_back({io.ln1_part, md->g + md->off[b + 0], md->g + md->off[b + 1],
+                    l > 0 ? md->g + md->off[b - PER_LAYER + 11] : nullptr});
+    }
+    md->ln_table = (LnReduceEntry *)alloc(lt.size() * sizeof(LnReduceEntry));
+    md->n_ln = (int)lt.size();
+    if (rc == TT_OK) {
+      const hipError_t e1 = hipMemcpyAsync(md->ln_table, lt.data(), lt.size() * sizeof(LnReduceEntry),
+                                           hipMemcpyHostToDevice, ctx->stream);
+      // the host vector dies here: make sure the copy has read it
+      const hipError_t e2 = e1 == hipSuccess ? hipStreamSynchronize(ctx->stream) : e1;
+      if (e2 != hipSuccess) rc = tt_set_error(ctx, TT_EHIP, "model_create: %s", hipGetErrorString(e2));
+    }
   }
   for (float *buf : {md->w, md->g, md->m, md->v})
     if (rc == TT_OK) rc = tt_fill_f32(ctx, buf, md->n_slots, 0.f);
@@ -788,10 +834,15 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   // down-projection bias gradient of the block below it.
   auto fcp_bias = [&](int l) { return md->g + md->off[P_LAYER0 + PER_LAYER * l + 11]; };
   void *rl_top = grouped ? md->lio[c.L - 1].rl_in : md->Rl;
-  TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
-                               md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
-                               lp ? (bf16_t *)rl_top : nullptr, md->g + md->off[lf],
-                               md->g + md->off[lf + 1], fcp_bias(c.L - 1)));
+  if (grouped)
+    TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
+                                 md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
+                                 lp ? (bf16_t *)rl_top : nullptr, md->lnf_part));
+  else
+    TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
+                                 md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
+                                 lp ? (bf16_t *)rl_top : nullptr, md->g + md->off[lf],
+                                 md->g + md->off[lf + 1], fcp_bias(c.L - 1)));
   for (int l = c.L - 1; l >= 0; --l) {
     layer_views(md, l, w, wt, gr);
     const BwdIO io = grouped ? md->lio[l]
@@ -799,9 +850,13 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
     TT_TRY(layer_bwd(ctx, mode, B, T, C, c.NH, c.F, w, md->layers[l], md->xs[l], md->R, io, gr,
                      md->sc, false, l > 0 ? fcp_bias(l - 1) : nullptr, true));
   }
-  // Every weight-matrix gradient (stored, not accumulated) in one launch;
-  // then the token rows of the embedding add into the token table's.
-  if (grouped) TT_TRY(tt_gemm_group_run(ctx, md->dw_group, N));
+  // Every weight-matrix gradient (stored, not accumulated) in one launch, the
+  // LayerNorm parameter and the projection bias gradients in another; then
+  // the token rows of the embedding add into the token table's.
+  if (grouped) {
+    TT_TRY(tt_gemm_group_run(ctx, md->dw_group, N));
+    TT_TRY(tt_layernorm_bwd_reduce_batch(ctx, N, C, md->ln_table, md->n_ln));
+  }
   TT_TRY(tt_embed_bwd(ctx, B, T, C, c.V, tok, md->R, md->g + md->off[P_WTE],
                       md->g + md->off[P_WPE]));
   // TT_FP16: the gradients carry the loss scale; divide it out and flag

@@ -213,10 +213,8 @@ __global__ void __launch_bounds__(64 * lnb_waves(NV)) layernorm_bwd_kernel(
 // combines the groups, then one atomic per element and slice.
 constexpr int LNR_SLICE = 32;
 
-__global__ void __launch_bounds__(256) layernorm_bwd_reduce_kernel(int G, int C,
-                                                                   const float *__restrict__ part,
-                                                                   float *dg, float *db,
-                                                                   float *dsum) {
+__device__ __forceinline__ void ln_reduce_body(int G, int C, const float *__restrict__ part,
+                                               float *dg, float *db, float *dsum) {
   const int nf = 3 * C / 4;
   const int f = blockIdx.x * 64 + (threadIdx.x & 63);
   const int grp = threadIdx.x >> 6;
@@ -240,6 +238,22 @@ __global__ void __launch_bounds__(256) layernorm_bwd_reduce_kernel(int G, int C,
   unsafeAtomicAdd(&dst[col + 1], (a.y + b.y) + (c.y + d.y));
   unsafeAtomicAdd(&dst[col + 2], (a.z + b.z) + (c.z + d.z));
   unsafeAtomicAdd(&dst[col + 3], (a.w + b.w) + (c.w + d.w));
+}
+
+__global__ void __launch_bounds__(256) layernorm_bwd_reduce_kernel(int G, int C,
+                                                                   const float *__restrict__ part,
+                                                                   float *dg, float *db,
+                                                                   float *dsum) {
+  ln_reduce_body(G, C, part, dg, db, dsum);
+}
+
+// The same for several LayerNorm backward calls at once (one table entry per
+// call, blockIdx.z): the whole-model step defers its 2L+1 reductions to one
+// launch after the backward.
+__global__ void __launch_bounds__(256) layernorm_bwd_reduce_batch_kernel(
+    int G, int C, const LnReduceEntry *__restrict__ table) {
+  const LnReduceEntry e = table[blockIdx.z];
+  ln_reduce_body(G, C, e.part, e.dg, e.db, e.dsum);
 }
 
 // Vectorised column sums: each thread owns 16 bytes of a row (8 bf16 or 4
@@ -568,21 +582,22 @@ int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, co
   return TT_EUNSUPPORTED;
 }
 
-int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
-                          const float *mean, const float *rstd, const float *g, const float *dy,
-                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
-                          float *dsum) {
-  TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
-  TT_REQUIRE(ctx, x && mean && rstd && g && dy && dx, "layernorm_bwd: NULL pointer");
-  if (N == 0) return TT_OK;
+int tt_layernorm_bwd_groups(int N, int C) {
   const int nv = (C / 4 + 63) / 64;
   // the dispatched template width: the smallest of 1, 2, 3, 4, 8, 16 >= nv
   const int nvt = nv <= 4 ? nv : (nv <= 8 ? 8 : 16);
   const int rows_per_wg = lnb_waves(nvt) * lnb_rpw(nvt);
-  const int G = (N + rows_per_wg - 1) / rows_per_wg;
-  tt_scratch_scope scope(ctx);
-  void *part;
-  TT_TRY(tt_arena_alloc(ctx, (size_t)G * 3 * C * 4, &part));
+  return (N + rows_per_wg - 1) / rows_per_wg;
+}
+
+int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                          const float *mean, const float *rstd, const float *g, const float *dy,
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *part) {
+  TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
+  TT_REQUIRE(ctx, x && mean && rstd && g && dy && dx && part, "layernorm_bwd: NULL pointer");
+  if (N == 0) return TT_OK;
+  const int nv = (C / 4 + 63) / 64;
+  const int G = tt_layernorm_bwd_groups(N, C);
   {
     tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
                        (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
@@ -601,13 +616,40 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
     TT_LNB(1) TT_LNB(2) TT_LNB(3) TT_LNB(4) TT_LNB(8) TT_LNB(16) return TT_EUNSUPPORTED;
 #undef TT_LNB
   }
-  TT_TRY(tt_check_launch(ctx, "layernorm_bwd"));
+  return tt_check_launch(ctx, "layernorm_bwd");
+}
+
+int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                          const float *mean, const float *rstd, const float *g, const float *dy,
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
+                          float *dsum) {
+  TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
+  if (N == 0) return TT_OK;
+  const int G = tt_layernorm_bwd_groups(N, C);
+  tt_scratch_scope scope(ctx);
+  void *part;
+  TT_TRY(tt_arena_alloc(ctx, (size_t)G * 3 * C * 4, &part));
+  TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,
+                               (float *)part));
   if (!dg && !db && !dsum) return TT_OK;
   tt_prof_scope prof(ctx, "layernorm_bwd_reduce_kernel", 0.0, 12.0 * G * C + 24.0 * C);
   hipLaunchKernelGGL(layernorm_bwd_reduce_kernel,
                      dim3((3 * C / 4 + 63) / 64, (G + LNR_SLICE - 1) / LNR_SLICE), dim3(256), 0,
                      ctx->stream, G, C, (const float *)part, dg, db, dsum);
   return tt_check_launch(ctx, "layernorm_bwd_reduce");
+}
+
+int tt_layernorm_bwd_reduce_batch(tt_ctx *ctx, int N, int C, const LnReduceEntry *table, int n) {
+  TT_REQUIRE(ctx, table && n > 0 && n < 65536 && C > 0 && C % 4 == 0,
+             "layernorm_bwd_reduce_batch: bad arguments");
+  if (N == 0) return TT_OK;
+  const int G = tt_layernorm_bwd_groups(N, C);
+  tt_prof_scope prof(ctx, "layernorm_bwd_reduce_batch_kernel", 0.0,
+                     n * (12.0 * G * C + 24.0 * C));
+  hipLaunchKernelGGL(layernorm_bwd_reduce_batch_kernel,
+                     dim3((3 * C / 4 + 63) / 64, (G + LNR_SLICE - 1) / LNR_SLICE, n), dim3(256), 0,
+                     ctx->stream, G, C, table);
+  return tt_check_launch(ctx, "layernorm_bwd_reduce_batch");
 }
 
 int tt_colsum(tt_ctx *ctx, int fmt, int M, int N, int ld, const void *src, float *out) {

@@ -271,6 +271,21 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                           const float *mean, const float *rstd, const float *g, const float *dy,
                           const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
                           float *dsum = nullptr);
+// The same in two parts: tt_layernorm_bwd_rows writes dx (and its copy) and
+// the per-workgroup column partials of dg, db and dsum into part
+// ([tt_layernorm_bwd_groups(N, C)][3][C] floats); the partials are added into
+// the outputs later, for several calls at once, by
+// tt_layernorm_bwd_reduce_batch (table: device array of n entries, all with
+// the same N and C).
+struct LnReduceEntry {
+  const float *part;
+  float *dg, *db, *dsum;   // nullable each
+};
+int tt_layernorm_bwd_groups(int N, int C);
+int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                          const float *mean, const float *rstd, const float *g, const float *dy,
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *part);
+int tt_layernorm_bwd_reduce_batch(tt_ctx *ctx, int N, int C, const LnReduceEntry *table, int n);
 // Column sums out[n] += sum_m src[m, n]; fmt: the source's tt_mode (float32,
 // bf16 or binary16).
 int tt_colsum(tt_ctx *ctx, int fmt, int M, int N, int ld, const void *src, float *out);
