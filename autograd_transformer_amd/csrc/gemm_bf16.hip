@@ -356,37 +356,70 @@ struct DOp {
       const int kr0 = kk + 8 * lg + (lr >> 2);
       const int kr1 = kr0 + 4;
       const int pc0 = (c >> 3) ^ rswz(kr0), pc1 = (c >> 3) ^ rswz(kr1);
-      // Issued as inline assembly: through the builtin, the compiler puts a
-      // full vmcnt(0) wait in front of the read whenever a buffer-to-LDS load
-      // is in flight (it cannot tell the stages apart), which would drain the
-      // operand ring every stage.  The caller waits for these reads itself
-      // (lds_frags_ready) before using the fragments.
-      const uint32_t a0 = (uint32_t)(uintptr_t)(lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7));
-      const uint32_t a1 = (uint32_t)(uintptr_t)(lds_v4s *)(t + kr1 * ROWS + pc1 * 8 + (c & 7));
-      v4s lo, hi;
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
+      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7)));
+      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(t + kr1 * ROWS + pc1 * 8 + (c & 7)));
       typedef short v8s __attribute__((ext_vector_type(8)));
       v8s v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(bf16x8_t, v);
     }
   }
+
+  // Row-major operand: LDS byte address of the first of a fragment's two
+  // transpose reads.  The second is TR_STEP bytes further: its rows are 4
+  // further (k0 + 4 .. k0 + 7 with k0 % 8 < 4, so rswz and the swizzled
+  // chunk are the same).
+  static constexpr int TR_STEP = 4 * ROWS * 2;
+  __device__ __forceinline__ static uint32_t tr_addr(const bf16_t *t, int rb, int kk, int lr, int lg) {
+    const int c = rb + 4 * (lr & 3);
+    const int kr0 = kk + 8 * lg + (lr >> 2);
+    const int pc0 = (c >> 3) ^ rswz(kr0);
+    return (uint32_t)(uintptr_t)(lds_v4s *)(t + kr0 * ROWS + pc0 * 8 + (c & 7));
+  }
 };
 
-// Wait for every LDS read this wave has issued (lgkmcnt(0)) and tie the
-// fragments to that wait: each passes through an empty asm statement after
-// it, so no use of a fragment can be scheduled above the wait.  Needed after
-// the inline-assembly transpose reads, which the compiler does not track.
-template <int KS, int FM, int FN>
-__device__ __forceinline__ void lds_frags_ready(bf16x8_t (&fa)[KS][FM], bf16x8_t (&fb)[KS][FN]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[s][i]));
-#pragma unroll
-    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[s][j]));
-  }
+// The weight-gradient tile's fragments (256 x 128, 4 x 2 waves: four of A,
+// four of B per 32-deep stage, both operands row-major): 16 transpose reads
+// and their wait (lgkmcnt(0)) in ONE asm statement.  Through the builtin, the
+// compiler puts a full vmcnt(0) wait in front of a transpose read whenever a
+// buffer-to-LDS load is in flight (it cannot tell the ring's stages apart),
+// which would drain the ring every stage; it does not look into inline
+// assembly.  With the wait inside the statement, no fragment register can be
+// read (or copied) before its data has landed.
+__device__ __forceinline__ void tr_frags_4x4(const uint32_t (&aa)[4], const uint32_t (&ab)[4],
+                                             bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
+  v4s a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7),
+        "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(b4), "=&v"(b5), "=&v"(b6), "=&v"(b7)
+      : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ab[0]), "v"(ab[1]), "v"(ab[2]),
+        "v"(ab[3])
+      : "memory");
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  fa[0] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  fa[1] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(a2, a3, 0, 1, 2, 3, 4, 5, 6, 7));
+  fa[2] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(a4, a5, 0, 1, 2, 3, 4, 5, 6, 7));
+  fa[3] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(a6, a7, 0, 1, 2, 3, 4, 5, 6, 7));
+  fb[0] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  fb[1] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7));
+  fb[2] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(b4, b5, 0, 1, 2, 3, 4, 5, 6, 7));
+  fb[3] = __builtin_bit_cast(bf16x8_t, (v8s)__builtin_shufflevector(b6, b7, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
@@ -647,10 +680,29 @@ gemm_bf16_v3_kernel(GemmParams p) {
           if constexpr (MF - PER * RD > 0) __builtin_amdgcn_sched_group_barrier(0x008, MF - PER * RD, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+      } else if constexpr (!A_KM && !B_KM && BM == 256 && BN == 128 && WM == 4 && WN == 2 &&
+                           BKV == 32) {
+        // The weight-gradient tile: next stage issued, then the stage's
+        // transpose reads and their wait in one asm statement
+        // (tr_frags_4x4), then the MFMAs while those loads are in flight.
+        static_assert(FM == 4 && FN == 4 && OA::TR_STEP == 2048 && OB::TR_STEP == 1024,
+                      "tr_frags_4x4 hard-codes this tile's fragment counts and read offsets");
+        if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
+        uint32_t aa[4], ab[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aa[i] = OA::tr_addr(as, wm * C::WTM + i * 16, 0, lr, lg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ab[j] = OB::tr_addr(bs, wn * C::WTN + j * 16, 0, lr, lg);
+        bf16x8_t fa[4], fb[4];
+        tr_frags_4x4(aa, ab, fa, fb);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = lp_mfma<F16>(fa[i], fb[j], acc[i][j]);
       } else {
-        // A transposed operand: the stage's fragments are read, the next
-        // stage's loads issued, then the reads waited for (lds_frags_ready)
-        // and the MFMAs run while those loads are in flight.
+        // Other tiles with a row-major operand (the builtin transpose read;
+        // the compiler's vmcnt(0) in front of it then drains the ring, so
+        // the next stage is issued after the reads): not on the step's path.
         constexpr int KS = BKV / 32;
         bf16x8_t fa[KS][FM], fb[KS][FN];
 #pragma unroll
@@ -662,7 +714,6 @@ gemm_bf16_v3_kernel(GemmParams p) {
         }
         asm volatile("" ::: "memory");
         if (it + NS - 1 < nk) issue(it + NS - 1, (it + NS - 1) % NS);
-        lds_frags_ready<KS, FM, FN>(fa, fb);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
