@@ -438,7 +438,7 @@ def main():
         f"(wall {wall:.2f}s)  loss {last_loss:.4f}")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "gpt2-124m" else METRIC.replace("GPT-2 124M", "GPT-2 350M"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
