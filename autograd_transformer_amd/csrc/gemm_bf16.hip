@@ -596,8 +596,8 @@ gemm_bf16_v3_kernel(GemmParams p) {
     p.lda = q.lda; p.ldb = q.ldb; p.ldo = q.ldo;
     p.M = q.M; p.N = q.N; p.n_valid = q.N;
     p.tiles_m = q.tiles_m; p.tiles_n = q.tiles_n; p.vec_out = q.vec_out;
-    p.a_bytes = (uint32_t)(((size_t)(p.K - 1) * q.lda + q.M) * 2);
-    p.b_bytes = (uint32_t)(((size_t)(p.K - 1) * q.ldb + q.N) * 2);
+    p.a_bytes = (uint32_t)gemm_extent_bytes(false, q.M, p.K, q.lda);
+    p.b_bytes = (uint32_t)gemm_extent_bytes(false, q.N, p.K, q.ldb);
     tile_coords(bid - q.tile0, q.tiles_m * q.tiles_n, q.tiles_m, q.tiles_n, q.raster_n, tm, tn,
                 false);
   } else {

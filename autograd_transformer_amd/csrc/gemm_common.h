@@ -174,9 +174,16 @@ inline double gemm_bytes(const GemmArgs &g) {
   return b;
 }
 
-// Bytes spanned by an operand: rows x reduction, k-major or row-major.
-inline size_t gemm_extent_bytes(bool kmajor, int rows, int K, int ld) {
-  return kmajor ? ((size_t)(rows - 1) * ld + K) * 2 : ((size_t)(K - 1) * ld + rows) * 2;
+// Bytes spanned by an operand: rows x reduction, k-major or row-major,
+// rounded up to whole dwords.  The buffer range check works per dword: an
+// extent ending inside a dword would read that dword -- and so the operand's
+// last element -- as 0.  The element the rounding adds is, for a row-major
+// operand, column `rows` of its last k row (it reaches only an output that is
+// not stored); for a k-major one, k = K of its last row (it meets the other
+// operand's rows past K, which read 0 through that operand's own check).
+__host__ __device__ inline size_t gemm_extent_bytes(bool kmajor, int rows, int K, int ld) {
+  const size_t elems = kmajor ? (size_t)(rows - 1) * ld + K : (size_t)(K - 1) * ld + rows;
+  return ((elems + 1) & ~(size_t)1) * 2;
 }
 
 }  // namespace tt_gemm_detail

@@ -147,6 +147,30 @@ def test_linear_bwd(ctx, mode, shape):
     assert rel_l2(host(db), db0 + db_ref) <= tol(mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_linear_bwd_last_element(ctx, mode):
+    """The last token's gradient in the last of an odd number of columns: the
+    only nonzero of dY.  dW's last column is then exactly that token's input
+    row, db's last entry 1 -- an operand range that ended inside its last
+    dword once read that element as 0."""
+    M, K, N = 33, 16, 17
+    x = _inputs(mode, (M, K), 120)
+    W = _inputs(mode, (K, N), 121, 0.1)
+    dy = np.zeros((M, N))
+    dy[M - 1, N - 1] = 1.0
+    X, Wd, dY = dev(x, lowp(mode)), dev(W, lowp(mode)), dev(dy, lowp(mode))
+    dX, dW, db = empty((M, K)), zeros((K, N)), zeros((N,))
+    if _fp16_refused(ctx, mode, K, N, lambda: tt.tt_linear_bwd(ctx, mode, M, K, N, X, Wd, dY, dX,
+                                                               dW, db)):
+        return
+    tt.tt_linear_bwd(ctx, mode, M, K, N, X, Wd, dY, dX, dW, db)
+    sync()
+    got = host(dW)
+    assert np.array_equal(got[:, N - 1], x[M - 1])
+    assert not np.any(got[:, : N - 1])
+    assert host(db)[N - 1] == 1.0 and not np.any(host(db)[: N - 1])
+
+
 # --------------------------------------------------------------- layernorm
 
 @pytest.mark.parametrize("mode", MODES)
