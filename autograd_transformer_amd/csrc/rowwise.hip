@@ -207,6 +207,148 @@ __global__ void __launch_bounds__(64 * lnb_waves(NV)) layernorm_bwd_kernel(
   }
 }
 
+// LayerNorm backward for rows of at most 1024 columns (NV <= 4): the same
+// arithmetic and partial-sum layout as above, but each wave walks a strided
+// list of rows with two rows' loads in flight while it computes and stores
+// the one before them, so a workgroup's reads and writes overlap (the
+// one-round kernel above reads every row of the grid, then writes them all).
+// Workgroup g owns rows [g R, (g + 1) R), R = 4 RPW; wave w takes rows
+// g R + w, g R + w + 4, ... (RPW of them).  The walk is unrolled and has no
+// branches (rows past the workgroup's end read zero, contribute zero and their
+// stores fall outside the buffer range), so the compiler sees straight-line
+// code and waits, before each row, only for that row's own loads.
+constexpr int LNP_WAVES = 4;
+constexpr int LNP_MAX_WG = 512;   // two workgroups per CU
+
+// rows per wave: the smallest of 2, 4, 8 that keeps the grid within
+// LNP_MAX_WG workgroups (8 beyond that)
+__host__ __device__ constexpr int lnp_rpw(int N) {
+  return N <= LNP_MAX_WG * LNP_WAVES * 2 ? 2 : (N <= LNP_MAX_WG * LNP_WAVES * 4 ? 4 : 8);
+}
+
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
+
+template <int NV>
+struct LnRow {
+  float4 x[NV], d[NV], r[NV];
+  float mu, rs;
+};
+
+template <int NV, int RPW, bool F16 = false>
+__global__ void __launch_bounds__(64 * LNP_WAVES) layernorm_bwd_pipe_kernel(
+    int N, int C, const float *__restrict__ x, const float *__restrict__ mean,
+    const float *__restrict__ rstd, const float *__restrict__ gamma, const float *__restrict__ dy,
+    const float *dres, float *dx, bf16_t *__restrict__ dx_bf16, float *__restrict__ part) {
+  __shared__ float4 red[LNP_WAVES][3][NV * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nv = C >> 2;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float inv_c = 1.0f / (float)C;
+  const int r0 = blockIdx.x * (RPW * LNP_WAVES), r1 = min(N, r0 + RPW * LNP_WAVES);
+  // one resource per tensor over the workgroup's rows; columns past C and
+  // rows past r1 take an out-of-range offset and read zero
+  const size_t base = (size_t)r0 * C;
+  const uint32_t bytes = (uint32_t)max(0, r1 - r0) * C * 4;
+  const __amdgpu_buffer_rsrc_t rx = ln_rsrc(x + base, bytes), rd = ln_rsrc(dy + base, bytes),
+                               rr = ln_rsrc(dres ? dres + base : x, dres ? bytes : 0u),
+                               wx = ln_rsrc(dx + base, bytes);
+  // the bf16 copy's resource has no range when there is no copy: its stores drop
+  const __amdgpu_buffer_rsrc_t wb =
+      ln_rsrc(dx_bf16 ? (const float *)(dx_bf16 + base) : dx, dx_bf16 ? bytes / 2 : 0u);
+  float4 ga[NV], pg[NV], pb[NV], ps[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + i * 64;
+    ga[i] = c < nv ? ((const float4 *)gamma)[c] : z4;
+    pg[i] = z4; pb[i] = z4; ps[i] = z4;
+  }
+  auto issue = [&](LnRow<NV> &t, int row) {
+    const bool ok = row < r1;
+    const int lrow = row - r0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + i * 64;
+      const uint32_t off = ok && c < nv ? (uint32_t)(lrow * C + 4 * c) * 4u : LN_OOB;
+      t.x[i] = ln_load4(rx, off);
+      t.d[i] = ln_load4(rd, off);
+      t.r[i] = ln_load4(rr, off);
+    }
+    const int rc = min(row, N - 1);
+    t.mu = mean[rc];
+    t.rs = rstd[rc];
+  };
+  auto process = [&](const LnRow<NV> &t, int row) {
+    float4 xh[NV], gg[NV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float4 d = t.d[i], xq = t.x[i];
+      xh[i] = make_float4((xq.x - t.mu) * t.rs, (xq.y - t.mu) * t.rs, (xq.z - t.mu) * t.rs,
+                          (xq.w - t.mu) * t.rs);
+      gg[i] = make_float4(d.x * ga[i].x, d.y * ga[i].y, d.z * ga[i].z, d.w * ga[i].w);
+      s1 += (gg[i].x + gg[i].y) + (gg[i].z + gg[i].w);
+      s2 += (gg[i].x * xh[i].x + gg[i].y * xh[i].y) + (gg[i].z * xh[i].z + gg[i].w * xh[i].w);
+      pg[i].x += d.x * xh[i].x; pg[i].y += d.y * xh[i].y;
+      pg[i].z += d.z * xh[i].z; pg[i].w += d.w * xh[i].w;
+      pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
+    }
+    const float m1 = wave_sum(s1) * inv_c;
+    const float m2 = wave_sum(s2) * inv_c;
+    // branch-free stores: columns past C take an out-of-range offset (and
+    // their partial-sum lanes are never written out)
+    const int lrow = row - r0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + i * 64;
+      const bool cok = c < nv;
+      float4 o;
+      o.x = t.rs * (gg[i].x - m1 - xh[i].x * m2) + t.r[i].x;
+      o.y = t.rs * (gg[i].y - m1 - xh[i].y * m2) + t.r[i].y;
+      o.z = t.rs * (gg[i].z - m1 - xh[i].z * m2) + t.r[i].z;
+      o.w = t.rs * (gg[i].w - m1 - xh[i].w * m2) + t.r[i].w;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, o), wx,
+                                             cok ? (uint32_t)(lrow * C + 4 * c) * 4u : LN_OOB, 0, 0);
+      const uint32_t lo = lp_pack2<F16>(o.x, o.y), hi = lp_pack2<F16>(o.z, o.w);
+      v2u32_t pk = {lo, hi};
+      __builtin_amdgcn_raw_buffer_store_b64(pk, wb, cok ? (uint32_t)(lrow * C + 4 * c) * 2u : LN_OOB,
+                                            0, 0);
+      // column sums of dx as stored (the bf16 copy when there is one)
+      if (dx_bf16) o = make_float4(lp_lo<F16>(lo), lp_hi<F16>(lo), lp_lo<F16>(hi), lp_hi<F16>(hi));
+      ps[i].x += o.x; ps[i].y += o.y; ps[i].z += o.z; ps[i].w += o.w;
+    }
+  };
+  LnRow<NV> t[RPW];
+  const int row = r0 + wave;
+  issue(t[0], row);
+  if constexpr (RPW > 1) issue(t[1], row + LNP_WAVES);
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    process(t[k], row + k * LNP_WAVES);
+    if (k + 2 < RPW) issue(t[k + 2], row + (k + 2) * LNP_WAVES);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + i * 64;
+    red[wave][0][c] = pg[i];
+    red[wave][1][c] = pb[i];
+    red[wave][2][c] = ps[i];
+  }
+  __syncthreads();
+  float4 *out = (float4 *)(part + (size_t)blockIdx.x * 3 * C);
+  for (int f = threadIdx.x; f < 3 * nv; f += 64 * LNP_WAVES) {
+    const int k = f / nv, c = f % nv;
+    float4 a = red[0][k][c];
+#pragma unroll
+    for (int w = 1; w < LNP_WAVES; ++w) {
+      const float4 b = red[w][k][c];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    out[f] = a;
+  }
+}
+
 // out_k[c] += sum_g part[g][k][c] for k = 0 (dgamma), 1 (dbeta), 2 (dx
 // column sums); a NULL output is skipped.  Thread: one float4 of the [3][C]
 // partial row, one of 4 row groups of a 32-row slice of the partials; LDS
@@ -584,8 +726,12 @@ int tt_layernorm_fwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, co
 
 int tt_layernorm_bwd_groups(int N, int C) {
   const int nv = (C / 4 + 63) / 64;
-  // the dispatched template width: the smallest of 1, 2, 3, 4, 8, 16 >= nv
-  const int nvt = nv <= 4 ? nv : (nv <= 8 ? 8 : 16);
+  if (nv <= 4) {   // the row-walking kernel: 4 waves x lnp_rpw(N) rows per workgroup
+    const int R = LNP_WAVES * lnp_rpw(N);
+    return (N + R - 1) / R;
+  }
+  // the dispatched template width: the smallest of 8, 16 >= nv
+  const int nvt = nv <= 8 ? 8 : 16;
   const int rows_per_wg = lnb_waves(nvt) * lnb_rpw(nvt);
   return (N + rows_per_wg - 1) / rows_per_wg;
 }
@@ -598,10 +744,26 @@ int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
   if (N == 0) return TT_OK;
   const int nv = (C / 4 + 63) / 64;
   const int G = tt_layernorm_bwd_groups(N, C);
+  const int rpw = lnp_rpw(N);   // rows per wave of the row-walking kernel (nv <= 4)
   {
     tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
                        (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
                            8.0 * N + 12.0 * G * C);
+#define TT_LNP_RPW(NV, RPW)                                                               \
+      if (rpw == RPW) {                                                                   \
+        if (mode == TT_FP16)                                                              \
+          hipLaunchKernelGGL((layernorm_bwd_pipe_kernel<NV, RPW, true>), dim3(G),         \
+                             dim3(64 * LNP_WAVES), 0, ctx->stream, N, C, x, mean, rstd, g, dy, \
+                             dres, dx, dx_bf16, (float *)part);                           \
+        else                                                                              \
+          hipLaunchKernelGGL((layernorm_bwd_pipe_kernel<NV, RPW>), dim3(G),               \
+                             dim3(64 * LNP_WAVES), 0, ctx->stream, N, C, x, mean, rstd, g, dy, \
+                             dres, dx, dx_bf16, (float *)part);                           \
+      } else
+#define TT_LNP(NV)                                                                        \
+    if (nv <= NV) {                                                                       \
+      TT_LNP_RPW(NV, 2) TT_LNP_RPW(NV, 4) TT_LNP_RPW(NV, 8) return TT_EUNSUPPORTED;       \
+    } else
 #define TT_LNB(NV)                                                                        \
     if (nv <= NV) {                                                                       \
       if (mode == TT_FP16)                                                              \
@@ -613,7 +775,9 @@ int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                            ctx->stream, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,    \
                            (float *)part);                                                \
     } else
-    TT_LNB(1) TT_LNB(2) TT_LNB(3) TT_LNB(4) TT_LNB(8) TT_LNB(16) return TT_EUNSUPPORTED;
+    TT_LNP(1) TT_LNP(2) TT_LNP(3) TT_LNP(4) TT_LNB(8) TT_LNB(16) return TT_EUNSUPPORTED;
+#undef TT_LNP
+#undef TT_LNP_RPW
 #undef TT_LNB
   }
   return tt_check_launch(ctx, "layernorm_bwd");

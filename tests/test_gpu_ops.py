@@ -174,7 +174,8 @@ def test_linear_bwd_last_element(ctx, mode):
 # --------------------------------------------------------------- layernorm
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("NC", [(1, 4), (37, 768), (1000, 1024), (5, 4096), (300, 36)])
+@pytest.mark.parametrize("NC", [(1, 4), (37, 768), (1000, 1024), (5, 4096), (300, 36),
+                                (4099, 768), (8195, 100)])
 def test_layernorm(ctx, mode, NC):
     N, C = NC
     x = syn.normal(120, (N, C), 2.0) + 0.5
