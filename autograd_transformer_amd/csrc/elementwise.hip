@@ -87,16 +87,23 @@ __global__ void __launch_bounds__(256) adamw_kernel(size_t n, float *__restrict_
   const size_t n4 = n / 4;
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
-    float4 W = ((float4 *)w)[i], G = ((const float4 *)g)[i];
-    float4 Mv = ((float4 *)m)[i], Vv = ((float4 *)v)[i];
+    // Every byte is touched once: non-temporal (streaming) loads and stores
+    // keep the 30 bytes per parameter from displacing cached data (measured
+    // 0.697 -> 0.683 ms per 124M-parameter update).
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f w_ = __builtin_nontemporal_load((const v4f *)w + i), g_ = __builtin_nontemporal_load((const v4f *)g + i);
+    const v4f m_ = __builtin_nontemporal_load((const v4f *)m + i), v_ = __builtin_nontemporal_load((const v4f *)v + i);
+    float4 W = make_float4(w_[0], w_[1], w_[2], w_[3]), G = make_float4(g_[0], g_[1], g_[2], g_[3]);
+    float4 Mv = make_float4(m_[0], m_[1], m_[2], m_[3]), Vv = make_float4(v_[0], v_[1], v_[2], v_[3]);
     adamw_one(W.x, G.x, Mv.x, Vv.x, lr, b1, b2, eps, wd, rbc1, rbc2);
     adamw_one(W.y, G.y, Mv.y, Vv.y, lr, b1, b2, eps, wd, rbc1, rbc2);
     adamw_one(W.z, G.z, Mv.z, Vv.z, lr, b1, b2, eps, wd, rbc1, rbc2);
     adamw_one(W.w, G.w, Mv.w, Vv.w, lr, b1, b2, eps, wd, rbc1, rbc2);
-    ((float4 *)w)[i] = W;
-    ((float4 *)m)[i] = Mv;
-    ((float4 *)v)[i] = Vv;
-    if (wl) ((uint2 *)wl)[i] = make_uint2(lp_pack2<F16>(W.x, W.y), lp_pack2<F16>(W.z, W.w));
+    __builtin_nontemporal_store((v4f){W.x, W.y, W.z, W.w}, (v4f *)w + i);
+    __builtin_nontemporal_store((v4f){Mv.x, Mv.y, Mv.z, Mv.w}, (v4f *)m + i);
+    __builtin_nontemporal_store((v4f){Vv.x, Vv.y, Vv.z, Vv.w}, (v4f *)v + i);
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    if (wl) __builtin_nontemporal_store((v2u){lp_pack2<F16>(W.x, W.y), lp_pack2<F16>(W.z, W.w)}, (v2u *)wl + i);
   }
   // tail
   for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
