@@ -156,6 +156,7 @@ struct BwdIO {
   // non-NULL: the LayerNorm backward leaves its column partials here and the
   // caller adds them up later (tt_layernorm_bwd_reduce_batch)
   float *ln2_part = nullptr, *ln1_part = nullptr;
+  int part_groups = 0;   // capacity of each partial buffer, in groups
 };
 
 // Block backward, in place on the residual gradient R (fp32): on entry R
@@ -188,7 +189,7 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   // attention projection's bias gradient.
   if (io.ln2_part)
     TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
-                                 lp ? (bf16_t *)io.rl_mid : nullptr, io.ln2_part));
+                                 lp ? (bf16_t *)io.rl_mid : nullptr, io.ln2_part, io.part_groups));
   else
     TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, s.x1, s.mean2, s.rstd2, w.ln2_g, sc.dtmp, R, R,
                                  lp ? (bf16_t *)io.rl_mid : nullptr, gr.ln2_g, gr.ln2_b, gr.b_proj));
@@ -210,7 +211,7 @@ int layer_bwd(tt_ctx *ctx, tt_mode mode, int B, int T, int C, int NH, int F,
   // LN1 backward + residual.
   if (io.ln1_part)
     TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
-                                 lp ? (bf16_t *)io.rl_out : nullptr, io.ln1_part));
+                                 lp ? (bf16_t *)io.rl_out : nullptr, io.ln1_part, io.part_groups));
   else
     TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, x, s.mean1, s.rstd1, w.ln1_g, sc.dtmp, R, R,
                                  lp ? (bf16_t *)io.rl_out : nullptr, gr.ln1_g, gr.ln1_b,
@@ -383,37 +384,117 @@ extern "C" int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int 
   TT_REQUIRE(ctx, tt_aligned16(h) && tt_aligned16(wte), "lmhead_ce: alignment");
   const int ld = (V + 63) / 64 * 64;
   tt_scratch_scope scope(ctx);
-  void *logits, *rows;
+  void *logits, *rows, *wte_t = nullptr;
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * ld * esize(mode), &logits));
   TT_TRY(tt_arena_alloc(ctx, (size_t)N * 4, &rows));
-  return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, nullptr, 0, targets, loss, dh, dwte,
+  if (tt_lowp(mode)) {
+    // The 16-bit token table transposed, [C, ld] with zero columns V .. ld-1,
+    // so that dh = dz · wte reads both operands k-major (the whole-model
+    // step's kernels); one launch.
+    TT_TRY(tt_arena_alloc(ctx, (size_t)C * ld * 2, &wte_t));
+    tt_tdesc_set ts;
+    TT_TRY(tt_tdesc_set_add(ts, (const bf16_t *)wte, (bf16_t *)wte_t, V, C, ld));
+    TT_TRY(tt_transpose_bf16_set(ctx, ts));
+  }
+  return lmhead_ce_core(ctx, mode, N, C, V, ld, h, wte, wte_t, ld, targets, loss, dh, dwte,
                         logits, (float *)rows, false);
 }
 
 // ------------------------------------------------------------ block ABI
 
+// In TT_BF16 / TT_FP16 the block runs the same kernels as the whole-model
+// step: the forward products read transposed 16-bit copies of the four
+// weight matrices (rebuilt from the caller's weights on every forward, one
+// launch), and the backward leaves its four weight gradients to one grouped
+// launch after the activation gradients are done.
 struct tt_block_saved {
   uint32_t magic;
   tt_block_cfg cfg;
   LayerBufs s;
   float *xin;  // copy of the block input (LN1's backward needs it)
+  bf16_t *wt = nullptr;       // 16-bit modes: Wqkvᵀ [3C,C], Wpᵀ [C,C], Wfcᵀ [F,C], Wfpᵀ [C,F]
+  GemmGroup dw;               // 16-bit modes: the four weight-gradient products
+  std::vector<GemmGroupEntry> dw_host;   // what dw's device table holds
 };
+
+namespace {
+
+// Scratch of one block backward in the 16-bit modes, carved in this order
+// from the arena at the reset point, so its addresses repeat from call to
+// call (and the grouped-gradient table rarely needs an upload).
+struct BlockBwdScratch {
+  BwdScratch sc;
+  void *rl_in = nullptr, *rl_mid = nullptr;
+};
+
+int alloc_block_bwd(tt_ctx *ctx, const tt_block_cfg &c, BlockBwdScratch &b) {
+  const int N = c.B * c.T;
+  TT_TRY(alloc_bwd_scratch(ctx, c.mode, N, c.C, c.F, c.B, c.NH, c.T, b.sc));
+  if (tt_lowp(c.mode)) {
+    TT_TRY(tt_arena_alloc(ctx, (size_t)N * c.C * 2, &b.rl_in));
+    TT_TRY(tt_arena_alloc(ctx, (size_t)N * c.C * 2, &b.rl_mid));
+  }
+  return TT_OK;
+}
+
+// The four weight-gradient products of a block: dW = Xᵀ · dY.
+std::vector<GemmGroupEntry> block_dw_entries(const tt_block_cfg &c, const LayerBufs &s,
+                                             const BlockBwdScratch &b, const tt_block_g *g) {
+  const int C = c.C, F = c.F;
+  std::vector<GemmGroupEntry> ent;
+  auto prod = [&](const void *X, int ldx, int rows, const void *dY, int ldy, int cols, float *out) {
+    GemmGroupEntry e{};
+    e.A = X; e.lda = ldx; e.M = rows;
+    e.B = dY; e.ldb = ldy; e.N = cols;
+    e.out = out; e.ldo = cols;
+    ent.push_back(e);
+  };
+  prod(s.g, F, F, b.rl_in, C, C, g->w_fcp);
+  prod(s.ln2, C, C, b.sc.dh, F, F, g->w_fc);
+  prod(s.att, C, C, b.rl_mid, C, C, g->w_proj);
+  prod(s.ln1, C, C, b.sc.dqkv, 3 * C, 3 * C, g->w_qkv);
+  return ent;
+}
+
+}  // namespace
 
 extern "C" int tt_block_saved_create(tt_ctx *ctx, const tt_block_cfg *cfg, tt_block_saved **out) {
   TT_TRY(tt_check_ctx(ctx));
   TT_TRY(check_block_cfg(ctx, cfg));
   TT_REQUIRE(ctx, out != nullptr, "block_saved_create: out is NULL");
+  const tt_block_cfg c = *cfg;
+  const size_t save = ctx->offset;
   tt_block_saved *sv = new tt_block_saved();
   sv->magic = TT_SAVED_MAGIC;
-  sv->cfg = *cfg;
+  sv->cfg = c;
   void *p = nullptr;
-  int rc = alloc_layer(ctx, cfg->mode, cfg->B * cfg->T, cfg->C, cfg->F, cfg->B, cfg->NH, cfg->T, sv->s);
-  if (rc == TT_OK) rc = tt_arena_alloc(ctx, (size_t)cfg->B * cfg->T * cfg->C * 4, &p);
+  const int N = c.B * c.T;
+  int rc = alloc_layer(ctx, c.mode, N, c.C, c.F, c.B, c.NH, c.T, sv->s);
+  if (rc == TT_OK) rc = tt_arena_alloc(ctx, (size_t)N * c.C * 4, &p);
+  sv->xin = (float *)p;
+  if (rc == TT_OK && tt_lowp(c.mode)) {
+    rc = tt_arena_alloc(ctx, ((size_t)4 * c.C * c.C + 2 * (size_t)c.C * c.F) * 2, &p);
+    sv->wt = (bf16_t *)p;
+    if (rc == TT_OK) {
+      // Plan the grouped weight gradients once: the device tables persist
+      // with the saved buffers, and each backward points the entries at its
+      // own scratch and the caller's gradients (the plan needs the shapes
+      // only; any aligned address stands in until then, nothing runs on it).
+      BlockBwdScratch b;
+      b.sc.dh = b.sc.dqkv = b.rl_in = b.rl_mid = sv->xin;
+      tt_block_g gdum;
+      gdum.w_qkv = gdum.w_proj = gdum.w_fc = gdum.w_fcp = sv->xin;
+      sv->dw_host = block_dw_entries(c, sv->s, b, &gdum);
+      rc = tt_gemm_group_plan(ctx, sv->dw_host.data(), (int)sv->dw_host.size(), N, &sv->dw,
+                              c.mode == TT_FP16);
+    }
+  }
   if (rc != TT_OK) {
+    ctx->offset = save;
+    sv->magic = 0;
     delete sv;
     return rc;
   }
-  sv->xin = (float *)p;
   *out = sv;
   return TT_OK;
 }
@@ -426,21 +507,42 @@ static int check_block_w(tt_ctx *ctx, const tt_block_w *w) {
   return TT_OK;
 }
 
+static int check_saved(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_saved *saved,
+                       const char *what) {
+  if (saved->magic != TT_SAVED_MAGIC) return tt_set_error(ctx, TT_ESTALE, "%s: stale saved", what);
+  TT_REQUIRE(ctx, saved->cfg.B == cfg->B && saved->cfg.T == cfg->T && saved->cfg.C == cfg->C &&
+                      saved->cfg.NH == cfg->NH && saved->cfg.F == cfg->F &&
+                      saved->cfg.mode == cfg->mode,
+             "%s: saved buffers were made for another shape", what);
+  return TT_OK;
+}
+
 extern "C" int tt_block_fwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
                             const float *x, float *y, tt_block_saved *saved) {
   TT_TRY(tt_check_ctx(ctx));
   TT_TRY(check_block_cfg(ctx, cfg));
   TT_TRY(check_block_w(ctx, w));
   TT_REQUIRE(ctx, x && y && saved, "block_fwd: NULL pointer");
-  if (saved->magic != TT_SAVED_MAGIC) return tt_set_error(ctx, TT_ESTALE, "block_fwd: stale saved");
-  TT_REQUIRE(ctx, saved->cfg.B == cfg->B && saved->cfg.T == cfg->T && saved->cfg.C == cfg->C &&
-                      saved->cfg.F == cfg->F && saved->cfg.mode == cfg->mode,
-             "block_fwd: saved buffers were made for another shape");
-  hipError_t e = hipMemcpyAsync(saved->xin, x, (size_t)cfg->B * cfg->T * cfg->C * 4,
+  TT_TRY(check_saved(ctx, cfg, saved, "block_fwd"));
+  const int C = cfg->C, F = cfg->F;
+  hipError_t e = hipMemcpyAsync(saved->xin, x, (size_t)cfg->B * cfg->T * C * 4,
                                 hipMemcpyDeviceToDevice, ctx->stream);
   if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_fwd copy: %s", hipGetErrorString(e));
-  return layer_fwd(ctx, cfg->mode, cfg->B, cfg->T, cfg->C, cfg->NH, cfg->F, cfg->ln_eps, *w,
-                   LayerWT(), saved->xin, y, saved->s);
+  LayerWT wt;
+  if (saved->wt) {
+    // transposed 16-bit weights: [K, N] -> [N, K], one launch for the four
+    bf16_t *q = saved->wt, *pj = q + (size_t)3 * C * C, *fc = pj + (size_t)C * C,
+           *fp = fc + (size_t)F * C;
+    tt_tdesc_set ts;
+    TT_TRY(tt_tdesc_set_add(ts, (const bf16_t *)w->w_qkv, q, C, 3 * C, C));
+    TT_TRY(tt_tdesc_set_add(ts, (const bf16_t *)w->w_proj, pj, C, C, C));
+    TT_TRY(tt_tdesc_set_add(ts, (const bf16_t *)w->w_fc, fc, C, F, C));
+    TT_TRY(tt_tdesc_set_add(ts, (const bf16_t *)w->w_fcp, fp, F, C, F));
+    TT_TRY(tt_transpose_bf16_set(ctx, ts));
+    wt.w_qkv = q; wt.w_proj = pj; wt.w_fc = fc; wt.w_fcp = fp;
+  }
+  return layer_fwd(ctx, cfg->mode, cfg->B, cfg->T, C, cfg->NH, F, cfg->ln_eps, *w, wt, saved->xin,
+                   y, saved->s);
 }
 
 extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
@@ -450,28 +552,44 @@ extern "C" int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block
   TT_TRY(check_block_cfg(ctx, cfg));
   TT_TRY(check_block_w(ctx, w));
   TT_REQUIRE(ctx, saved && dy && dx && g, "block_bwd: NULL pointer");
-  if (saved->magic != TT_SAVED_MAGIC) return tt_set_error(ctx, TT_ESTALE, "block_bwd: stale saved");
+  TT_TRY(check_saved(ctx, cfg, saved, "block_bwd"));
   TT_REQUIRE(ctx, g->ln1_g && g->ln1_b && g->w_qkv && g->b_qkv && g->w_proj && g->b_proj &&
                       g->ln2_g && g->ln2_b && g->w_fc && g->b_fc && g->w_fcp && g->b_fcp,
              "block_bwd: a gradient pointer is NULL");
   const tt_mode mode = cfg->mode;
   const int N = cfg->B * cfg->T, C = cfg->C;
+  const bool lp = tt_lowp(mode);
   tt_scratch_scope scope(ctx);
-  BwdScratch sc;
-  TT_TRY(alloc_bwd_scratch(ctx, mode, N, C, cfg->F, cfg->B, cfg->NH, cfg->T, sc));
+  BlockBwdScratch b;
+  TT_TRY(alloc_block_bwd(ctx, *cfg, b));
   // R = dy (in place on dx from here on)
   if (dx != dy) {
     hipError_t e = hipMemcpyAsync(dx, dy, (size_t)N * C * 4, hipMemcpyDeviceToDevice, ctx->stream);
     if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "block_bwd copy: %s", hipGetErrorString(e));
   }
-  void *Rl = dx;
-  if (tt_lowp(mode)) {
-    TT_TRY(tt_arena_alloc(ctx, (size_t)N * C * 2, &Rl));
-    TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)Rl, mode == TT_FP16));
+  if (!lp) {
+    const BwdIO io{dx, dx, dx, b.sc.dh, b.sc.dqkv, false};
+    return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx,
+                     io, *g, b.sc, true, nullptr, false);
   }
-  const BwdIO io{Rl, Rl, Rl, sc.dh, sc.dqkv, false};
-  return layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, io,
-                   *g, sc, true, nullptr, false);
+  // 16-bit modes: the activation gradients the weight gradients read stay
+  // apart (rl_in: dy's copy; rl_mid: the LN2 backward's output; dh; dqkv),
+  // and the four weight gradients run as one grouped launch at the end.
+  TT_TRY(tt_cast_f32_bf16(ctx, (size_t)N * C, dx, (bf16_t *)b.rl_in, mode == TT_FP16));
+  const BwdIO io{b.rl_in, b.rl_mid, nullptr, b.sc.dh, b.sc.dqkv, true};
+  TT_TRY(layer_bwd(ctx, mode, cfg->B, cfg->T, C, cfg->NH, cfg->F, *w, saved->s, saved->xin, dx, io,
+                   *g, b.sc, true, nullptr, false));
+  tt_block_saved *sv = const_cast<tt_block_saved *>(saved);
+  const std::vector<GemmGroupEntry> ent = block_dw_entries(*cfg, saved->s, b, g);
+  bool same = ent.size() == sv->dw_host.size();
+  for (size_t i = 0; same && i < ent.size(); ++i)
+    same = ent[i].A == sv->dw_host[i].A && ent[i].B == sv->dw_host[i].B &&
+           ent[i].out == sv->dw_host[i].out;
+  if (!same) {
+    TT_TRY(tt_gemm_group_update(ctx, sv->dw, ent.data(), (int)ent.size(), N));
+    sv->dw_host = ent;
+  }
+  return tt_gemm_group_run(ctx, sv->dw, N, true);
 }
 
 extern "C" void tt_block_saved_destroy(tt_block_saved *saved) {
@@ -522,6 +640,7 @@ struct tt_model {
   float *lnf_part = nullptr;
   LnReduceEntry *ln_table = nullptr;   // device, 2L+1 entries
   int n_ln = 0;
+  int ln_part_groups = 0;   // capacity of each partial buffer (every N <= B_max T_max)
   // TT_FP16: dynamic loss scaling (device state; host-side policy)
   tt_loss_scale *ls = nullptr;
   int ls_interval = 1000;
@@ -636,7 +755,8 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
       tt_tdesc d;
       d.src = md->lowp ? md->lowp + md->off[idx] : nullptr;
       d.dst = md->lowp_t ? md->lowp_t + md->off[idx] : nullptr;
-      d.rows = rows; d.cols = cols; d.tiles_c = (cols + 63) / 64; d.tile0 = md->t_tiles;
+      d.rows = rows; d.cols = cols; d.pad_rows = rows;
+      d.tiles_c = (cols + 63) / 64; d.tile0 = md->t_tiles;
       md->tdesc.push_back(d);
       md->t_tiles += ((rows + 63) / 64) * d.tiles_c;
       md->t_elems += (double)rows * cols;
@@ -708,7 +828,10 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
     }
     // LayerNorm partials: LN_f, then each layer's LN2 and LN1 from the top
     // (the order the backward runs them; the table's order does not matter).
-    const size_t part_floats = (size_t)tt_layernorm_bwd_groups(N, c.C) * 3 * c.C;
+    // sized for every step shape up to the capacity: the group count is not
+    // monotone in the number of rows
+    md->ln_part_groups = tt_layernorm_bwd_groups_max(N, c.C);
+    const size_t part_floats = (size_t)md->ln_part_groups * 3 * c.C;
     std::vector<LnReduceEntry> lt;
     const int lf = p_lnf_g(md);
     md->lnf_part = (float *)alloc(part_floats * 4);
@@ -719,6 +842,7 @@ extern "C" int tt_model_create(tt_ctx *ctx, const tt_model_cfg *cfg, tt_model **
       BwdIO &io = md->lio[l];
       io.ln2_part = (float *)alloc(part_floats * 4);
       io.ln1_part = (float *)alloc(part_floats * 4);
+      io.part_groups = md->ln_part_groups;
       // LN2: gamma, beta, and the projection bias (column sums of its output)
       lt.push_back({io.ln2_part, md->g + md->off[b + 6], md->g + md->off[b + 7],
                     md->g + md->off[b + 5]});
@@ -837,7 +961,7 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   if (grouped)
     TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
                                  md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
-                                 lp ? (bf16_t *)rl_top : nullptr, md->lnf_part));
+                                 lp ? (bf16_t *)rl_top : nullptr, md->lnf_part, md->ln_part_groups));
   else
     TT_TRY(tt_layernorm_bwd_impl(ctx, mode, N, C, md->xs[c.L], md->meanf, md->rstdf,
                                  md->w + md->off[lf], md->sc.dtmp, nullptr, md->R,
@@ -865,15 +989,20 @@ extern "C" int tt_model_fwd_bwd(tt_ctx *ctx, tt_model *md, int B, int T, const i
   return TT_OK;
 }
 
+// skip (nullable, device): a nonzero flag drops the update (weights,
+// moments and both shadows stay as they are).
 static int model_adamw(tt_ctx *ctx, tt_model *md, float lr, float beta1, float beta2, float eps,
-                       float wd, int t, int32_t *overflow_out) {
+                       float wd, int t, int32_t *overflow_out, const int32_t *skip = nullptr) {
   TT_TRY(tt_check_ctx(ctx));
   int rc = check_model(md);
   if (rc != TT_OK) return tt_set_error(ctx, rc, "adamw: bad model handle");
   TT_REQUIRE(ctx, t >= 1, "adamw: t is 1-based");
   const bool f16 = md->cfg.mode == TT_FP16;
+  if (md->ls) skip = &md->ls->overflow;
   TT_TRY(tt_adamw_flat(ctx, md->w, md->g, md->m, md->v, md->lowp, md->n_slots, lr, beta1, beta2,
-                       eps, wd, t, f16, md->ls ? &md->ls->overflow : nullptr));
+                       eps, wd, t, f16, skip));
+  // (a dropped update leaves lowp unchanged, so the rebuilt transposed
+  // shadow is unchanged too)
   TT_TRY(refresh_transposed(md));
   if (md->ls)
     TT_TRY(tt_loss_scale_update(ctx, md->ls, md->ls_interval, md->ls_growth, md->ls_backoff,
@@ -894,11 +1023,14 @@ extern "C" int tt_train_step(tt_ctx *ctx, tt_model *md, int B, int T, const int3
   TT_TRY(tt_model_fwd_bwd(ctx, md, B, T, tok, targets, loss));
   if (md->ls)   // TT_FP16: the flag is the step's gradient overflow (update dropped)
     return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nonfinite);
-  if (nonfinite) {
-    TT_TRY(tt_fill_f32(ctx, (float *)nonfinite, 1, 0.f));
-    TT_TRY(tt_check_finite(ctx, loss, 1, nonfinite));
-  }
-  return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nullptr);
+  if (!nonfinite) return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nullptr);
+  // The C++/CUDA page (section 5.2) checks for NaN before the optimizer step:
+  // the flag is raised by an inf / NaN in the loss or in any gradient, and
+  // AdamW then leaves weights, moments and shadows as they were.
+  TT_TRY(tt_fill_f32(ctx, (float *)nonfinite, 1, 0.f));
+  TT_TRY(tt_check_finite(ctx, loss, 1, nonfinite));
+  TT_TRY(tt_check_finite(ctx, md->g, md->n_slots, nonfinite));
+  return model_adamw(ctx, md, lr, beta1, beta2, eps, wd, t, nullptr, nonfinite);
 }
 
 extern "C" int tt_model_loss_scale_set(tt_ctx *ctx, tt_model *md, float scale, int interval,

@@ -186,28 +186,27 @@ __global__ void ls_set_kernel(tt_loss_scale *st, float scale) {
 }
 
 // Batched bf16 transpose: descriptor i maps src [rows, cols] (row pitch cols)
-// to dst [cols, rows] (row pitch rows).  One workgroup per 64 x 64 tile,
+// to dst [cols, pad_rows] (row pitch pad_rows >= rows; the columns rows ..
+// pad_rows-1 of dst are written as zeros).  One workgroup per 64 x 64 tile,
 // staged through LDS so that both the reads and the writes are 16-byte
 // coalesced; ragged edges fall back to element accesses.
-__global__ void __launch_bounds__(256) transpose_bf16_kernel(const tt_tdesc *__restrict__ d,
-                                                             int nd) {
+__device__ __forceinline__ void transpose_tile(const tt_tdesc &d, int local) {
   __shared__ bf16_t t[64][66];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int i = 0;
-  while (i + 1 < nd && d[i + 1].tile0 <= b) ++i;
-  const bf16_t *src = d[i].src;
-  bf16_t *dst = d[i].dst;
-  const int rows = d[i].rows, cols = d[i].cols;
-  const int local = b - d[i].tile0;
-  const int r0 = (local / d[i].tiles_c) * 64, c0 = (local % d[i].tiles_c) * 64;
-  const bool vec_in = (cols & 7) == 0, vec_out = (rows & 7) == 0;
+  const int tid = threadIdx.x;
+  const bf16_t *src = d.src;
+  bf16_t *dst = d.dst;
+  const int rows = d.rows, cols = d.cols, prow = d.pad_rows;
+  const int r0 = (local / d.tiles_c) * 64, c0 = (local % d.tiles_c) * 64;
+  const bool vec_in = (cols & 7) == 0, vec_out = (prow & 7) == 0;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int q = tid + k * 256;
     const int r = q >> 3, c = (q & 7) * 8;
     const int gr = r0 + r, gc = c0 + c;
-    if (gr >= rows) continue;
-    if (vec_in && gc + 7 < cols) {
+    if (gr >= prow) continue;
+    if (gr >= rows) {   // padding rows of the source read as zero
+      for (int j = 0; j < 8; ++j) t[r][c + j] = 0;
+    } else if (vec_in && gc + 7 < cols) {
       const uint4 u = *(const uint4 *)(src + (size_t)gr * cols + gc);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -224,17 +223,40 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const tt_tdesc *__r
     const int c = q >> 3, r = (q & 7) * 8;
     const int gc = c0 + c, gr = r0 + r;
     if (gc >= cols) continue;
-    if (vec_out && gr + 7 < rows) {
+    if (vec_out && gr + 7 < prow) {
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         w[j] = (uint32_t)t[r + 2 * j][c] | ((uint32_t)t[r + 2 * j + 1][c] << 16);
-      *(uint4 *)(dst + (size_t)gc * rows + gr) = make_uint4(w[0], w[1], w[2], w[3]);
+      *(uint4 *)(dst + (size_t)gc * prow + gr) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       for (int j = 0; j < 8; ++j)
-        if (gr + j < rows) dst[(size_t)gc * rows + gr + j] = t[r + j][c];
+        if (gr + j < prow) dst[(size_t)gc * prow + gr + j] = t[r + j][c];
     }
   }
+}
+
+// Descriptors in device memory, ordered by tile0 (the model's shadows).
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const tt_tdesc *__restrict__ d,
+                                                             int nd) {
+  const int b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < nd && d[i + 1].tile0 <= b) ++i;
+  transpose_tile(d[i], b - d[i].tile0);
+}
+
+// Up to TT_TSET descriptors passed by value (no device table to upload).
+__global__ void __launch_bounds__(256) transpose_bf16_set_kernel(tt_tdesc_set s) {
+  const int b = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < TT_TSET; ++j)
+    if (j < s.n && s.d[j].tile0 <= b) i = j;
+  tt_tdesc d = s.d[0];
+#pragma unroll
+  for (int j = 1; j < TT_TSET; ++j)
+    if (i == j) d = s.d[j];
+  transpose_tile(d, b - d.tile0);
 }
 
 template <typename T>
@@ -254,11 +276,19 @@ __global__ void __launch_bounds__(256) gelu_bwd_kernel(size_t n, const T *__rest
     Elem<T>::store(dx, i, Elem<T>::load(dy, i) * gelu_grad_f(Elem<T>::load(x, i)));
 }
 
+// flag |= 1 when any of x[0..n) is inf or NaN (x 16-byte aligned: four per
+// load; every byte is read once, so the loads are non-temporal).
 __global__ void __launch_bounds__(256) finite_kernel(size_t n, const float *__restrict__ x,
                                                      int32_t *__restrict__ flag) {
   const size_t stride = (size_t)gridDim.x * 256;
+  const size_t n4 = n / 4;
   bool bad = false;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const v4f v = __builtin_nontemporal_load((const v4f *)x + i);
+    bad |= !(isfinite(v[0]) && isfinite(v[1]) && isfinite(v[2]) && isfinite(v[3]));
+  }
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
     bad |= !isfinite(x[i]);
   if (bad) atomicOr(flag, 1);
 }
@@ -370,6 +400,26 @@ int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tile
   return tt_check_launch(ctx, "transpose_bf16");
 }
 
+int tt_tdesc_set_add(tt_tdesc_set &s, const bf16_t *src, bf16_t *dst, int rows, int cols,
+                     int pad_rows) {
+  if (s.n >= TT_TSET || rows <= 0 || cols <= 0 || pad_rows < rows) return TT_EINVAL;
+  tt_tdesc &d = s.d[s.n++];
+  d.src = src; d.dst = dst;
+  d.rows = rows; d.cols = cols; d.pad_rows = pad_rows;
+  d.tiles_c = (cols + 63) / 64;
+  d.tile0 = s.tiles;
+  s.tiles += ((pad_rows + 63) / 64) * d.tiles_c;
+  s.elems += (double)pad_rows * cols;
+  return TT_OK;
+}
+
+int tt_transpose_bf16_set(tt_ctx *ctx, const tt_tdesc_set &s) {
+  if (s.n == 0 || s.tiles == 0) return TT_OK;
+  tt_prof_scope prof(ctx, "transpose_bf16_set_kernel", 0.0, 4.0 * s.elems);
+  hipLaunchKernelGGL(transpose_bf16_set_kernel, dim3(s.tiles), dim3(256), 0, ctx->stream, s);
+  return tt_check_launch(ctx, "transpose_bf16_set");
+}
+
 int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf16_t *w_lowp,
                   size_t n, float lr, float beta1, float beta2, float eps, float wd, int t,
                   bool f16, const int32_t *skip) {
@@ -388,7 +438,10 @@ int tt_adamw_flat(tt_ctx *ctx, float *w, const float *g, float *m, float *v, bf1
 }
 
 int tt_check_finite(tt_ctx *ctx, const float *x, size_t n, int32_t *flag) {
-  hipLaunchKernelGGL(finite_kernel, dim3(grid_for(n, 8)), dim3(256), 0, ctx->stream, n, x, flag);
+  if (n == 0) return TT_OK;
+  TT_REQUIRE(ctx, tt_aligned16(x), "check_finite: x must be 16-byte aligned");
+  tt_prof_scope prof(ctx, "finite_kernel", 0.0, 4.0 * n);
+  hipLaunchKernelGGL(finite_kernel, dim3(grid_for(n, 16)), dim3(256), 0, ctx->stream, n, x, flag);
   return tt_check_launch(ctx, "finite");
 }
 

@@ -43,8 +43,9 @@ struct Operand {
   // offset OOB and no branch is needed.  Unit u covers 8 consecutive elements
   // along the contiguous dimension; consecutive lanes take consecutive units.
   // Rows past the matrix (m >= M, n >= N) only feed outputs that are not
-  // stored; k >= K must read zero in at least one operand, which the host
-  // guarantees (K % 8 == 0, or a row-major operand whose k rows are masked).
+  // stored; k >= K must read zero in at least one operand and never reach
+  // another row's data, which the host guarantees (K % 8 == 0 whenever an
+  // operand is k-major; row-major operands mask their k rows).
   template <int NT>
   __device__ __forceinline__ static void load(uint4 *reg, __amdgpu_buffer_rsrc_t rs, int ld, int r0,
                                               int k0, int R, int K, int tid) {
@@ -881,11 +882,15 @@ int launch_skinny(tt_ctx *ctx, const GemmArgs &g) {
 }  // namespace
 
 // Host guard: the buffer-load path needs every operand extent below the OOB
-// offset, and a zero in one operand for k >= K (see Operand::load).
+// offset, and K % 8 == 0 whenever an operand is k-major.  A k-major row is
+// read in 8-element chunks; with K % 8 != 0 the last chunk of a row would
+// reach k >= K, i.e. the next row or bytes past the tensor, and a zero in
+// the partner operand does not cancel an inf / NaN there (0 * inf = NaN).
+// Such products take the generic kernels.
 bool tt_gemm_bf16_ok(const GemmArgs &g) {
   if (gemm_extent_bytes(g.a_kmajor, g.M, g.K, g.lda) >= OOB) return false;
   if (gemm_extent_bytes(g.b_kmajor, g.N, g.K, g.ldb) >= OOB) return false;
-  return g.K % 8 == 0 || !g.a_kmajor || !g.b_kmajor;
+  return g.K % 8 == 0 || (!g.a_kmajor && !g.b_kmajor);
 }
 
 // Tiles (8 waves, direct-to-LDS v3 kernel unless noted), chosen from sweeps
@@ -989,12 +994,13 @@ using GT = GroupTile<TT_GROUP_TILE>;
 constexpr int GBM = GT::bm, GBN = GT::bn, GBK = GT::bk;
 }
 
-int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max,
-                       GemmGroup *out, bool f16) {
-  TT_REQUIRE(ctx, entries && out && n > 0 && k_max > 0, "gemm_group: bad arguments");
-  std::vector<GemmGroupEntry> t(entries, entries + n);
-  int tiles = 0;
-  double mn2 = 0, bytes_k = 0, bytes_out = 0;
+namespace {
+// Validate the entries for reduction lengths up to k_max and fill in their
+// tile fields; tiles, mn2, bytes_k, bytes_out receive the totals.
+int group_fill(tt_ctx *ctx, std::vector<GemmGroupEntry> &t, int k_max, int &tiles, double &mn2,
+               double &bytes_k, double &bytes_out) {
+  tiles = 0;
+  mn2 = bytes_k = bytes_out = 0;
   for (auto &e : t) {
     TT_REQUIRE(ctx, e.A && e.B && e.out && e.M > 0 && e.N > 0, "gemm_group: bad entry");
     TT_REQUIRE(ctx, e.lda >= e.M && e.ldb >= e.N && e.ldo >= e.N, "gemm_group: bad leading dims");
@@ -1016,6 +1022,17 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
     bytes_k += 2.0 * (e.M + e.N);
     bytes_out += 4.0 * e.M * e.N;
   }
+  return TT_OK;
+}
+}  // namespace
+
+int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max,
+                       GemmGroup *out, bool f16) {
+  TT_REQUIRE(ctx, entries && out && n > 0 && k_max > 0, "gemm_group: bad arguments");
+  std::vector<GemmGroupEntry> t(entries, entries + n);
+  int tiles = 0;
+  double mn2 = 0, bytes_k = 0, bytes_out = 0;
+  TT_TRY(group_fill(ctx, t, k_max, tiles, mn2, bytes_k, bytes_out));
   const int grid = (tiles + 7) / 8 * 8;
   TT_REQUIRE(ctx, grid < 0xffff && n < 0xffff, "gemm_group: too many tiles");
   std::vector<uint16_t> map(grid, 0xffff);
@@ -1045,12 +1062,31 @@ int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_
   return TT_OK;
 }
 
-int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K) {
+int tt_gemm_group_update(tt_ctx *ctx, GemmGroup &g, const GemmGroupEntry *entries, int n,
+                         int k_max) {
+  TT_REQUIRE(ctx, g.table && g.map && entries && n == g.n && k_max > 0,
+             "gemm_group_update: not planned for %d products", n);
+  std::vector<GemmGroupEntry> t(entries, entries + n);
+  int tiles = 0;
+  double mn2 = 0, bytes_k = 0, bytes_out = 0;
+  TT_TRY(group_fill(ctx, t, k_max, tiles, mn2, bytes_k, bytes_out));
+  TT_REQUIRE(ctx, tiles == g.tiles && mn2 == g.mn2, "gemm_group_update: product shapes changed");
+  hipError_t e = hipMemcpyAsync(g.table, t.data(), t.size() * sizeof(GemmGroupEntry),
+                                hipMemcpyHostToDevice, ctx->stream);
+  // the host vector dies here: make sure the copy has read it
+  if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return tt_set_error(ctx, TT_EHIP, "gemm_group_update: %s", hipGetErrorString(e));
+  g.bytes_k = bytes_k;
+  g.bytes_out = bytes_out;
+  return TT_OK;
+}
+
+int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K, bool accumulate) {
   TT_REQUIRE(ctx, g.table && g.map && g.grid > 0 && K > 0, "gemm_group: not planned");
   GemmParams p{};
   p.K = K;
   p.k_chunk = (K + GBK - 1) / GBK * GBK;
-  p.epi = EPI_STORE;
+  p.epi = accumulate ? EPI_STORE_ACC : EPI_STORE;
   p.out_bf16 = 0;
   p.raster_n = 0;
   p.group = g.table;

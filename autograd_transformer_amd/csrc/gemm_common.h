@@ -177,10 +177,10 @@ inline double gemm_bytes(const GemmArgs &g) {
 // Bytes spanned by an operand: rows x reduction, k-major or row-major,
 // rounded up to whole dwords.  The buffer range check works per dword: an
 // extent ending inside a dword would read that dword -- and so the operand's
-// last element -- as 0.  The element the rounding adds is, for a row-major
-// operand, column `rows` of its last k row (it reaches only an output that is
-// not stored); for a k-major one, k = K of its last row (it meets the other
-// operand's rows past K, which read 0 through that operand's own check).
+// last element -- as 0.  The rounding can add an element only to a row-major
+// operand (k-major operands of the fast kernels have K and ld multiples of
+// 8): column `rows` of its last k row, which reaches only an output that is
+// not stored.
 __host__ __device__ inline size_t gemm_extent_bytes(bool kmajor, int rows, int K, int ld) {
   const size_t elems = kmajor ? (size_t)(rows - 1) * ld + K : (size_t)(K - 1) * ld + rows;
   return ((elems + 1) & ~(size_t)1) * 2;

@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels: LayerNorm forward/backward, fused softmax +
 // cross-entropy, column sums (bias gradients).  One wave (64 lanes) owns a
 // row; row statistics are wave-shuffle reductions; loads are 16-byte vectors.
+#include <algorithm>
+
 #include "tt_internal.h"
 
 namespace {
@@ -736,14 +738,39 @@ int tt_layernorm_bwd_groups(int N, int C) {
   return (N + rows_per_wg - 1) / rows_per_wg;
 }
 
+// The group count is not monotone in N (the rows per wave of the row-walking
+// kernel step from 2 to 4 to 8, which halves the count at each step), so a
+// buffer for every N up to N_max takes the largest count over the regimes:
+// within one regime the count grows with N, so the candidates are N_max and
+// the regime ends below it.
+int tt_layernorm_bwd_groups_max(int N_max, int C) {
+  if (N_max <= 0) return 0;
+  int G = tt_layernorm_bwd_groups(N_max, C);
+  for (int r : {2, 4}) {
+    const int end = LNP_MAX_WG * LNP_WAVES * r;   // last N with lnp_rpw(N) == r
+    if (end < N_max) G = std::max(G, tt_layernorm_bwd_groups(end, C));
+  }
+  return G;
+}
+
+extern "C" int tt_layernorm_bwd_workspace(int n_rows, int C, size_t *bytes) {
+  if (!bytes || n_rows < 0 || C <= 0 || C % 4 != 0 || C > 4096) return TT_EINVAL;
+  *bytes = (size_t)tt_layernorm_bwd_groups_max(n_rows, C) * 3 * C * sizeof(float);
+  return TT_OK;
+}
+
 int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
                           const float *mean, const float *rstd, const float *g, const float *dy,
-                          const float *dres, float *dx, bf16_t *dx_bf16, float *part) {
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *part,
+                          int part_groups) {
   TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
   TT_REQUIRE(ctx, x && mean && rstd && g && dy && dx && part, "layernorm_bwd: NULL pointer");
   if (N == 0) return TT_OK;
   const int nv = (C / 4 + 63) / 64;
   const int G = tt_layernorm_bwd_groups(N, C);
+  TT_REQUIRE(ctx, G <= part_groups,
+             "layernorm_bwd: %d rows need %d workgroup partials, the buffer holds %d", N, G,
+             part_groups);
   const int rpw = lnp_rpw(N);   // rows per wave of the row-walking kernel (nv <= 4)
   {
     tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
@@ -793,8 +820,19 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
   tt_scratch_scope scope(ctx);
   void *part;
   TT_TRY(tt_arena_alloc(ctx, (size_t)G * 3 * C * 4, &part));
-  TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16,
-                               (float *)part));
+  return tt_layernorm_bwd_ws(ctx, mode, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16, dg, db,
+                             dsum, (float *)part, G);
+}
+
+int tt_layernorm_bwd_ws(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                        const float *mean, const float *rstd, const float *g, const float *dy,
+                        const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
+                        float *dsum, float *part, int part_groups) {
+  TT_REQUIRE(ctx, N >= 0 && C > 0 && C % 4 == 0 && C <= 4096, "layernorm: need C %% 4 == 0, C <= 4096");
+  if (N == 0) return TT_OK;
+  const int G = tt_layernorm_bwd_groups(N, C);
+  TT_TRY(tt_layernorm_bwd_rows(ctx, mode, N, C, x, mean, rstd, g, dy, dres, dx, dx_bf16, part,
+                               part_groups));
   if (!dg && !db && !dsum) return TT_OK;
   tt_prof_scope prof(ctx, "layernorm_bwd_reduce_kernel", 0.0, 12.0 * G * C + 24.0 * C);
   hipLaunchKernelGGL(layernorm_bwd_reduce_kernel,

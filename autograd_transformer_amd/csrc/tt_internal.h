@@ -256,8 +256,13 @@ struct GemmGroup {
 // kernel's layout rules for K up to k_max.
 int tt_gemm_group_plan(tt_ctx *ctx, const GemmGroupEntry *entries, int n, int k_max, GemmGroup *out,
                        bool f16 = false);
-// Run every product of the group in one launch with reduction length K.
-int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K);
+// Point a planned group at other operands and outputs (same product shapes);
+// uploads the table and waits for the stream.
+int tt_gemm_group_update(tt_ctx *ctx, GemmGroup &g, const GemmGroupEntry *entries, int n,
+                         int k_max);
+// Run every product of the group in one launch with reduction length K;
+// accumulate: out += product (else out = product).
+int tt_gemm_group_run(tt_ctx *ctx, const GemmGroup &g, int K, bool accumulate = false);
 // bf16 operands with 16-byte aligned rows (the fast path; called by tt_gemm).
 int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g);
 bool tt_gemm_bf16_ok(const GemmArgs &g);
@@ -271,6 +276,13 @@ int tt_layernorm_bwd_impl(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
                           const float *mean, const float *rstd, const float *g, const float *dy,
                           const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
                           float *dsum = nullptr);
+// The same with the column-partial workspace given: part holds part_groups
+// groups of 3 C floats (tt_layernorm_bwd_groups(N, C) are used; every one of
+// them is written before it is read, so the workspace needs no clearing).
+int tt_layernorm_bwd_ws(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                        const float *mean, const float *rstd, const float *g, const float *dy,
+                        const float *dres, float *dx, bf16_t *dx_bf16, float *dg, float *db,
+                        float *dsum, float *part, int part_groups);
 // The same in two parts: tt_layernorm_bwd_rows writes dx (and its copy) and
 // the per-workgroup column partials of dg, db and dsum into part
 // ([tt_layernorm_bwd_groups(N, C)][3][C] floats); the partials are added into
@@ -282,9 +294,14 @@ struct LnReduceEntry {
   float *dg, *db, *dsum;   // nullable each
 };
 int tt_layernorm_bwd_groups(int N, int C);
+// Largest tt_layernorm_bwd_groups(n, C) over 1 <= n <= N_max: the size (in
+// groups of 3 C floats) of a partial buffer that serves every N up to N_max.
+int tt_layernorm_bwd_groups_max(int N_max, int C);
+// part holds part_groups groups; more needed is TT_EINVAL, nothing enqueued.
 int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
                           const float *mean, const float *rstd, const float *g, const float *dy,
-                          const float *dres, float *dx, bf16_t *dx_bf16, float *part);
+                          const float *dres, float *dx, bf16_t *dx_bf16, float *part,
+                          int part_groups);
 int tt_layernorm_bwd_reduce_batch(tt_ctx *ctx, int N, int C, const LnReduceEntry *table, int n);
 // Column sums out[n] += sum_m src[m, n]; fmt: the source's tt_mode (float32,
 // bf16 or binary16).
@@ -308,13 +325,25 @@ int tt_loss_scale_set(tt_ctx *ctx, tt_loss_scale *st, float scale);
 // One 64 x 64 tile range of a batched bf16 transpose (src [rows, cols] ->
 // dst [cols, rows]); tile0 is the first workgroup of this matrix, tiles are
 // numbered row-major with tiles_c = ceil(cols / 64) per tile row.
+// src [rows, cols] -> dst [cols, pad_rows] (dst columns rows .. pad_rows-1
+// zero); tiles_c = ceil(cols / 64); tile0 = first workgroup of this entry.
 struct tt_tdesc {
   const bf16_t *src;
   bf16_t *dst;
-  int rows, cols, tiles_c, tile0;
+  int rows, cols, pad_rows, tiles_c, tile0;
 };
 // d_dev: device copy of the descriptor table, ordered by tile0.
 int tt_transpose_bf16(tt_ctx *ctx, const tt_tdesc *d_dev, int nd, int total_tiles, double elems);
+// A few descriptors passed to the kernel by value.
+constexpr int TT_TSET = 4;
+struct tt_tdesc_set {
+  tt_tdesc d[TT_TSET];
+  int n = 0, tiles = 0;
+  double elems = 0;
+};
+int tt_tdesc_set_add(tt_tdesc_set &s, const bf16_t *src, bf16_t *dst, int rows, int cols,
+                     int pad_rows);
+int tt_transpose_bf16_set(tt_ctx *ctx, const tt_tdesc_set &s);
 // Inference (decode.hip): copy a prefill's keys and values (qkv columns
 // C..3C of rows b*T + t) into the cache [B_max, T_max, 2C]; attention of one
 // new position pos over the cache, appending its key and value first, with

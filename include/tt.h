@@ -161,10 +161,17 @@ int tt_layernorm_fwd(tt_ctx *ctx, tt_mode mode, int N, int C, float eps, const f
                      const float *g, const float *b, void *y, float *mean, float *rstd);
 
 /* LayerNorm backward (chain rule of the above).  dy [N,C] float32.
- * dx [N,C] float32 +=.  dg, db [C] float32 +=.  Same C limits. */
+ * dx [N,C] float32 +=.  dg, db [C] float32 +=.  Same C limits.  The column
+ * sums behind dg and db are formed per workgroup into a partial-sum
+ * workspace (arena scratch) and then added up by a second launch. */
 int tt_layernorm_bwd(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
                      const float *mean, const float *rstd, const float *g, const float *dy,
                      float *dx, float *dg, float *db);
+/* Size in bytes of that workspace for every N <= n_rows rows of width C
+ * (host only, no GPU needed): the number of workgroups does not grow
+ * monotonically with N (each wave takes 2, 4 or 8 rows depending on N), so
+ * this is the maximum over N.  TT_EINVAL for a C the kernels do not take. */
+int tt_layernorm_bwd_workspace(int n_rows, int C, size_t *bytes);
 
 /* GELU, tanh form (tinytorch page §3 item 4), elementwise on n values of a
  * mode tensor.  Backward uses the analytic derivative of the tanh form
@@ -267,16 +274,24 @@ typedef struct {
   float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_proj, *b_proj;
   float *ln2_g, *ln2_b, *w_fc, *b_fc, *w_fcp, *b_fcp;
 } tt_block_g;
-/* Activations the backward needs, carved from the arena (opaque). */
+/* Activations the backward needs, carved from the arena (opaque).  In the
+ * 16-bit modes it also holds transposed copies of the four weight matrices
+ * (2 (4C^2 + 2CF) bytes) and the plan of the grouped weight-gradient launch;
+ * creation then waits for the stream once. */
 typedef struct tt_block_saved tt_block_saved;
 int tt_block_saved_create(tt_ctx *ctx, const tt_block_cfg *cfg, tt_block_saved **out);
 /* NULL-safe; the device memory returns with the arena. */
 void tt_block_saved_destroy(tt_block_saved *saved);
-/* x, y [B,T,C] float32. */
+/* x, y [B,T,C] float32.  16-bit modes: the weight matrices are transposed
+ * into the saved buffers first (one launch), so the forward products run the
+ * same k-major kernels as the whole-model step. */
 int tt_block_fwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w, const float *x,
                  float *y, tt_block_saved *saved);
 /* dy [B,T,C] float32 -> dx [B,T,C] float32 (written); grads +=.  Scratch
- * from the arena. */
+ * from the arena.  16-bit modes: the four weight gradients run as one
+ * grouped launch after the activation gradients (as in the whole-model
+ * step); when the scratch or gradient addresses differ from the previous
+ * call's, the launch table is re-uploaded and the call waits for the stream. */
 int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
                  const tt_block_saved *saved, const float *dy, float *dx, tt_block_g *g);
 
@@ -284,7 +299,9 @@ int tt_block_bwd(tt_ctx *ctx, const tt_block_cfg *cfg, const tt_block_w *w,
  * items 5-6; Forge page "瓶颈分析是否合理").  h [N,C] mode tensor, wte [V,C]
  * mode tensor, targets [N] int32.  loss: one float32 (written, the mean).
  * dh [N,C] float32 (written).  dwte [V,C] float32 (+=).  The [N,V] logits
- * live in arena scratch (mode dtype) and are overwritten by their gradient. */
+ * live in arena scratch (mode dtype) and are overwritten by their gradient;
+ * in the 16-bit modes the arena also holds wte transposed ([C, V rounded up
+ * to 64], one launch) so that dh reads both operands k-major. */
 int tt_lmhead_ce_fwdbwd(tt_ctx *ctx, tt_mode mode, int N, int C, int V, const void *h,
                         const void *wte, const int32_t *targets, float *loss, float *dh,
                         float *dwte);
@@ -315,9 +332,14 @@ int tt_model_refresh_shadow(tt_model *model);
 /* One training step (tinytorch page §3 item 7: forward, zero grads, backward,
  * Adam update), loss on every position with next-token targets, mean over the
  * B*T positions.  tok, targets [B,T] int32.  loss: one float32 (written).
- * nonfinite: nullable int32 flag set to 1 if the loss is not finite (AdamW
- * still runs; callers that want to skip it use tt_model_fwd_bwd + their own
- * check).  t: 1-based AdamW step.  B <= B_max, T <= T_max. */
+ * nonfinite: nullable int32 device flag.  When given, it is cleared and then
+ * set to 1 if the loss or any gradient entry is inf or NaN, and the AdamW
+ * update is then dropped: weights, moments and shadows stay bit for bit as
+ * they were (the C++/CUDA page, section 5.2, checks for NaN before the
+ * optimizer step).  The check reads the whole gradient buffer once (4 bytes
+ * per parameter); with NULL there is no check and AdamW always runs.  In
+ * TT_FP16 the flag is the loss-scaled step's overflow (tt_model_loss_scale_*).
+ * t: 1-based AdamW step.  B <= B_max, T <= T_max. */
 int tt_train_step(tt_ctx *ctx, tt_model *model, int B, int T, const int32_t *tok,
                   const int32_t *targets, float lr, float beta1, float beta2, float eps,
                   float wd, int t, float *loss, int32_t *nonfinite);

@@ -70,3 +70,38 @@ def test_null_and_stale_handles_without_gpu(lib):
     assert lib.tt_model_decode(fp, fp, fp, 1, 0, fp, None, fp) == -4
     assert lib.tt_argmax(fp, 0, 1, 1, 1, fp, fp) == -4
     assert lib.tt_ctx_create(0, None, 1 << 20, None, None) == -1
+
+
+def _ln_workspace(lib, n, C):
+    out = ctypes.c_size_t(0)
+    assert lib.tt_layernorm_bwd_workspace(n, C, ctypes.byref(out)) == 0
+    return out.value
+
+
+def test_layernorm_workspace_covers_every_smaller_step(lib):
+    """The LayerNorm backward's partial-sum workspace, sized once for up to
+    n_rows rows, must hold what any N <= n_rows needs.  Its workgroup count
+    drops where a wave's rows step from 2 to 4 (N = 4096) and from 4 to 8
+    (N = 8192), so the size for n_rows is the maximum over N <= n_rows and
+    never shrinks as n_rows grows."""
+    C = 768
+    per_group = 3 * C * 4
+    # row-walking kernel: 4 waves x 2 rows per workgroup up to N = 4096,
+    # 4 x 4 up to 8192, 4 x 8 beyond
+    def groups(n):
+        r = 2 if n <= 4096 else (4 if n <= 8192 else 8)
+        return -(-n // (4 * r))
+    prev = 0
+    for n in sorted(set(range(1, 20000, 97)) | {4095, 4096, 4097, 6144, 8192, 8193, 16384, 16385}):
+        ws = _ln_workspace(lib, n, C)
+        assert ws >= prev, (n, ws, prev)
+        prev = ws
+        assert ws == per_group * max(groups(m) for m in {n, min(n, 4096), min(n, 8192)}), n
+    # the case that overran: a capacity of 6 x 1024 rows run at 4 x 1024
+    assert _ln_workspace(lib, 6144, C) >= per_group * groups(4096) == per_group * 512
+    assert _ln_workspace(lib, 6144, C) > per_group * groups(6144)
+    # wide rows take the other kernel, whose count is monotone
+    assert _ln_workspace(lib, 5000, 2048) >= _ln_workspace(lib, 4999, 2048)
+    bad = ctypes.c_size_t(0)
+    assert lib.tt_layernorm_bwd_workspace(10, 766, ctypes.byref(bad)) == -1
+    assert lib.tt_layernorm_bwd_workspace(10, 768, None) == -1

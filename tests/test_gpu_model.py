@@ -125,18 +125,40 @@ def test_train_step_matches_fwd_bwd_then_adamw():
     m1.close(); m2.close(); ctx.close()
 
 
-def test_nonfinite_flag_and_target_range():
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_nonfinite_flag_and_target_range(mode):
+    """A NaN in the MLP bias makes the loss and the gradients NaN: the step's
+    flag is raised and AdamW is dropped -- weights, moments and the 16-bit
+    shadow stay bit for bit as they were (the C++/CUDA page, section 5.2,
+    checks for NaN before the optimizer step).  A clean step afterwards
+    clears the flag and updates."""
     shape = syn.ModelShape(n_layer=1, n_embd=64, n_head=1, vocab=50, block_size=16)
     params = syn.gpt2_params(shape, seed=33)
     params["h0.b_fc"][3] = np.nan
     ctx = tt.Context(arena_bytes=1 << 29)
-    m = make_model(ctx, shape, 1, 16, "f32", params)
+    m = make_model(ctx, shape, 1, 16, mode, params, V_pad=64)
     tok, tgt = syn.gpt2_tokens(1, 16, 50, seed=33)
     loss, flag = empty((1,)), zeros((1,), "i32")
+    # moments from one clean step first, so that "unchanged" is not "zero"
+    clean = dict(params)
+    clean["h0.b_fc"] = np.zeros_like(params["h0.b_fc"])
+    m.load(clean)
     tt.tt_train_step(ctx, m, 1, 16, dev(tok, "i32"), dev(tgt, "i32"), 3e-4, 0.9, 0.95, 1e-8,
                      0.1, 1, loss, flag)
     ctx.sync()
+    assert host(flag)[0] == 0 and np.isfinite(host(loss)[0])
+    b = host(m.tensor("h0.b_fc", "w")).astype(np.float32)
+    b[3] = np.nan
+    m.tensor("h0.b_fc", "w").copy_(dev(b))
+    kinds = ("w", "m", "v") + (("w_lowp",) if mode != "f32" else ())
+    before = {(k, w): host(m.tensor(k, w)).copy() for k in m.names for w in kinds}
+    tt.tt_train_step(ctx, m, 1, 16, dev(tok, "i32"), dev(tgt, "i32"), 3e-4, 0.9, 0.95, 1e-8,
+                     0.1, 2, loss, flag)
+    ctx.sync()
     assert host(flag)[0] == 1 and not np.isfinite(host(loss)[0])
+    assert not np.all(np.isfinite(host(m.tensor("h0.w_fc", "g"))))   # a NaN gradient
+    for key, val in before.items():
+        assert np.array_equal(host(m.tensor(*key)), val, equal_nan=True), key
     bad = tgt.copy()
     bad[0, 3] = 50
     tt.tt_model_fwd_bwd(ctx, m, 1, 16, dev(tok, "i32"), dev(bad, "i32"), loss)
@@ -157,7 +179,107 @@ def test_model_rejects_bad_configs():
     ctx.close()
 
 
+def test_layernorm_partials_sized_for_smaller_steps():
+    """Capacity 6 x 1024 tokens run at 4 x 1024: the LayerNorm backward then
+    uses more workgroups (512: two rows per wave up to 4096 rows) than at the
+    capacity (384: four rows per wave), and its partial buffers are sized for
+    the larger count.  Loss and every gradient against the oracle, at both
+    batch sizes."""
+    shape = syn.ModelShape(n_layer=1, n_embd=128, n_head=2, vocab=97, block_size=1024)
+    cfg = og.GPTConfig(n_layer=1, n_embd=128, n_head=2, vocab=97, block_size=1024)
+    params = syn.gpt2_params(shape, seed=35, w_std=0.05, bias_std=0.05, ln_std=0.1)
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    ctx = tt.Context(arena_bytes=4 << 30)
+    model = make_model(ctx, shape, 6, 1024, "bf16", params, V_pad=128)
+    loss = empty((1,))
+    for B in (4, 6):
+        tok, tgt = syn.gpt2_tokens(B, 1024, 97, seed=35 + B)
+        tt.tt_model_fwd_bwd(ctx, model, B, 1024, dev(tok, "i32"), dev(tgt, "i32"), loss)
+        ctx.sync()
+        l_ref, g_ref = og.model_fwd_bwd(p64, tok, tgt, cfg, "bf16")
+        assert abs(host(loss)[0] - l_ref) / l_ref <= 2e-2
+        _check_grads(grads_of(model), g_ref, "bf16")
+    model.close()
+    ctx.close()
+
+
 # ------------------------------------------------------------ full size
+
+def test_gpt2_width_b8_t1024_two_layers_elementwise():
+    """The benchmarked launch configuration -- B=8, T=1024, C=768, 12 heads,
+    V=50257 (table padded to 50304), bf16 -- with two layers, element by
+    element against the oracle run here (define-by-run page section 4.2:
+    compare with an independent computation on fixed seeds).  Every kernel
+    path of the 124M step runs at its full-size launch shape: the 256 x 128
+    forward tile (>= 512 tiles), the GELU-backward product, the N = 768
+    products, the LM head at K = 50304 and the grouped weight gradients at
+    K = 8192.  Checked: the loss, every gradient tensor (rel-L2), the tails
+    -- the last vocabulary tile of the token-table gradient, the rows of the
+    last inputs and targets, the last position's row of the position-table
+    gradient (which sums the last token's input gradient over the batch) --
+    and the AdamW update and moments."""
+    L, B, T, C, V = 2, 8, 1024, 768, 50257
+    shape = syn.ModelShape(n_layer=L, n_embd=C, n_head=12, vocab=V, block_size=T)
+    cfg = og.GPTConfig(n_layer=L, n_embd=C, n_head=12, vocab=V, block_size=T)
+    params = syn.gpt2_params(shape, seed=51, bias_std=0.02, ln_std=0.05)
+    tok, tgt = syn.gpt2_tokens(B, T, V, seed=51)
+    ctx = tt.Context(arena_bytes=16 << 30)
+    model = make_model(ctx, shape, B, T, "bf16", params, V_pad=50304)
+    loss = empty((1,))
+    tt.tt_model_fwd_bwd(ctx, model, B, T, dev(tok, "i32"), dev(tgt, "i32"), loss)
+    sync()
+    g = grads_of(model)
+    print("[oracle] 2-layer GPT-2 width, 8 x 1024 tokens ...", flush=True)
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    l_ref, g_ref = og.model_fwd_bwd(p64, tok, tgt, cfg, "bf16")
+    l_gpu = host(loss)[0]
+    assert abs(l_gpu - l_ref) / l_ref <= 2e-2
+    errs, kb = {}, {}
+    for k in g_ref:
+        got = g[k][:V] if k == "wte" else g[k]
+        rest, rest_ref, key = split_key_bias(k, got, g_ref[k], C)
+        errs[k] = rel_l2(rest, rest_ref)
+        if key is not None:
+            kb[k] = np.linalg.norm(key) / np.linalg.norm(rest_ref)
+    assert np.all(g["wte"][V:] == 0)
+    tails = {
+        "wte last vocab tile": rel_l2(g["wte"][50176:V], g_ref["wte"][50176:V]),
+        "wte rows of the last inputs": rel_l2(g["wte"][tok[:, -1]], g_ref["wte"][tok[:, -1]]),
+        "wte rows of the last targets": rel_l2(g["wte"][tgt[:, -1]], g_ref["wte"][tgt[:, -1]]),
+        "wte row 50256": rel_l2(g["wte"][V - 1], g_ref["wte"][V - 1]),
+        "wpe last position": rel_l2(g["wpe"][T - 1], g_ref["wpe"][T - 1]),
+        "wpe first position": rel_l2(g["wpe"][0], g_ref["wpe"][0]),
+    }
+    bad = {k: e for k, e in {**errs, **tails}.items() if not e <= 2e-2}
+    print(f"loss {l_gpu:.6f} vs {l_ref:.6f}; max grad rel-L2 {max(errs.values()):.2e}; "
+          f"tails {max(tails.values()):.2e}")
+    assert not bad, bad
+    assert max(kb.values()) <= KEY_BIAS_NOISE["bf16"], kb
+    # AdamW, t = 1: the update and both moments against the oracle's
+    tt.tt_model_adamw(ctx, model, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["wd"], 1)
+    sync()
+    upd, mom = {}, {}
+    for k in g_ref:
+        w_ref, m_ref, v_ref = oracle.adamw_update(p64[k], g_ref[k], 0, 0, t=1, **{
+            "lr": HP["lr"], "beta1": HP["beta1"], "beta2": HP["beta2"], "eps": HP["eps"],
+            "wd": HP["wd"]})
+        sl = slice(0, V) if k == "wte" else slice(None)
+        gk = g_ref[k].copy()
+        if k.endswith("b_qkv"):
+            gk[C:2 * C] = 0.0      # exact value of the key-bias gradient
+        rms = np.linalg.norm(gk) / np.sqrt(gk.size)
+        upd[k] = check_post_adamw(host(model.tensor(k, "w"))[sl], p64[k], gk, w_ref,
+                                  HP["lr"], HP["wd"], 2e-2, rms)
+        m_gpu, v_gpu = host(model.tensor(k, "m"))[sl], host(model.tensor(k, "v"))[sl]
+        rest_m, rest_mr, _ = split_key_bias(k, m_gpu, m_ref, C)
+        rest_v, rest_vr, _ = split_key_bias(k, np.sqrt(v_gpu), np.sqrt(v_ref), C)
+        mom[k] = max(rel_l2(rest_m, rest_mr), rel_l2(rest_v, rest_vr))
+    print(f"AdamW update max rel-L2 {max(upd.values()):.2e}; moments {max(mom.values()):.2e}")
+    bad = {k: e for k, e in mom.items() if not e <= 2e-2}
+    assert not bad, bad
+    model.close()
+    ctx.close()
+
 
 @pytest.fixture(scope="module")
 def gpt2_124m():
