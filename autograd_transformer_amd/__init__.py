@@ -140,6 +140,12 @@ def tt_layernorm_bwd(ctx, mode, N, C, x, mean, rstd, g, dy, dx, dg=None, db=None
                                             _ptr(db)))
 
 
+def tt_layernorm_bwd_noalloc(ctx, mode, N, C, x, mean, rstd, g, dy, dx, dg=None, db=None):
+    return ctx.check(lib().tt_layernorm_bwd_noalloc(ctx.handle, _mode(mode), N, C, _ptr(x),
+                                                    _ptr(mean), _ptr(rstd), _ptr(g), _ptr(dy),
+                                                    _ptr(dx), _ptr(dg), _ptr(db)))
+
+
 def tt_gelu_fwd(ctx, mode, n, x, y):
     return ctx.check(lib().tt_gelu_fwd(ctx.handle, _mode(mode), n, _ptr(x), _ptr(y)))
 

@@ -70,6 +70,7 @@ SIGS = {
     "tt_layernorm_fwd": (i32, [vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
     "tt_layernorm_bwd": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
     "tt_layernorm_bwd_workspace": (i32, [i32, i32, P(sz)]),
+    "tt_layernorm_bwd_noalloc": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
     "tt_gelu_fwd": (i32, [vp, i32, sz, vp, vp]),
     "tt_gelu_bwd": (i32, [vp, i32, sz, vp, vp, vp]),
     "tt_attn_fwd": (i32, [vp, i32, i32, i32, i32, i32, vp, vp, vp]),

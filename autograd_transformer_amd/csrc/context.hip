@@ -97,6 +97,15 @@ extern "C" int tt_ctx_create(int device, void *hip_stream, size_t arena_bytes, v
     delete c;
     return TT_ENOMEM;
   }
+  // the fixed workspace of tt_layernorm_bwd_noalloc on this device (looked
+  // up once per device, with the device current)
+  const int rc = tt_noalloc_init(device);
+  if (rc != TT_OK) {
+    (void)hipFree(c->dev_flags);
+    if (c->owns_arena) (void)hipFree(c->arena);
+    delete c;
+    return rc;
+  }
   *out = c;
   return TT_OK;
 }

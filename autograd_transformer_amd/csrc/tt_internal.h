@@ -53,6 +53,12 @@ struct tt_prof_scope {
   ~tt_prof_scope();
 };
 
+// Workspace of tt_layernorm_bwd_noalloc: a fixed device array per GPU,
+// looked up once per device by tt_noalloc_init (called by tt_ctx_create with
+// the device current).
+constexpr size_t TT_NOALLOC_SCRATCH_BYTES = (size_t)8 << 20;
+int tt_noalloc_init(int device);
+
 // Validate a context handle (magic word catches freed or foreign pointers,
 // the debug guard idea of the microcrad page's Value.magic).
 int tt_check_ctx(const tt_ctx *ctx);

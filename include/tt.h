@@ -172,6 +172,21 @@ int tt_layernorm_bwd(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
  * monotonically with N (each wave takes 2, 4 or 8 rows depending on N), so
  * this is the maximum over N.  TT_EINVAL for a C the kernels do not take. */
 int tt_layernorm_bwd_workspace(int n_rows, int C, size_t *bytes);
+/* tt_layernorm_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, layout and results as tt_layernorm_bwd (dx, dg, db +=), but
+ * the partial-sum workspace is a fixed array of 8 MiB in the library's device
+ * memory (one per GPU, held until the process ends) instead of arena scratch:
+ * the call allocates nothing, on the device or through the arena.  A shape
+ * whose workspace (tt_layernorm_bwd_workspace) exceeds 8 MiB is TT_EINVAL with
+ * nothing enqueued — e.g. up to 16384 rows at C <= 1024 fit.  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race on it; calls ordered on one stream do not
+ * (each call writes every partial it reads, so leftover contents are never
+ * read).  Its kernels are not timed by tt_ctx_profile. */
+int tt_layernorm_bwd_noalloc(tt_ctx *ctx, tt_mode mode, int N, int C, const float *x,
+                             const float *mean, const float *rstd, const float *g,
+                             const float *dy, float *dx, float *dg, float *db);
 
 /* GELU, tanh form (tinytorch page §3 item 4), elementwise on n values of a
  * mode tensor.  Backward uses the analytic derivative of the tanh form
