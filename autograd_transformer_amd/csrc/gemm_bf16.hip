@@ -774,6 +774,258 @@ int launch3(tt_ctx *ctx, const GemmArgs &g, int split, size_t out_zstride = 0) {
   return TT_EINVAL;
 }
 
+// --------------------------------------------------------------------------
+// Ping-pong k-major GEMM (both operands k-major), used for the N = 768
+// products of the step (attention and MLP down-projections, the dX of the
+// qkv and fc layers, the LM-head dH).  One workgroup of 8 waves owns a
+// 128 x BN output tile.  The waves form two groups of four -- waves 0-3 and
+// 4-7, so every SIMD holds one wave of each -- and the groups take alternate
+// BKP-deep k-stages (group 0 the even ones, group 1 the odd ones), each group
+// with an LDS ring of its own NSG stages.  Each wave accumulates a 128 x
+// (BN/4) block of its group's partial tile (8 x BN/64 MFMA tiles of 16 x 16),
+// which keeps the LDS bytes read per MFMA low: (128 + BN/4) / (128 BN/4) per
+// output element and k, about 0.6x those of a 64 x 48 block.  128 x 192
+// tiles put exactly 256 workgroups on the N = 768 products (one per CU).
+//
+// The groups run in alternating phases, offset by one: while one group
+// issues its MFMAs for a stage, the other reads its next stage's fragments
+// from LDS and issues the global loads of a later stage into its ring.  Each
+// phase ends with one workgroup barrier, so on every SIMD the MFMA wave and
+// the memory wave of a phase run side by side, and the MFMA pipe always has
+// a wave with a stage in registers.  Loads run D = NSG - 1 of a group's
+// stages ahead; a wave waits for its own loads of the stage it reads next
+// (vmcnt) before the barrier that opens that stage, and reads complete
+// (lgkmcnt(0)) before the barrier that closes its memory phase, so a ring
+// slot is refilled only after its readers are done with it.
+//
+// At the end the two partial tiles meet in LDS (group 0 stores, group 1
+// adds: a fixed order, so the result is deterministic) and all 512 threads
+// run the usual epilogue with row-coalesced accesses.
+//
+// Measured (single products, MI355X): with the global loads removed the
+// schedule runs the LM-head dH at 1.67 PFLOP/s, so the MFMA/LDS side is not
+// the limit; with them, the operand stream bounds it (1.05 PFLOP/s).  64-deep
+// stages (whole 128-byte lines per k-major row) beat 32-deep ones by 5-25 %.
+// --------------------------------------------------------------------------
+template <int BN, int NSG, int BKP = 32>
+struct PPCfg {
+  static constexpr int BM = 128, BK = BKP, NW = 8, NT = 512, GW = 4;
+  static constexpr int KS = BK / 32;               // MFMA k-steps per stage
+  static constexpr int WTN = BN / GW;              // columns per wave
+  static constexpr int FM = BM / 16, FN = WTN / 16;
+  using OA = DOp<BM, BK, true>;
+  using OB = DOp<BN, BK, true>;
+  static constexpr int STAGE = OA::ELEMS + OB::ELEMS;   // bf16 elements
+  static constexpr int LPW = OA::CHUNKS / GW + OB::CHUNKS / GW;   // loads per wave per stage
+  static constexpr int RING = NSG * STAGE;                      // per group
+  static constexpr int OPER_BYTES = 2 * RING * 2;
+  static constexpr int LDC = BN + 4;
+  static constexpr int EPI_BYTES = BM * LDC * 4;
+  static constexpr int SMEM = OPER_BYTES > EPI_BYTES ? OPER_BYTES : EPI_BYTES;
+  static_assert(WTN % 16 == 0, "BN must be a multiple of 64");
+  static_assert(OA::CHUNKS % GW == 0 && OB::CHUNKS % GW == 0, "loads not divisible by waves");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(NSG >= 2 && (NSG - 2) * LPW < 64, "ring depth / vmcnt range");
+};
+
+// s_waitcnt lgkmcnt(0), other counters left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// A workgroup barrier that nothing crosses: the empty asm statements keep
+// memory accesses on their side at the IR level, the scheduling barriers keep
+// every instruction (the MFMAs included) on its side in the machine
+// scheduler.
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// vmcnt(r * LPW) for r in [0, 3]: loads of the last r stages may still fly.
+template <int LPW>
+__device__ __forceinline__ void wait_vm_stages(int r) {
+  if (r >= 3) wait_vm<3 * LPW>();
+  else if (r == 2) wait_vm<2 * LPW>();
+  else if (r == 1) wait_vm<LPW>();
+  else wait_vm<0>();
+}
+
+template <int BN, int NSG, int BKP, bool F16>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
+  using C = PPCfg<BN, NSG, BKP>;
+  constexpr int KS = C::KS;
+  using OA = typename C::OA;
+  using OB = typename C::OB;
+  constexpr int BM = C::BM, BK = C::BK, FM = C::FM, FN = C::FN, LPW = C::LPW;
+  constexpr int D = NSG - 1;   // prefetch distance, in the group's own stages
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::SMEM];
+  bf16_t *smem = (bf16_t *)smem_raw;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // the wave index is the same on every lane: keep it (and every branch on
+  // the group) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wj = wave & 3;
+  const int lr = lane & 15, lg = lane >> 4;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.raster_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int K = p.K;
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  bf16_t *ring = smem + grp * C::RING;
+  auto At = [&](int slot) { return ring + slot * C::STAGE; };
+  auto Bt = [&](int slot) { return ring + slot * C::STAGE + OA::ELEMS; };
+  const int nk = (K + BK - 1) / BK;            // global k-stages
+  const int nkg = (nk - grp + 1) / 2;           // this group's stages (global 2 i + grp)
+  const int iters = (nk + 1) / 2;               // phases pairs, the same for both groups
+  // own stage i -> LDS slot i % NSG, global k offset (2 i + grp) BK
+  auto issue = [&](int i) {
+    const int k0 = (2 * i + grp) * BK;
+    OA::template issue<4>(At(i % NSG), rsa, p.lda, m0, k0, p.M, K, wj, lane);
+    OB::template issue<4>(Bt(i % NSG), rsb, p.ldb, n0, k0, p.N, K, wj, lane);
+  };
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < nkg) issue(i);
+  // own stage 0 landed (the loads of stages 1 .. D-1 may still fly)
+  wait_vm_stages<LPW>(min(D - 1, nkg - 1));
+  pp_barrier();
+  if (grp == 1) pp_barrier();   // group 1 runs one phase behind
+  bf16x8_t fa[KS][FM], fb[KS][FN];
+  for (int i = 0; i < iters; ++i) {
+    const bool have = i < nkg;
+    // ---- memory phase: this stage's fragments, a later stage's loads
+    if (have) {
+      const bf16_t *as = At(i % NSG), *bs = Bt(i % NSG);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[s][j] = OB::frag(bs, wj * C::WTN + j * 16, 32 * s, lr, lg);
+#pragma unroll
+        for (int m = 0; m < FM; ++m) fa[s][m] = OA::frag(as, m * 16, 32 * s, lr, lg);
+      }
+      if (i + D < nkg) issue(i + D);
+      wait_lgkm0();
+    }
+    pp_barrier();
+    // ---- compute phase
+    if (have) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int m = 0; m < FM; ++m)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[m][j] = lp_mfma<F16>(fa[s][m], fb[s][j], acc[m][j]);
+      // own stage i+1 must have landed before the barrier that opens it;
+      // the loads of stages i+2 .. i+D may still fly
+      if (i + 1 < nkg) wait_vm_stages<LPW>(min(D - 1, nkg - 2 - i));
+    }
+    pp_barrier();
+  }
+  if (grp == 0) pp_barrier();   // both groups have passed the same number
+
+  // ---- the two partial tiles meet in LDS: group 0 stores, group 1 adds
+  float *Cs = (float *)smem_raw;
+  if (grp == 0) {
+#pragma unroll
+    for (int m = 0; m < FM; ++m)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Cs[(m * 16 + lg * 4 + r) * C::LDC + wj * C::WTN + j * 16 + lr] = acc[m][j][r];
+  }
+  __syncthreads();
+  if (grp == 1) {
+#pragma unroll
+    for (int m = 0; m < FM; ++m)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Cs[(m * 16 + lg * 4 + r) * C::LDC + wj * C::WTN + j * 16 + lr] += acc[m][j][r];
+  }
+  __syncthreads();
+  // ---- epilogue: 4 consecutive columns per thread, rows in turn; column
+  // sums (bias gradients) of the stored values go back into the tile and
+  // thread t < BN adds up column t.
+  constexpr int TPR = BN / 4;
+  const int nv = p.n_valid;
+  for (int idx = tid; idx < BM * TPR; idx += C::NT) {
+    const int rr = idx / TPR, cc = (idx % TPR) * 4;
+    const int m = m0 + rr, n = n0 + cc;
+    float4 *cp = (float4 *)(Cs + rr * C::LDC + cc);
+    if (m >= p.M || n >= nv) {
+      if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    float4 v = *cp;
+    if (p.bias) {
+      if (n + 3 < nv) {
+        const float4 b = *(const float4 *)(p.bias + n);
+        v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+      } else {
+        v.x += p.bias[n];
+        if (n + 1 < nv) v.y += p.bias[n + 1];
+        if (n + 2 < nv) v.z += p.bias[n + 2];
+      }
+    }
+    const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
+    if (p.colsum) *cp = st;
+  }
+  if (p.colsum) {
+    __syncthreads();
+    if (tid < BN && n0 + tid < nv) {
+      float csum = 0.f;
+      for (int rr = 0; rr < BM; ++rr) csum += Cs[rr * C::LDC + tid];
+      unsafeAtomicAdd(&p.colsum[n0 + tid], csum);
+    }
+  }
+}
+
+template <int BN, int NSG, int BKP>
+int launch_pp(tt_ctx *ctx, const GemmArgs &g) {
+  using C = PPCfg<BN, NSG, BKP>;
+  GemmParams p{};
+  p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb;
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.epi = g.epi; p.out = g.out; p.ldo = g.ldo; p.out_bf16 = g.out_bf16 ? 1 : 0;
+  p.bias = g.bias; p.resid = g.resid; p.ldr = g.ldr; p.aux = g.aux; p.ldx = g.ldx;
+  p.n_valid = g.n_valid > 0 ? min(g.n_valid, g.N) : g.N;
+  p.vec_out = gemm_vec_out(g) ? 1 : 0;
+  p.colsum = g.colsum;
+  p.raster_n = g.raster == 2 ? 1 : 0;
+  p.a_bytes = (uint32_t)gemm_extent_bytes(true, g.M, g.K, g.lda);
+  p.b_bytes = (uint32_t)gemm_extent_bytes(true, g.N, g.K, g.ldb);
+  p.tiles_m = (g.M + C::BM - 1) / C::BM;
+  p.tiles_n = (g.N + BN - 1) / BN;
+  p.k_chunk = g.K;
+  const int tiles = p.tiles_m * p.tiles_n;
+  static char names[2][80];
+  char *name = names[g.f16 ? 1 : 0];
+  if (!name[0])
+    snprintf(name, sizeof names[0], "gemm_pp_kernel<%d, %d, %d, %s>", BN, NSG, BKP,
+             g.f16 ? "true" : "false");
+  tt_prof_scope prof(ctx, name, 2.0 * g.M * g.N * g.K, gemm_bytes(g));
+  if (g.f16)
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, NSG, BKP, true>), dim3(tiles), dim3(C::NT), 0, ctx->stream, p);
+  else
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, NSG, BKP, false>), dim3(tiles), dim3(C::NT), 0, ctx->stream, p);
+  return tt_check_launch(ctx, "gemm_pp");
+}
+
 // out (+)= sum of the split partials (accumulate = 0: out is overwritten).
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(float *__restrict__ out, int ldo,
                                                              const float *__restrict__ ws, int M,
@@ -897,6 +1149,9 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 // of the GPT-2 step's shapes on MI355X:
 //  * k-major x k-major products (dX = dY W, forward GEMMs against transposed
 //    weights, the LM head):
+//      N < 1536 (the N = 768 products), M > 128: the ping-pong kernel,
+//        128 x 192, two 64-deep stages per group (gemm_pp_kernel)
+//    and otherwise:
 //      K >= 8192 (LM-head dH)                   128 x 192, BK 64, 3 stages
 //      >= 512 tiles of 256 x 128:  GELU-backward epilogue -> 128 x 192, BK 64,
 //                                  2 stages; others -> 256 x 128, BK 32, 3
@@ -927,6 +1182,9 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
     if (g.colsum && !(g.a_kmajor && g.b_kmajor))
       return tt_set_error(ctx, TT_EINVAL, "gemm_bf16: column sums need the k-major kernel");
     if (!(g.a_kmajor && g.b_kmajor)) return launch<256, 128, 4, 2>(ctx, g, 1);
+    // the narrow products (N = 768: projections, down-projection, every dX
+    // but the GELU-backward one, the LM-head dH): ping-pong tile
+    if (g.N < 1536 && g.M > 128) return launch_pp<192, 2, 64>(ctx, g);
     if (g.K >= 8192) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
     if (tiles >= 512) {
       if (g.epi == EPI_GELU_BWD) return launch3<128, 192, 64, 2, 4, 2>(ctx, g, 1);
