@@ -518,3 +518,21 @@ def tt_model_prefill(ctx, model, cache, B, T, tok, logits, next_tok):
 def tt_model_decode(ctx, model, cache, B, pos, tok, logits, next_tok):
     return ctx.check(lib().tt_model_decode(ctx.handle, model.handle, cache.handle, B, pos,
                                            _ptr(tok), _ptr(logits), _ptr(next_tok)))
+
+
+# ------------------------------------------------------------------ probes
+
+def tt_probe_mfma(ctx, waves_per_simd=2, accumulators=16, iters=20000):
+    """Dense bf16 MFMA rate (TFLOP/s) with register operands only."""
+    out = _C.c_double(0.0)
+    ctx.check(lib().tt_probe_mfma(ctx.handle, waves_per_simd, accumulators, iters, _C.byref(out)))
+    return out.value
+
+
+def tt_probe_hbm(ctx, buf, copy=False):
+    """Streaming HBM rate (GB/s) over a device tensor (read, or copy of its
+    first half over its second)."""
+    out = _C.c_double(0.0)
+    nbytes = buf.numel() * buf.element_size()
+    ctx.check(lib().tt_probe_hbm(ctx.handle, _ptr(buf), nbytes, 1 if copy else 0, _C.byref(out)))
+    return out.value

@@ -121,6 +121,8 @@ SIGS = {
     "tt_kvcache_destroy": (None, [vp]),
     "tt_model_prefill": (i32, [vp, vp, vp, i32, i32, vp, vp, vp]),
     "tt_model_decode": (i32, [vp, vp, vp, i32, i32, vp, vp, vp]),
+    "tt_probe_mfma": (i32, [vp, i32, i32, i32, P(C.c_double)]),
+    "tt_probe_hbm": (i32, [vp, vp, sz, i32, P(C.c_double)]),
 }
 
 _lib = None

@@ -29,6 +29,13 @@ CFLAGS = [
 ]
 
 
+# Per-file additions.  The MFMA probe keeps its accumulators in VGPRs: left
+# to choose, the compiler holds them in AGPRs and copies every one between
+# the two register files on each loop iteration, which the probe would then
+# measure instead of the MFMA pipe.
+FILE_FLAGS = {"probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -37,7 +44,7 @@ def hipcc():
 
 
 def _compile(src, obj):
-    cmd = [hipcc()] + CFLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + CFLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

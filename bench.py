@@ -1,9 +1,12 @@
 """Benchmark: one GPT-2 training step (forward, backward, AdamW) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m]
+    python bench.py --workload block-fp32  (one GPT-2 block fwd+bwd in fp32, B=4, T=256)
+    python bench.py --workload lmhead-ce   (the tied LM head + CE fwd+bwd alone, N=8192)
     python bench.py --dtype fp16         (the same step in fp16 with dynamic loss scaling)
     python bench.py --decode             (greedy decoding with the KV cache, B=8)
     python bench.py --mlp                (the tiny classifier through the graph autograd)
+    python bench.py --probe              (the roofline probes alone: MFMA and HBM rates)
     python bench.py --calibrate-copy     (1 GiB device copies, for HBM counter scaling)
 
 Workload (default): GPT-2 124M — 12 layers, d=768, 12 heads, vocab 50257
@@ -26,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "train tokens/sec, GPT-2 124M fwd+bwd+AdamW step at 1 GPU; MFMA util %"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 (MFMA)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 WORKLOADS = {
@@ -97,11 +101,11 @@ def measured_traffic(workload, B, T, kernel):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
-def bound_of(k):
+def bound_of(k, peak_mfma=PEAK_BF16_TFLOPS):
     """The roofline that bounds a kernel: MFMA when its algorithmic intensity
     (FLOPs per HBM byte) reaches the ridge point of the two peaks, else HBM."""
     if k["flops"] > 0 and (k["bytes"] <= 0 or
-                           k["flops"] / k["bytes"] >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)):
+                           k["flops"] / k["bytes"] >= peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)):
         return "mfma"
     return "hbm"
 
@@ -111,7 +115,7 @@ def roofline(kernels, steps, ms, peak_mfma=PEAK_BF16_TFLOPS):
     pass): algorithmic FLOPs or bytes per launch over its average launch."""
     dom = max(kernels, key=lambda k: k["ms"])
     avg_ms = dom["ms"] / dom["calls"]
-    if bound_of(dom) == "mfma":
+    if bound_of(dom, peak_mfma) == "mfma":
         achieved = dom["flops"] / dom["calls"] / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s"}
@@ -126,6 +130,55 @@ def roofline(kernels, steps, ms, peak_mfma=PEAK_BF16_TFLOPS):
     roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
     roof["share_of_step"] = round(dom["ms"] / steps / ms, 4)
     return roof
+
+
+def measured_peaks(ctx):
+    """The roofline probes run live: dense bf16 MFMA on register operands
+    (the best of 2 and 4 waves per SIMD, 16 and 32 accumulators) and a
+    streaming HBM read and copy over 4 GiB."""
+    import torch
+    import autograd_transformer_amd as tt
+    mfma = max(tt.tt_probe_mfma(ctx, w, a, 4000) for w, a in ((2, 32), (4, 16), (4, 32)))
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    read = tt.tt_probe_hbm(ctx, buf, copy=False)
+    copy = tt.tt_probe_hbm(ctx, buf, copy=True)
+    del buf
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(read, 1),
+            "hbm_copy_gbs": round(copy, 1)}
+
+
+def add_measured(roof, peaks):
+    """The dominant kernel's rate against the live probe's ceiling too."""
+    if peaks is None:
+        return
+    if roof["bound"] == "mfma" and roof["peak"] == PEAK_BF16_TFLOPS:
+        m = peaks["mfma_bf16_tflops"]
+    elif roof["bound"] == "hbm":
+        m = peaks["hbm_copy_gbs"]
+    else:
+        return
+    roof["peak_measured"] = m
+    roof["frac_of_measured"] = round(roof["achieved"] / m, 4)
+
+
+def counter_mfma_busy(workload, B, T, kernel):
+    """The dominant kernel's MFMA busy share from the committed rocprofv3
+    counter summary (SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE over the MFMA
+    probe's ratio), or None when absent or measured on other sources."""
+    from autograd_transformer_amd.pmc_traffic import source_digest
+    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_t{T}_mfma_busy.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != source_digest():
+        log(f"[bench] {os.path.basename(path)} was measured on other sources: mfma_busy null")
+        return None
+    k = rec["kernels"].get(kernel)
+    if k is None:
+        hits = [v for n, v in rec["kernels"].items() if n.split("<")[0] == kernel]
+        k = hits[0] if len(hits) == 1 else None
+    return None if k is None else k["mfma_busy"]
 
 
 def log_kernels(kernels, steps, n=8):
@@ -332,12 +385,194 @@ def mlp_main(args):
     print(json.dumps(out), flush=True)
 
 
+def timed_steps(step, stream, warmup, steps):
+    """Warm-up, then `steps` steps between HIP events on `stream`: ms/step."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def profiled(ctx, step, steps):
+    ctx.profile(True)
+    for _ in range(steps):
+        step()
+    kernels = ctx.profile_report()
+    ctx.profile(False)
+    ctx.sync()
+    return kernels
+
+
+def oracle_rate(fn, min_s=10.0):
+    """Run fn repeatedly for about min_s seconds; seconds per call, calls."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return dt / n, n
+
+
+def block_main(args):
+    """One pre-LN GPT-2 block, forward and backward, in fp32 through
+    tt_block_fwd / tt_block_bwd: B=4, T=256, C=768, 12 heads, MLP 3072;
+    x ~ N(0,1), weights ~ N(0,0.02), LN 1/0, biases 0, upstream grad ~ N(0,1)
+    (weight gradients accumulate, as the call defines)."""
+    import numpy as np
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    d = syn.block_inputs(seed=2)
+    B, T, C, NH, F = d["B"], d["T"], d["C"], d["n_head"], d["F"]
+    ctx = tt.Context(arena_bytes=4 << 30, stream=stream)
+    w = {k: torch.from_numpy(v).cuda() for k, v in d["w"].items()}
+    g = {k: torch.zeros_like(v) for k, v in w.items()}
+    x, dy = torch.from_numpy(d["x"]).cuda(), torch.from_numpy(d["dy"]).cuda()
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    saved = tt.BlockSaved(ctx, B, T, C, NH, F, "f32")
+
+    def step():
+        tt.tt_block_fwd(ctx, saved, w, x, y)
+        tt.tt_block_bwd(ctx, saved, w, dy, dx, g)
+
+    K = max(args.steps, 50)
+    ms = timed_steps(step, stream, args.warmup, K)
+    kernels = profiled(ctx, step, K)
+    flops = step_flops(L=1, C=C, V=0, T=T, B=B, F=F)
+    tflops = flops / (ms / 1e3) / 1e12
+    log(f"[bench] block fp32: {ms * 1e3:.1f} us/step  {tflops:.1f} TFLOP/s "
+        f"({flops / 1e9:.2f} GFLOP)")
+    out = {
+        "metric": "single GPT-2 block fwd+bwd time, fp32 (B=4, T=256, d=768, 12 heads, MLP 3072)",
+        "value": round(ms * 1e3, 2), "unit": "us/step", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) input and upstream gradient, N(0,0.02) weights)",
+        "config": {"workload": "single GPT-2 block fwd+bwd, fp32, B=4 T=256 C=768 NH=12 F=3072",
+                   "tokens": B * T, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "roofline": roofline(kernels, K, ms, peak_mfma=PEAK_FP32_TFLOPS),
+    }
+    log_kernels(kernels, K)
+    if not args.no_cpu_baseline:
+        from oracle import gpt2 as og  # test infrastructure: the baseline leg only
+        cores = len(os.sched_getaffinity(0))
+        w64 = {k: v.astype(np.float64) for k, v in d["w"].items()}
+
+        def ref():
+            _, cache = og.block_fwd(d["x"], w64, NH, "f32")
+            og.block_bwd(cache, w64, d["dy"], NH, "f32")
+        dt, n = oracle_rate(ref)
+        out["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"{n} full block fwd+bwd steps of the same workload "
+                                         f"(float64 NumPy) in {n * dt:.1f} s"}
+    saved.close()
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+def lmhead_main(args):
+    """The tied LM head + mean cross-entropy, forward and backward, alone
+    (tt_lmhead_ce_fwdbwd): hidden [8192, 768] bf16 ~ N(0,1), W_emb [50257, 768]
+    bf16 ~ N(0,0.02), targets uniform; logits, loss, dHidden and dW_emb with
+    float32 accumulation."""
+    import numpy as np
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    N, C, V = 8192, 768, 50257
+    d = syn.lmhead_inputs(seed=4, N=N, C=C, V=V)
+    ctx = tt.Context(arena_bytes=4 << 30, stream=stream)
+    h = torch.from_numpy(d["h"]).to(torch.bfloat16).cuda()
+    wte = torch.from_numpy(d["wte"]).to(torch.bfloat16).cuda()
+    tgt = torch.from_numpy(d["targets"]).cuda()
+    loss = torch.zeros(1, device="cuda")
+    dh = torch.empty(N, C, device="cuda")
+    dwte = torch.zeros(V, C, device="cuda")
+
+    def step():
+        tt.tt_lmhead_ce_fwdbwd(ctx, "bf16", N, C, V, h, wte, tgt, loss, dh, dwte)
+
+    K = args.steps
+    ms = timed_steps(step, stream, args.warmup, K)
+    kernels = profiled(ctx, step, K)
+    flops = 3 * 2.0 * N * C * V
+    tflops = flops / (ms / 1e3) / 1e12
+    value = N / (ms / 1e3)
+    log(f"[bench] LM head + CE: {ms:.3f} ms/step  {value:,.0f} tokens/s  {tflops:.1f} TFLOP/s")
+    out = {
+        "metric": "fused LM head + cross-entropy fwd+bwd tokens/sec (hidden [8192,768] x "
+                  "W_emb [50257,768], bf16, fp32 accumulation)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden, N(0,0.02) W_emb, uniform targets)",
+        "config": {"workload": "LM head + CE fwd+bwd, N=8192 C=768 V=50257, bf16 / fp32 acc",
+                   "tokens": N, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline(kernels, K, ms),
+    }
+    log_kernels(kernels, K)
+    if not args.no_cpu_baseline:
+        from oracle import ops as oo  # test infrastructure: the baseline leg only
+        cores = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
+        rows = 512
+        h64 = d["h"][:rows].astype(np.float64)
+        w64 = d["wte"].astype(np.float64)
+
+        def ref():
+            oo.lmhead_ce_fwdbwd(h64, w64, d["targets"][:rows])
+        dt, n = oracle_rate(ref)
+        out["cpu_baseline"] = {"value": round(rows / dt, 2), "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"{n} oracle LM head + CE fwd+bwd calls on the first "
+                                         f"{rows} of the 8192 rows (float64 NumPy) in "
+                                         f"{n * dt:.1f} s"}
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+def probe_main(args):
+    """The roofline probes alone, several shapes of each."""
+    import torch
+    import autograd_transformer_amd as tt
+    torch.cuda.set_device(0)
+    ctx = tt.Context(arena_bytes=1 << 28)
+    res = {}
+    for w in (1, 2, 4):
+        for a in (8, 16, 32):
+            res[f"mfma_bf16_w{w}_acc{a}"] = round(tt.tt_probe_mfma(ctx, w, a, 8000), 1)
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    res["hbm_read_gbs"] = round(tt.tt_probe_hbm(ctx, buf, copy=False), 1)
+    res["hbm_copy_gbs"] = round(tt.tt_probe_hbm(ctx, buf, copy=True), 1)
+    ctx.close()
+    print(json.dumps({"probe": "roofline", "peak_vendor": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS,
+                                                           "hbm_gbs": PEAK_HBM_GBS},
+                      "measured": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="gpt2-124m",
+                    choices=sorted(WORKLOADS) + ["block-fp32", "lmhead-ce"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="16-bit format of the training step (fp16: dynamic loss scaling)")
@@ -345,6 +580,8 @@ def main():
                     help="measure greedy decoding with the KV cache instead of training")
     ap.add_argument("--mlp", action="store_true",
                     help="measure the tiny classifier's step through the graph autograd")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the roofline probes (MFMA and HBM) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -371,6 +608,15 @@ def main():
 
     if args.mlp:
         mlp_main(args)
+        return
+    if args.probe:
+        probe_main(args)
+        return
+    if args.workload == "block-fp32":
+        block_main(args)
+        return
+    if args.workload == "lmhead-ce":
+        lmhead_main(args)
         return
     w = WORKLOADS[args.workload]
     if args.decode:
@@ -462,6 +708,11 @@ def main():
     out["roofline"] = roofline(kernels, args.steps, ms)
     out["roofline"]["traffic"] = (measured_traffic(args.workload, B, T, out["roofline"]["kernel"])
                                   if args.dtype == "bf16" else None)
+    out["roofline"]["mfma_busy"] = (counter_mfma_busy(args.workload, B, T,
+                                                      out["roofline"]["kernel"])
+                                    if args.dtype == "bf16" else None)
+    # the live probes, after the timed and profiled passes
+    add_measured(out["roofline"], measured_peaks(ctx))
     log_kernels(kernels, args.steps)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")

@@ -507,6 +507,25 @@ int tt_graph_step(tt_graph *graph);
  * flows through it) and shape; every output nullable. */
 int tt_graph_tensor(tt_graph *graph, int id, float **value, float **grad, int *rows, int *cols);
 
+/* ------------------------------------------------------------------------ */
+/* Roofline probes (measurement only; the C++/CUDA page, section 2.2, times  */
+/* each op with an event pair).  They time, with HIP events on the context's */
+/* stream, what the GPU sustains with nothing else in the way; the benchmark */
+/* reports kernels against these next to the vendor's peak figures.  Both    */
+/* wait for the stream.                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* v_mfma_f32_16x16x32_bf16 on register operands only: waves_per_simd (1..8)
+ * four-wave workgroups per CU, each wave cycling over `accumulators` (8, 16
+ * or 32) independent accumulators for `iters` rounds (<= 2^24).  *tflops
+ * [host] receives the dense bf16 rate (2*16*16*32 FLOP per MFMA). */
+int tt_probe_mfma(tt_ctx *ctx, int waves_per_simd, int accumulators, int iters, double *tflops);
+/* Streaming HBM rate over a caller's device buffer of `bytes` (>= 1 MiB,
+ * multiple of 32, 16-byte aligned; its contents are read, and with copy != 0
+ * its first half is copied over its second half).  Five passes after one
+ * warm-up; *gbs [host] receives bytes read (+ written) per second / 1e9. */
+int tt_probe_hbm(tt_ctx *ctx, void *buf, size_t bytes, int copy, double *gbs);
+
 #ifdef __cplusplus
 }
 #endif
