@@ -8,7 +8,9 @@ import ctypes as C
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtt.so")
+# TT_LIB_PATH: another build of the same library (the host-sanitized one the
+# CPU ABI tests run against); by default the in-tree libtt.so
+LIB_PATH = os.environ.get("TT_LIB_PATH") or os.path.join(_PKG, "libtt.so")
 
 vp = C.c_void_p
 i32 = C.c_int
