@@ -487,6 +487,60 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
               Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
       }
       __syncthreads();
+      if (p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out) {
+        // The GELU-backward product: every pre-activation load of this
+        // thread's items is issued first, then the items are finished --
+        // one memory round trip per pass instead of one per item.
+        constexpr int ITEMS = (C::WTM * TPR + NT - 1) / NT;
+        uint2 hv[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          const int idx = tid + it * NT;
+          const int rr = idx / TPR, cc = (idx % TPR) * 4;
+          const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
+          hv[it] = make_uint2(0u, 0u);
+          if (idx < C::WTM * TPR && m < p.M && n + 3 < nv)
+            hv[it] = *(const uint2 *)((const bf16_t *)p.aux + (size_t)m * p.ldx + n);
+        }
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          const int idx = tid + it * NT;
+          if (idx >= C::WTM * TPR) break;
+          const int rr = idx / TPR, cc = (idx % TPR) * 4;
+          const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
+          float4 *cp = (float4 *)(Cs + rr * C::LDC + cc);
+          if (m >= p.M || n >= nv) {
+            if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
+            continue;
+          }
+          float4 v = *cp;
+          if (p.bias && blockIdx.z == 0) {
+            v.x += p.bias[n];
+            if (n + 1 < nv) v.y += p.bias[n + 1];
+            if (n + 2 < nv) v.z += p.bias[n + 2];
+            if (n + 3 < nv) v.w += p.bias[n + 3];
+          }
+          float4 st;
+          if (n + 3 < nv) {
+            const float h[4] = {lp_lo<F16>(hv[it].x), lp_hi<F16>(hv[it].x), lp_lo<F16>(hv[it].y),
+                                lp_hi<F16>(hv[it].y)};
+            const float a[4] = {v.x * gelu_grad_f(h[0]), v.y * gelu_grad_f(h[1]),
+                                v.z * gelu_grad_f(h[2]), v.w * gelu_grad_f(h[3])};
+            *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
+                make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
+            st = round_stored<F16>(p, a, 4);
+          } else {
+            st = epilogue4<F16>(p, m, n, v, nv - n);   // the ragged last columns
+          }
+          if (p.colsum) *cp = st;
+        }
+        if (p.colsum) {
+          __syncthreads();
+          if (tid < BN)
+            for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
+        }
+        continue;
+      }
       for (int idx = tid; idx < C::WTM * TPR; idx += NT) {
         const int rr = idx / TPR, cc = (idx % TPR) * 4;
         const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
@@ -963,6 +1017,48 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   // thread t < BN adds up column t.
   constexpr int TPR = BN / 4;
   const int nv = p.n_valid;
+  if (p.epi == EPI_RESID && p.vec_out && !p.colsum) {
+    // residual products: every residual load of this thread's items is
+    // issued first, then the sums are stored -- one memory round trip
+    // instead of one per item
+    constexpr int ITEMS = (BM * TPR + C::NT - 1) / C::NT;
+    float4 rv[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * C::NT;
+      const int rr = idx / TPR, cc = (idx % TPR) * 4;
+      const int m = m0 + rr, n = n0 + cc;
+      rv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx < BM * TPR && m < p.M && n + 3 < nv)
+        rv[it] = *(const float4 *)(p.resid + (size_t)m * p.ldr + n);
+    }
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * C::NT;
+      if (idx >= BM * TPR) break;
+      const int rr = idx / TPR, cc = (idx % TPR) * 4;
+      const int m = m0 + rr, n = n0 + cc;
+      if (m >= p.M || n >= nv) continue;
+      float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
+      if (p.bias) {
+        if (n + 3 < nv) {
+          const float4 b = *(const float4 *)(p.bias + n);
+          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+        } else {
+          v.x += p.bias[n];
+          if (n + 1 < nv) v.y += p.bias[n + 1];
+          if (n + 2 < nv) v.z += p.bias[n + 2];
+        }
+      }
+      if (n + 3 < nv) {
+        *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) =
+            make_float4(rv[it].x + v.x, rv[it].y + v.y, rv[it].z + v.z, rv[it].w + v.w);
+      } else {
+        epilogue4<F16>(p, m, n, v, nv - n);   // the ragged last columns
+      }
+    }
+    return;
+  }
   for (int idx = tid; idx < BM * TPR; idx += C::NT) {
     const int rr = idx / TPR, cc = (idx % TPR) * 4;
     const int m = m0 + rr, n = n0 + cc;
