@@ -81,24 +81,33 @@ def cpu_baseline(w, dtype="bf16"):
                       f"rounding, float64 NumPy) on 1 sequence of {T} tokens; {dt:.1f} s"}
 
 
-def measured_traffic(workload, B, T, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the library
+def _counter_record(key, what, kernel, field):
+    """`field` of `kernel` in the committed rocprofv3 counter summary
+    profiles/<key>_<what>.json, or None when there is none or the library
     sources changed since the counters were taken."""
     from autograd_transformer_amd.pmc_traffic import source_digest
-    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_t{T}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{key}_{what}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("source_digest") != source_digest():
-        log(f"[bench] {os.path.basename(path)} was measured on other sources: traffic null")
+        log(f"[bench] {os.path.basename(path)} was measured on other sources: {field} null")
         return None
     k = rec["kernels"].get(kernel)
     if k is None:   # timer names drop template arguments that rocprofv3 keeps
         hits = [v for n, v in rec["kernels"].items() if n.split("<")[0] == kernel]
         k = hits[0] if len(hits) == 1 else None
-    return None if k is None else k["hbm_bytes_per_launch"]
+    return None if k is None else k[field]
+
+
+def counter_fields(roof, key):
+    """roofline.traffic (HBM bytes per launch of the dominant kernel, from
+    FETCH_SIZE / WRITE_SIZE scaled by a device copy) and roofline.mfma_busy
+    (its MFMA utilisation from SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE),
+    both from the committed counter summaries of workload `key`."""
+    roof["traffic"] = _counter_record(key, "hbm_traffic", roof["kernel"], "hbm_bytes_per_launch")
+    roof["mfma_busy"] = _counter_record(key, "mfma_busy", roof["kernel"], "mfma_busy")
 
 
 def bound_of(k, peak_mfma=PEAK_BF16_TFLOPS):
@@ -159,26 +168,6 @@ def add_measured(roof, peaks):
         return
     roof["peak_measured"] = m
     roof["frac_of_measured"] = round(roof["achieved"] / m, 4)
-
-
-def counter_mfma_busy(workload, B, T, kernel):
-    """The dominant kernel's MFMA busy share from the committed rocprofv3
-    counter summary (SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE over the MFMA
-    probe's ratio), or None when absent or measured on other sources."""
-    from autograd_transformer_amd.pmc_traffic import source_digest
-    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_t{T}_mfma_busy.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        rec = json.load(fh)
-    if rec.get("source_digest") != source_digest():
-        log(f"[bench] {os.path.basename(path)} was measured on other sources: mfma_busy null")
-        return None
-    k = rec["kernels"].get(kernel)
-    if k is None:
-        hits = [v for n, v in rec["kernels"].items() if n.split("<")[0] == kernel]
-        k = hits[0] if len(hits) == 1 else None
-    return None if k is None else k["mfma_busy"]
 
 
 def log_kernels(kernels, steps, n=8):
@@ -463,6 +452,7 @@ def block_main(args):
         "tflops": round(tflops, 2),
         "roofline": roofline(kernels, K, ms, peak_mfma=PEAK_FP32_TFLOPS),
     }
+    counter_fields(out["roofline"], "block-fp32_b4_t256")
     log_kernels(kernels, K)
     if not args.no_cpu_baseline:
         from oracle import gpt2 as og  # test infrastructure: the baseline leg only
@@ -526,6 +516,8 @@ def lmhead_main(args):
         "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline(kernels, K, ms),
     }
+    counter_fields(out["roofline"], "lmhead-ce_n8192_v50257")
+    add_measured(out["roofline"], measured_peaks(ctx))
     log_kernels(kernels, K)
     if not args.no_cpu_baseline:
         from oracle import ops as oo  # test infrastructure: the baseline leg only
@@ -706,11 +698,8 @@ def main():
         "loss": round(last_loss, 5),
     }
     out["roofline"] = roofline(kernels, args.steps, ms)
-    out["roofline"]["traffic"] = (measured_traffic(args.workload, B, T, out["roofline"]["kernel"])
-                                  if args.dtype == "bf16" else None)
-    out["roofline"]["mfma_busy"] = (counter_mfma_busy(args.workload, B, T,
-                                                      out["roofline"]["kernel"])
-                                    if args.dtype == "bf16" else None)
+    counter_fields(out["roofline"], f"{args.workload}_b{B}_t{T}" + ("" if args.dtype == "bf16"
+                                                                   else "_" + args.dtype))
     # the live probes, after the timed and profiled passes
     add_measured(out["roofline"], measured_peaks(ctx))
     log_kernels(kernels, args.steps)

@@ -381,6 +381,43 @@ def test_gpt2_124m_batch_of_8_is_mean_of_sequences(gpt2_124m):
     _batch_is_mean_of_sequences(ctx, model, params, 8, 768, seed=41)
 
 
+def test_gpt2_350m_width_b16_t1024_two_layers_elementwise():
+    """The 350M step's launch configuration -- B=16, T=1024, C=1024, 16 heads,
+    MLP 4096, V=50257 padded to 50304, bf16 -- with two layers, element by
+    element against the oracle run here: the loss, every gradient tensor, the
+    last vocabulary rows and last position of the embedding gradients."""
+    L, B, T, C, NH, V = 2, 16, 1024, 1024, 16, 50257
+    shape = syn.ModelShape(n_layer=L, n_embd=C, n_head=NH, vocab=V, block_size=T)
+    cfg = og.GPTConfig(n_layer=L, n_embd=C, n_head=NH, vocab=V, block_size=T)
+    params = syn.gpt2_params(shape, seed=53, bias_std=0.02, ln_std=0.05)
+    tok, tgt = syn.gpt2_tokens(B, T, V, seed=53)
+    ctx = tt.Context(arena_bytes=24 << 30)
+    model = make_model(ctx, shape, B, T, "bf16", params, V_pad=50304)
+    loss = empty((1,))
+    tt.tt_model_fwd_bwd(ctx, model, B, T, dev(tok, "i32"), dev(tgt, "i32"), loss)
+    sync()
+    g = grads_of(model)
+    model.close()
+    ctx.close()
+    print("[oracle] 2-layer GPT-2 350M width, 16 x 1024 tokens ...", flush=True)
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    l_ref, g_ref = og.model_fwd_bwd(p64, tok, tgt, cfg, "bf16")
+    errs, kb = {}, {}
+    for k in g_ref:
+        got = g[k][:V] if k == "wte" else g[k]
+        rest, rest_ref, key = split_key_bias(k, got, g_ref[k], C)
+        errs[k] = rel_l2(rest, rest_ref)
+        if key is not None:
+            kb[k] = np.linalg.norm(key) / np.linalg.norm(rest_ref)
+    errs["wte last vocab rows"] = rel_l2(g["wte"][V - 81:V], g_ref["wte"][V - 81:V])
+    errs["wpe last position"] = rel_l2(g["wpe"][T - 1], g_ref["wpe"][T - 1])
+    print(f"loss {host(loss)[0]:.6f} vs {l_ref:.6f}; max rel-L2 {max(errs.values()):.2e}")
+    assert abs(host(loss)[0] - l_ref) / l_ref <= 2e-2
+    bad = {k: e for k, e in errs.items() if not e <= 2e-2}
+    assert not bad, bad
+    assert max(kb.values()) <= KEY_BIAS_NOISE["bf16"], kb
+
+
 # GPT-2 350M (24 layers, C=1024, 16 heads, MLP 4096) at its batch of 16.
 
 @pytest.fixture(scope="module")

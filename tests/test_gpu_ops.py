@@ -403,6 +403,32 @@ def test_lmhead_ce_full_size_against_oracle_samples(ctx):
         assert rel_l2(flat[np.array(r["idx"])], np.array(r["val"])) <= 2e-2, name
 
 
+def test_lmhead_ce_full_size_elementwise(ctx):
+    """The LM head + CE workload at its benchmarked size (hidden [8192, 768] x
+    W_emb [50257, 768], bf16) element by element against the oracle run here:
+    the loss, the whole of dHidden and dW_emb (rel-L2), their last rows (the
+    ragged end of the token and vocabulary ranges) and the dW_emb rows of the
+    targets."""
+    N, C, V = 8192, 768, 50257
+    d = syn.lmhead_inputs(seed=4, N=N, C=C, V=V)
+    loss, dh, dw = empty((1,)), empty((N, C)), zeros((V, C))
+    tt.tt_lmhead_ce_fwdbwd(ctx, "bf16", N, C, V, dev(d["h"], "bf16"), dev(d["wte"], "bf16"),
+                           dev(d["targets"], "i32"), loss, dh, dw)
+    sync()
+    l_ref, dh_ref, dw_ref, _ = oracle.lmhead_ce_fwdbwd(
+        d["h"].astype(np.float64), d["wte"].astype(np.float64), d["targets"],
+        store_logits=oracle.round_bf16, store_dlogits=oracle.round_bf16)
+    got_dh, got_dw = host(dh), host(dw)
+    errs = {"loss": abs(host(loss)[0] - l_ref) / l_ref,
+            "dh": rel_l2(got_dh, dh_ref), "dwte": rel_l2(got_dw, dw_ref),
+            "dh last row": rel_l2(got_dh[-1], dh_ref[-1]),
+            "dwte last rows": rel_l2(got_dw[V - 81:], dw_ref[V - 81:]),
+            "dwte target rows": rel_l2(got_dw[d["targets"][-64:]], dw_ref[d["targets"][-64:]])}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: e for k, e in errs.items() if not e <= 2e-2}
+    assert not bad, bad
+
+
 # ------------------------------------------------------------ error paths
 
 def test_errors_are_reported_not_raised_by_kernels(ctx):
