@@ -382,11 +382,17 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
   const int vecn = 16 / esz;
   bool vec = tt_aligned16(g.A) && tt_aligned16(g.B) && (g.lda % vecn == 0) &&
              (g.ldb % vecn == 0);
+  // fp32 products whose 128 x 128 tile grid would leave CUs idle (the
+  // single-block workload has 1024 tokens: 48 to 144 such tiles for 256 CUs)
+  // take 64 x 64 tiles: four times the workgroups, each of four waves of
+  // 32 x 32.
+  const bool small_f32 = mode == TT_F32 && ((g.M + 127) / 128) * ((g.N + 127) / 128) < 256;
+  const int tb = small_f32 ? 64 : 128;
   int split = 1;
   if (g.epi == EPI_ACCUM) {
     // Split the reduction when the output tile grid is too small to fill 256
     // CUs; partial sums meet in the float32 output through atomics.
-    int tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    int tiles = ((g.M + tb - 1) / tb) * ((g.N + tb - 1) / tb);
     int kb = (g.K + 63) / 64;
     split = 1;
     while (tiles * split < 512 && split * 2 <= kb / 4) split *= 2;
@@ -411,6 +417,8 @@ int tt_gemm(tt_ctx *ctx, tt_mode mode, const GemmArgs &g) {
     TT_TRY(tt_gemm_bf16(ctx, h));
   else if (mode == TT_BF16)
     TT_TRY((dispatch_layout<bf16_t, 128, 128, 64, 2, 2>(ctx, h, split, vec)));
+  else if (small_f32)
+    TT_TRY((dispatch_layout<float, 64, 64, 32, 2, 2>(ctx, h, split, vec)));
   else
     TT_TRY((dispatch_layout<float, 128, 128, 32, 2, 2>(ctx, h, split, vec)));
   if (g.colsum && !fused_sum) {
