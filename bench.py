@@ -95,10 +95,24 @@ def _counter_record(key, what, kernel, field):
         log(f"[bench] {os.path.basename(path)} was measured on other sources: {field} null")
         return None
     k = rec["kernels"].get(kernel)
-    if k is None:   # timer names drop template arguments that rocprofv3 keeps
-        hits = [v for n, v in rec["kernels"].items() if n.split("<")[0] == kernel]
-        k = hits[0] if len(hits) == 1 else None
-    return None if k is None else k[field]
+    if k is not None:
+        return k[field]
+    # A timer name can stand for several template instances that rocprofv3
+    # lists apart ("gemm_kernel<f32>" covers every fp32 layout and tile):
+    # combine them, bytes weighted by launches, utilisation by busy time.
+    base, _, targ = kernel.partition("<")
+    dtype = {"f32>": "float", "bf16>": "__bf16"}.get(targ)
+    hits = [v for n, v in rec["kernels"].items()
+            if n.split("<")[0] == base and
+            (dtype is None or n.partition("<")[2].split(",")[0].strip(" >") == dtype)]
+    if not hits:
+        return None
+    wkey = "gui_active" if field == "mfma_busy" else "launches"
+    w = sum(v[wkey] for v in hits)
+    if w <= 0:
+        return None
+    val = sum(v[field] * v[wkey] for v in hits) / w
+    return round(val, 4) if field == "mfma_busy" else int(round(val))
 
 
 def counter_fields(roof, key):
