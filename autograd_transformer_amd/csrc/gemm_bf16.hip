@@ -526,8 +526,8 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
                                 lp_hi<F16>(hv[it].y)};
             const float a[4] = {v.x * gelu_grad_f(h[0]), v.y * gelu_grad_f(h[1]),
                                 v.z * gelu_grad_f(h[2]), v.w * gelu_grad_f(h[3])};
-            *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-                make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
+            out_store((bf16_t *)p.out + (size_t)m * p.ldo + n,
+                      make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3])));
             st = round_stored<F16>(p, a, 4);
           } else {
             st = epilogue4<F16>(p, m, n, v, nv - n);   // the ragged last columns
@@ -1051,8 +1051,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
         }
       }
       if (n + 3 < nv) {
-        *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) =
-            make_float4(rv[it].x + v.x, rv[it].y + v.y, rv[it].z + v.z, rv[it].w + v.w);
+        out_store((float *)p.out + (size_t)m * p.ldo + n,
+                  make_float4(rv[it].x + v.x, rv[it].y + v.y, rv[it].z + v.z, rv[it].w + v.w));
       } else {
         epilogue4<F16>(p, m, n, v, nv - n);   // the ragged last columns
       }

@@ -26,6 +26,19 @@ struct GemmParams {
   const uint16_t *group_map;     // grouped launch: workgroup -> table entry
 };
 
+// Vector stores of a product's outputs: streaming (non-temporal) stores,
+// which the L2 keeps at the front of its eviction order, so the tiles being
+// written do not push the operand panels that other workgroups still read
+// out of L2 (measured: 1.6 % off the GPT-2 124M step).
+__device__ __forceinline__ void out_store(void *dst, uint2 v) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, (u32x2_t *)dst);
+}
+__device__ __forceinline__ void out_store(void *dst, float4 v) {
+  typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f32x4v_t{v.x, v.y, v.z, v.w}, (f32x4v_t *)dst);
+}
+
 // out_bf16: the output is 16-bit (bf16, or binary16 when F16).
 template <bool F16 = false>
 __device__ __forceinline__ void store_out(void *out, int ldo, int out_bf16, int m, int n, float v) {
@@ -61,8 +74,8 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
       if (p.epi == EPI_GELU) {
         if (p.aux) {
           if (full && p.out_bf16)
-            *(uint2 *)((bf16_t *)p.aux + (size_t)m * p.ldx + n) =
-                make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
+            out_store((bf16_t *)p.aux + (size_t)m * p.ldx + n,
+                      make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3])));
           else
             for (int q = 0; q < lim; ++q) store_out<F16>(p.aux, p.ldx, p.out_bf16, m, n + q, a[q]);
         }
@@ -71,10 +84,10 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
       }
       if (full) {
         if (p.out_bf16)
-          *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-              make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
+          out_store((bf16_t *)p.out + (size_t)m * p.ldo + n,
+                    make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3])));
         else
-          *(float4 *)((float *)p.out + (size_t)m * p.ldo + n) = make_float4(a[0], a[1], a[2], a[3]);
+          out_store((float *)p.out + (size_t)m * p.ldo + n, make_float4(a[0], a[1], a[2], a[3]));
       } else {
         for (int q = 0; q < lim; ++q) store_out<F16>(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
       }
@@ -85,7 +98,7 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
       float *op = (float *)p.out + (size_t)m * p.ldo + n;
       if (full) {
         float4 r = *(const float4 *)rp;
-        *(float4 *)op = make_float4(r.x + a[0], r.y + a[1], r.z + a[2], r.w + a[3]);
+        out_store(op, make_float4(r.x + a[0], r.y + a[1], r.z + a[2], r.w + a[3]));
       } else {
         for (int q = 0; q < lim; ++q) op[q] = rp[q] + a[q];
       }
@@ -109,8 +122,8 @@ __device__ __forceinline__ float4 epilogue4(const GemmParams &p, int m, int n, f
 #pragma unroll
       for (int q = 0; q < 4; ++q) a[q] *= gelu_grad_f(h[q]);
       if (full && p.out_bf16)
-        *(uint2 *)((bf16_t *)p.out + (size_t)m * p.ldo + n) =
-            make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3]));
+        out_store((bf16_t *)p.out + (size_t)m * p.ldo + n,
+                  make_uint2(lp_pack2<F16>(a[0], a[1]), lp_pack2<F16>(a[2], a[3])));
       else
         for (int q = 0; q < lim; ++q) store_out<F16>(p.out, p.ldo, p.out_bf16, m, n + q, a[q]);
       return round_stored<F16>(p, a, lim);

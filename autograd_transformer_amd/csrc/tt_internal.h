@@ -182,24 +182,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))).
-// tanh(u) = 1 - 2/(exp(2u)+1) evaluated with the hardware exp; saturates
-// correctly for |u| large (exp -> inf gives 1, exp -> 0 gives -1).
+// GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi)(x + 0.044715 x^3).
+// The kernels use the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), so
+// gelu(x) = x s with s = 1 / (1 + 2^(-2u log2 e)): one hardware exp2 and one
+// hardware reciprocal per element instead of an exp and an IEEE division.
+// The derivative is s + x s (1 - s) 2u'(x), u'(x) = sqrt(2/pi)(1 + 3 0.044715
+// x^2).  Saturation: for large |x| the exp2 goes to 0 or inf and s to 1 or 0.
 #define TT_GELU_K 0.7978845608028654f
 #define TT_GELU_A 0.044715f
-__device__ __forceinline__ float tt_tanh(float u) {
-  float e = __expf(2.0f * u);
-  return 1.0f - 2.0f / (e + 1.0f);
+#define TT_GELU_C0 (-2.302208198144325f)    // -2 K log2(e)
+#define TT_GELU_C1 (-0.1029432395800235f)   // -2 K A log2(e)
+__device__ __forceinline__ float gelu_sig(float x) {   // s = 1 / (1 + exp(-2u))
+  const float w = __builtin_fmaf(x * x, TT_GELU_C1, TT_GELU_C0);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w * x));
 }
-__device__ __forceinline__ float gelu_f(float x) {
-  float u = TT_GELU_K * (x + TT_GELU_A * x * x * x);
-  return 0.5f * x * (1.0f + tt_tanh(u));
-}
+__device__ __forceinline__ float gelu_f(float x) { return x * gelu_sig(x); }
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  float u = TT_GELU_K * (x + TT_GELU_A * x * x * x);
-  float t = tt_tanh(u);
-  float du = TT_GELU_K * (1.0f + 3.0f * TT_GELU_A * x * x);
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * du;
+  const float s = gelu_sig(x);
+  const float du2 = __builtin_fmaf(x * x, 6.0f * TT_GELU_K * TT_GELU_A, 2.0f * TT_GELU_K);   // 2u'(x)
+  return __builtin_fmaf(x * du2, __builtin_fmaf(-s, s, s), s);
 }
 
 // ---------------------------------------------------------------------------
