@@ -686,15 +686,33 @@ __global__ void __launch_bounds__(CE_THREADS, 8) ce_reg_kernel(int N, int V, int
 }
 
 // Deterministic mean of n floats in one block.
-__global__ void __launch_bounds__(256) mean_kernel(int n, const float *__restrict__ src,
-                                                   float *__restrict__ out) {
+// Mean of n values by one workgroup of 1024 threads, in a fixed order (the
+// same bits every run): each thread sums a strided share with 8 independent
+// loads in flight per round, then waves and workgroup reduce.
+__global__ void __launch_bounds__(1024) mean_kernel(int n, const float *__restrict__ src,
+                                                    float *__restrict__ out) {
+  constexpr int U = 8;
   float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) s += src[i];
-  __shared__ float red[4];
+  for (int i0 = threadIdx.x; i0 < n; i0 += 1024 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 1024;
+      v[u] = i < n ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  __shared__ float red[16];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) out[0] = ((red[0] + red[1]) + (red[2] + red[3])) / (float)n;
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += red[w];
+    out[0] = t / (float)n;
+  }
 }
 
 }  // namespace
@@ -919,6 +937,6 @@ int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
   }
   TT_TRY(tt_check_launch(ctx, "ce"));
   tt_prof_scope prof(ctx, "mean_kernel", 0.0, 4.0 * N);
-  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, ctx->stream, N, per_row_loss, loss);
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, ctx->stream, N, per_row_loss, loss);
   return tt_check_launch(ctx, "ce_mean");
 }
