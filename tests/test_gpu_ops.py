@@ -215,6 +215,27 @@ def test_gelu(ctx, mode):
     assert host(Y)[np.argmin(np.abs(x))] == pytest.approx(0.0, abs=1e-3)
 
 
+def test_gelu_saturation_and_sign(ctx):
+    """GELU and its derivative from the far negative tail (exp overflow: the
+    sigmoid factor must become exactly 0, not NaN) through zero to the far
+    positive tail (GELU(x) = x, derivative 1), element by element in fp32."""
+    x = np.array([-1e4, -100, -20, -10, -5, -3, -1, -0.1, -1e-3, 0.0,
+                  1e-3, 0.1, 1, 3, 5, 10, 20, 100, 1e4], np.float32)
+    n = x.size
+    dy = np.ones(n, np.float32)
+    X, dY = dev(x), dev(dy)
+    Y, dX = empty((n,)), empty((n,))
+    tt.tt_gelu_fwd(ctx, "f32", n, X, Y)
+    tt.tt_gelu_bwd(ctx, "f32", n, X, dY, dX)
+    sync()
+    y, g = host(Y), host(dX)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(g))
+    y_ref, g_ref = oracle.gelu_fwd(x), oracle.gelu_bwd(x, dy)
+    np.testing.assert_allclose(y, y_ref, rtol=4e-6, atol=1e-30)
+    np.testing.assert_allclose(g, g_ref, rtol=4e-6, atol=2e-6)
+    assert y[x <= -20].max() <= 0.0 and y[x >= 20].tolist() == x[x >= 20].tolist()
+
+
 # ---------------------------------------------------------------- attention
 
 ATTN = [(2, 1, 2), (1, 77, 3), (2, 256, 2), (1, 300, 1), (1, 1024, 1)]
