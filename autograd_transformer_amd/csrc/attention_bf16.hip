@@ -492,15 +492,16 @@ attn_dq_bf16_kernel(int T, int NH, const bf16_t *__restrict__ qkv, const bf16_t 
         for (int j = 0; j < 4; ++j) {
           const f32x4_t sacc = mfma<F16>(row_frag(ks, j * 16, 32, lr, lg), qf[1],
                                     mfma<F16>(row_frag(ks, j * 16, 0, lr, lg), qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-          const f32x4_t dpacc = mfma<F16>(row_frag(vs, j * 16, 32, lr, lg), of[1],
-                                     mfma<F16>(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          // dPᵀ - D: the accumulation starts from -D
+          const f32x4_t dpd = mfma<F16>(row_frag(vs, j * 16, 32, lr, lg), of[1],
+                                   mfma<F16>(row_frag(vs, j * 16, 0, lr, lg), of[0], f32x4_t{-Dq, -Dq, -Dq, -Dq}));
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float pv = ex2(fmaf(sacc[r], SL2, -lq));
             if constexpr (MASK) {
               if (k0 + j * 16 + lg * 4 + r > q) pv = 0.f;
             }
-            dsv[j][r] = pv * (dpacc[r] - Dq);
+            dsv[j][r] = pv * dpd[r];
           }
         }
       };
