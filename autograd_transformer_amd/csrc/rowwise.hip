@@ -791,7 +791,7 @@ int tt_layernorm_bwd_rows(tt_ctx *ctx, tt_mode mode, int N, int C, const float *
              part_groups);
   const int rpw = lnp_rpw(N);   // rows per wave of the row-walking kernel (nv <= 4)
   {
-    tt_prof_scope prof(ctx, "layernorm_bwd_kernel", 0.0,
+    tt_prof_scope prof(ctx, nv <= 4 ? "layernorm_bwd_pipe_kernel" : "layernorm_bwd_kernel", 0.0,
                        (double)N * C * (12.0 + (dres ? 4.0 : 0.0) + (dx_bf16 ? 2.0 : 0.0)) +
                            8.0 * N + 12.0 * G * C);
 #define TT_LNP_RPW(NV, RPW)                                                               \
@@ -910,11 +910,14 @@ int tt_ce_impl(tt_ctx *ctx, tt_mode mode, int N, int V, int ld, void *logits,
   TT_REQUIRE(ctx, logits && targets && per_row_loss && loss, "ce: NULL pointer");
   {
   // algorithmic: one read and one write of the logits
-  tt_prof_scope prof(ctx, "ce_kernel", 0.0, 2.0 * N * (double)ld * (tt_lowp(mode) ? 2.0 : 4.0) + 8.0 * N);
+  // (named after the kernel the row length selects)
+  const bool reg = tt_lowp(mode) && ld <= CE_VPT * 8 * CE_THREADS;
+  tt_prof_scope prof(ctx, reg ? "ce_reg_kernel" : "ce_kernel", 0.0,
+                     2.0 * N * (double)ld * (tt_lowp(mode) ? 2.0 : 4.0) + 8.0 * N);
   if (tt_lowp(mode)) {
     TT_REQUIRE(ctx, ld % 8 == 0 && tt_aligned16(logits), "ce(16-bit): ld %% 8 and 16-byte alignment required");
     const bool f16 = mode == TT_FP16;
-    if (ld <= CE_VPT * 8 * CE_THREADS) {
+    if (reg) {
       if (f16)
         hipLaunchKernelGGL(ce_reg_kernel<true>, dim3(N), dim3(CE_THREADS), 0, ctx->stream, N, V, ld,
                            (bf16_t *)logits, targets, per_row_loss, grad_scale, scale_dev,

@@ -184,6 +184,25 @@ def add_measured(roof, peaks):
     roof["frac_of_measured"] = round(roof["achieved"] / m, 4)
 
 
+def hbm_kernels(kernels, steps, ms, key, min_share=0.005):
+    """The HBM-bound kernels of the profiled pass (below the ridge point) with
+    at least `min_share` of the step: algorithmic bytes per launch over the
+    average launch, against 8 TB/s, and (while the committed counter summary
+    matches the sources) the same with the bytes rocprofv3 counted."""
+    rows = []
+    for k in sorted(kernels, key=lambda k: -k["ms"]):
+        if k["bytes"] <= 0 or bound_of(k) != "hbm" or k["ms"] / steps < min_share * ms:
+            continue
+        avg_s = k["ms"] / k["calls"] / 1e3
+        gbs = k["bytes"] / k["calls"] / avg_s / 1e9
+        row = {"kernel": k["name"], "ms_per_step": round(k["ms"] / steps, 4),
+               "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        counted = _counter_record(key, "hbm_traffic", k["name"], "hbm_bytes_per_launch")
+        row["counter_gbs"] = None if counted is None else round(counted / avg_s / 1e9, 1)
+        rows.append(row)
+    return rows
+
+
 def log_kernels(kernels, steps, n=8):
     for k in sorted(kernels, key=lambda k: -k["ms"])[:n]:
         rate = (f"{k['flops'] / (k['ms'] / 1e3) / 1e12:7.1f} TFLOP/s" if bound_of(k) == "mfma" else
@@ -389,18 +408,21 @@ def mlp_main(args):
 
 
 def timed_steps(step, stream, warmup, steps):
-    """Warm-up, then `steps` steps between HIP events on `stream`: ms/step."""
+    """Warm-up, then `steps` steps with a HIP event on `stream` after each
+    (the first and last bracket them all): ms/step over the whole run, and
+    the sorted per-step times."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps, per_step
 
 
 def profiled(ctx, step, steps):
@@ -449,7 +471,7 @@ def block_main(args):
         tt.tt_block_bwd(ctx, saved, w, dy, dx, g)
 
     K = max(args.steps, 50)
-    ms = timed_steps(step, stream, args.warmup, K)
+    ms, per_step = timed_steps(step, stream, args.warmup, K)
     kernels = profiled(ctx, step, K)
     flops = step_flops(L=1, C=C, V=0, T=T, B=B, F=F)
     tflops = flops / (ms / 1e3) / 1e12
@@ -458,8 +480,9 @@ def block_main(args):
     out = {
         "metric": "single GPT-2 block fwd+bwd time, fp32 (B=4, T=256, d=768, 12 heads, MLP 3072)",
         "value": round(ms * 1e3, 2), "unit": "us/step", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "ms_median": round(per_step[K // 2], 5), "ms_min": round(per_step[0], 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,1) input and upstream gradient, N(0,0.02) weights)",
         "config": {"workload": "single GPT-2 block fwd+bwd, fp32, B=4 T=256 C=768 NH=12 F=3072",
                    "tokens": B * T, "parallelism": "single GPU"},
@@ -467,6 +490,7 @@ def block_main(args):
         "roofline": roofline(kernels, K, ms, peak_mfma=PEAK_FP32_TFLOPS),
     }
     counter_fields(out["roofline"], "block-fp32_b4_t256")
+    out["hbm_kernels"] = hbm_kernels(kernels, K, ms, "block-fp32_b4_t256")
     log_kernels(kernels, K)
     if not args.no_cpu_baseline:
         from oracle import gpt2 as og  # test infrastructure: the baseline leg only
@@ -511,7 +535,7 @@ def lmhead_main(args):
         tt.tt_lmhead_ce_fwdbwd(ctx, "bf16", N, C, V, h, wte, tgt, loss, dh, dwte)
 
     K = args.steps
-    ms = timed_steps(step, stream, args.warmup, K)
+    ms, per_step = timed_steps(step, stream, args.warmup, K)
     kernels = profiled(ctx, step, K)
     flops = 3 * 2.0 * N * C * V
     tflops = flops / (ms / 1e3) / 1e12
@@ -521,8 +545,9 @@ def lmhead_main(args):
         "metric": "fused LM head + cross-entropy fwd+bwd tokens/sec (hidden [8192,768] x "
                   "W_emb [50257,768], bf16, fp32 accumulation)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "ms_median": round(per_step[K // 2], 5), "ms_min": round(per_step[0], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) hidden, N(0,0.02) W_emb, uniform targets)",
         "config": {"workload": "LM head + CE fwd+bwd, N=8192 C=768 V=50257, bf16 / fp32 acc",
                    "tokens": N, "parallelism": "single GPU"},
@@ -531,6 +556,7 @@ def lmhead_main(args):
         "roofline": roofline(kernels, K, ms),
     }
     counter_fields(out["roofline"], "lmhead-ce_n8192_v50257")
+    out["hbm_kernels"] = hbm_kernels(kernels, K, ms, "lmhead-ce_n8192_v50257")
     add_measured(out["roofline"], measured_peaks(ctx))
     log_kernels(kernels, K)
     if not args.no_cpu_baseline:
@@ -656,18 +682,21 @@ def main():
         t += 1
     ctx.sync()
     log(f"[bench] timing {args.steps} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step: the first and last bracket the K steps, the
+    # ones between give each step's own time (median, min)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step(t)
         t += 1
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ctx.sync()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     last_loss = float(loss.item())
     if not math.isfinite(last_loss) or int(flag.item()) != 0:
         log(f"[bench] WARNING: non-finite loss {last_loss} or a dropped (overflowed) step")
@@ -697,6 +726,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(per_step[len(per_step) // 2], 4),
+        "ms_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -712,8 +743,9 @@ def main():
         "loss": round(last_loss, 5),
     }
     out["roofline"] = roofline(kernels, args.steps, ms)
-    counter_fields(out["roofline"], f"{args.workload}_b{B}_t{T}" + ("" if args.dtype == "bf16"
-                                                                   else "_" + args.dtype))
+    ckey = f"{args.workload}_b{B}_t{T}" + ("" if args.dtype == "bf16" else "_" + args.dtype)
+    counter_fields(out["roofline"], ckey)
+    out["hbm_kernels"] = hbm_kernels(kernels, args.steps, ms, ckey)
     # the live probes, after the timed and profiled passes
     add_measured(out["roofline"], measured_peaks(ctx))
     log_kernels(kernels, args.steps)
