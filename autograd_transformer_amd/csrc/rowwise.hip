@@ -27,13 +27,15 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(int N, int C, float 
   const float4 *xr = (const float4 *)(x + (size_t)row * C);
   float4 v[LN_MAXV];
   float s = 0.f;
+  // every load of the row is issued before the first use (a lane past the
+  // row end reads the row's last vector and contributes zero): one memory
+  // round trip, where a load under a branch would wait for each in turn
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) v[i] = xr[min(lane + i * 64, nv - 1)];
 #pragma unroll
   for (int i = 0; i < LN_MAXV; ++i) {
-    int c = lane + i * 64;
-    if (c < nv) {
-      v[i] = xr[c];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
+    if (lane + i * 64 >= nv) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   const float mean = wave_sum(s) / (float)C;
   float q = 0.f;

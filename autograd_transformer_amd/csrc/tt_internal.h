@@ -170,16 +170,43 @@ template <> struct Elem<f16_t> {
   __device__ __forceinline__ static void store(f16_t *p, size_t i, float v) { p[i] = (f16_t)v; }
 };
 
-// Wave64 reductions (butterfly over all 64 lanes).
+// Wave64 reductions, every lane receiving the result.  Inside each 16-lane
+// row the partners are exchanged with DPP (quad permutations xor 1 and xor
+// 2, then the half-row and row mirrors, which pair the already-reduced
+// quads and half-rows); across rows with gfx950's row swaps
+// (v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap the two
+// halves).  All of it stays in the VALU: no round trip through the LDS
+// crossbar, which a shuffle takes.  Each step adds a value to its partner's
+// in both lanes of a pair, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float2 rowswap16_f(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 rowswap32_f(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f<0x141>(v);   // row_half_mirror: quad 0 <-> quad 1 of each 8 lanes
+  v += dpp_f<0x140>(v);   // row_mirror: half-rows of each 16 lanes
+  float2 r = rowswap16_f(v);
+  r = rowswap32_f(r.x + r.y);
+  return r.x + r.y;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  float2 r = rowswap16_f(v);
+  r = rowswap32_f(fmaxf(r.x, r.y));
+  return fmaxf(r.x, r.y);
 }
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi)(x + 0.044715 x^3).
