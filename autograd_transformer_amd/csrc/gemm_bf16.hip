@@ -452,6 +452,18 @@ struct Cfg3 {
   static constexpr int WAVES_PER_EU = (NW * WG_PER_CU + 3) / 4;
 };
 
+// A workgroup barrier for LDS reuse only: every wave's LDS accesses have
+// completed (lgkmcnt(0)) before any wave passes.  Unlike __syncthreads() it
+// does not wait for the wave's outstanding global stores -- between the
+// epilogue's passes that wait costs a full store round trip per pass -- and
+// the stores need no ordering among themselves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Epilogue shared by the direct-to-LDS kernels: the C tile goes through LDS
 // one wave-row at a time (fp32), then every thread applies bias / activation /
 // residual to 4 consecutive columns with row-coalesced accesses; optional
@@ -476,7 +488,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
     float csum = 0.f;
 #pragma unroll
     for (int pass = 0; pass < WM; ++pass) {
-      if (pass > 0) __syncthreads();
+      if (pass > 0) lds_barrier();
       if (wm == pass) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -486,7 +498,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
             for (int r = 0; r < 4; ++r)
               Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
       }
-      __syncthreads();
+      lds_barrier();
       if (p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out) {
         // The GELU-backward product: every pre-activation load of this
         // thread's items is issued first, then the items are finished --
@@ -535,7 +547,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
           if (p.colsum) *cp = st;
         }
         if (p.colsum) {
-          __syncthreads();
+          lds_barrier();
           if (tid < BN)
             for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
         }
@@ -560,7 +572,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
         if (p.colsum) *cp = st;
       }
       if (p.colsum) {
-        __syncthreads();
+        lds_barrier();
         if (tid < BN)
           for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
       }
@@ -582,10 +594,15 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
       if (n + 2 < nv) bias.z = p.bias[n + 2];
     }
   }
+  // The bias has landed before the row loop starts.  Without this wait the
+  // compiler cannot tell, inside the loop, whether the bias load is still in
+  // flight, and waits for every outstanding memory operation -- the stores
+  // of all earlier rows included -- before each row.
+  wait_vm<0>();
   float4 csum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int pass = 0; pass < WM; ++pass) {
-    if (pass > 0) __syncthreads();
+    if (pass > 0) lds_barrier();
     if (wm == pass) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -595,7 +612,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
           for (int r = 0; r < 4; ++r)
             Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
     }
-    __syncthreads();
+    lds_barrier();
     for (int rr = tid / TPR; rr < C::WTM; rr += RPP) {
       const int m = m0 + pass * C::WTM + rr;
       if (m >= p.M || n >= nv) continue;
@@ -608,10 +625,10 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
   // Column sums of the stored tile (bias gradients): combine the RPP row
   // groups in LDS, then one atomic per column and workgroup.
   if (p.colsum) {
-    __syncthreads();
+    lds_barrier();
     float *red = (float *)smem_raw;   // [RPP][BN]
     *(float4 *)&red[(tid / TPR) * BN + cc] = csum;
-    __syncthreads();
+    lds_barrier();
     for (int c = tid; c < BN; c += NT) {
       float t = 0.f;
 #pragma unroll
@@ -1082,7 +1099,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
     if (p.colsum) *cp = st;
   }
   if (p.colsum) {
-    __syncthreads();
+    lds_barrier();
     if (tid < BN && n0 + tid < nv) {
       float csum = 0.f;
       for (int rr = 0; rr < BM; ++rr) csum += Cs[rr * C::LDC + tid];
