@@ -465,10 +465,13 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Epilogue shared by the direct-to-LDS kernels: the C tile goes through LDS
-// one wave-row at a time (fp32), then every thread applies bias / activation /
+// one wave-row at a time (fp32), then every thread applies the activation /
 // residual to 4 consecutive columns with row-coalesced accesses; optional
-// column sums of the stored values (bias gradients).  The caller has passed
-// a barrier after the last LDS read of the main loop.
+// column sums of the stored values (bias gradients).  The bias is already in
+// the accumulators (the kernels start them from it), so the row loops issue
+// no loads of their own but the residual / pre-activation ones: a load in the
+// loop would make every row wait for the stores of the rows before it.  The
+// caller has passed a barrier after the last LDS read of the main loop.
 template <class C, bool F16>
 __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM][C::FN], char *smem_raw,
                                             int m0, int n0) {
@@ -525,13 +528,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
             if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
             continue;
           }
-          float4 v = *cp;
-          if (p.bias && blockIdx.z == 0) {
-            v.x += p.bias[n];
-            if (n + 1 < nv) v.y += p.bias[n + 1];
-            if (n + 2 < nv) v.z += p.bias[n + 2];
-            if (n + 3 < nv) v.w += p.bias[n + 3];
-          }
+          const float4 v = *cp;
           float4 st;
           if (n + 3 < nv) {
             const float h[4] = {lp_lo<F16>(hv[it].x), lp_hi<F16>(hv[it].x), lp_lo<F16>(hv[it].y),
@@ -561,14 +558,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
           if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
           continue;
         }
-        float4 v = *cp;
-        if (p.bias && blockIdx.z == 0) {
-          v.x += p.bias[n];
-          if (n + 1 < nv) v.y += p.bias[n + 1];
-          if (n + 2 < nv) v.z += p.bias[n + 2];
-          if (n + 3 < nv) v.w += p.bias[n + 3];
-        }
-        const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
+        const float4 st = epilogue4<F16>(p, m, n, *cp, nv - n);
         if (p.colsum) *cp = st;
       }
       if (p.colsum) {
@@ -584,21 +574,6 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
   const int cc = (tid % TPR) * 4;
   const int n = n0 + cc;
   const int nv = p.n_valid;
-  float4 bias = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (p.bias && blockIdx.z == 0) {
-    if (n + 3 < nv) {
-      bias = *(const float4 *)(p.bias + n);
-    } else {
-      if (n < nv) bias.x = p.bias[n];
-      if (n + 1 < nv) bias.y = p.bias[n + 1];
-      if (n + 2 < nv) bias.z = p.bias[n + 2];
-    }
-  }
-  // The bias has landed before the row loop starts.  Without this wait the
-  // compiler cannot tell, inside the loop, whether the bias load is still in
-  // flight, and waits for every outstanding memory operation -- the stores
-  // of all earlier rows included -- before each row.
-  wait_vm<0>();
   float4 csum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int pass = 0; pass < WM; ++pass) {
@@ -616,9 +591,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
     for (int rr = tid / TPR; rr < C::WTM; rr += RPP) {
       const int m = m0 + pass * C::WTM + rr;
       if (m >= p.M || n >= nv) continue;
-      float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
-      v.x += bias.x; v.y += bias.y; v.z += bias.z; v.w += bias.w;
-      const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
+      const float4 st = epilogue4<F16>(p, m, n, *(const float4 *)(Cs + rr * C::LDC + cc), nv - n);
       csum.x += st.x; csum.y += st.y; csum.z += st.z; csum.w += st.w;
     }
   }
@@ -683,11 +656,20 @@ gemm_bf16_v3_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
 
+  // The bias starts the accumulators (lane columns wn WTN + 16 j + lane % 16;
+  // only the first k split carries it).  Its loads go out ahead of the
+  // operand prologue and land under it.
+  float bcol[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn * C::WTN + j * 16 + lr;
+    bcol[j] = !GROUP && p.bias && blockIdx.z == 0 && n < p.n_valid ? p.bias[n] : 0.f;
+  }
   f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{bcol[j], bcol[j], bcol[j], bcol[j]};
 
   auto At = [&](int s) { return smem + s * C::STAGE; };
   auto Bt = [&](int s) { return smem + s * C::STAGE + OA::ELEMS; };
@@ -949,11 +931,19 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
 
+  // The bias starts group 0's accumulators (lane columns wj WTN + 16 j +
+  // lane % 16); the two partial tiles are summed once.
+  float bcol[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wj * C::WTN + j * 16 + lr;
+    bcol[j] = p.bias && grp == 0 && n < p.n_valid ? p.bias[n] : 0.f;
+  }
   f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{bcol[j], bcol[j], bcol[j], bcol[j]};
 
   bf16_t *ring = smem + grp * C::RING;
   auto At = [&](int slot) { return ring + slot * C::STAGE; };
@@ -1056,17 +1046,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
       const int rr = idx / TPR, cc = (idx % TPR) * 4;
       const int m = m0 + rr, n = n0 + cc;
       if (m >= p.M || n >= nv) continue;
-      float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
-      if (p.bias) {
-        if (n + 3 < nv) {
-          const float4 b = *(const float4 *)(p.bias + n);
-          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-        } else {
-          v.x += p.bias[n];
-          if (n + 1 < nv) v.y += p.bias[n + 1];
-          if (n + 2 < nv) v.z += p.bias[n + 2];
-        }
-      }
+      const float4 v = *(const float4 *)(Cs + rr * C::LDC + cc);
       if (n + 3 < nv) {
         out_store((float *)p.out + (size_t)m * p.ldo + n,
                   make_float4(rv[it].x + v.x, rv[it].y + v.y, rv[it].z + v.z, rv[it].w + v.w));
@@ -1084,18 +1064,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
       if (p.colsum) *cp = make_float4(0.f, 0.f, 0.f, 0.f);
       continue;
     }
-    float4 v = *cp;
-    if (p.bias) {
-      if (n + 3 < nv) {
-        const float4 b = *(const float4 *)(p.bias + n);
-        v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-      } else {
-        v.x += p.bias[n];
-        if (n + 1 < nv) v.y += p.bias[n + 1];
-        if (n + 2 < nv) v.z += p.bias[n + 2];
-      }
-    }
-    const float4 st = epilogue4<F16>(p, m, n, v, nv - n);
+    const float4 st = epilogue4<F16>(p, m, n, *cp, nv - n);
     if (p.colsum) *cp = st;
   }
   if (p.colsum) {
