@@ -464,6 +464,23 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Sum of column c over the first ROWS rows of a staged tile (row stride LD):
+// four interleaved partial sums, added in a fixed order at the end, so the
+// LDS reads are not one serial add chain.
+template <int ROWS, int LD>
+__device__ __forceinline__ float column_sum(const float *t, int c) {
+  static_assert(ROWS % 4 == 0, "rows in fours");
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 4
+  for (int r = 0; r < ROWS; r += 4) {
+    s0 += t[r * LD + c];
+    s1 += t[(r + 1) * LD + c];
+    s2 += t[(r + 2) * LD + c];
+    s3 += t[(r + 3) * LD + c];
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
 // Epilogue shared by the direct-to-LDS kernels: the C tile goes through LDS
 // one wave-row at a time (fp32), then every thread applies the activation /
 // residual to 4 consecutive columns with row-coalesced accesses; optional
@@ -489,6 +506,26 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
     // thread t < BN adds up column t after each pass.
     const int nv = p.n_valid;
     float csum = 0.f;
+    // The GELU-backward product: every pre-activation load of this thread's
+    // items, over all passes, is issued before the first pass stages its
+    // rows -- one memory round trip for the tile instead of one per pass
+    // (or per item).
+    constexpr int ITEMS = (C::WTM * TPR + NT - 1) / NT;
+    const bool gelu_bwd = p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out;
+    uint2 hv[WM][ITEMS];
+    if (gelu_bwd) {
+#pragma unroll
+      for (int pass = 0; pass < WM; ++pass)
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          const int idx = tid + it * NT;
+          const int rr = idx / TPR, cc = (idx % TPR) * 4;
+          const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
+          hv[pass][it] = make_uint2(0u, 0u);
+          if (idx < C::WTM * TPR && m < p.M && n + 3 < nv)
+            hv[pass][it] = *(const uint2 *)((const bf16_t *)p.aux + (size_t)m * p.ldx + n);
+        }
+    }
 #pragma unroll
     for (int pass = 0; pass < WM; ++pass) {
       if (pass > 0) lds_barrier();
@@ -502,21 +539,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
               Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
       }
       lds_barrier();
-      if (p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out) {
-        // The GELU-backward product: every pre-activation load of this
-        // thread's items is issued first, then the items are finished --
-        // one memory round trip per pass instead of one per item.
-        constexpr int ITEMS = (C::WTM * TPR + NT - 1) / NT;
-        uint2 hv[ITEMS];
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-          const int idx = tid + it * NT;
-          const int rr = idx / TPR, cc = (idx % TPR) * 4;
-          const int m = m0 + pass * C::WTM + rr, n = n0 + cc;
-          hv[it] = make_uint2(0u, 0u);
-          if (idx < C::WTM * TPR && m < p.M && n + 3 < nv)
-            hv[it] = *(const uint2 *)((const bf16_t *)p.aux + (size_t)m * p.ldx + n);
-        }
+      if (gelu_bwd) {
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
           const int idx = tid + it * NT;
@@ -531,8 +554,8 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
           const float4 v = *cp;
           float4 st;
           if (n + 3 < nv) {
-            const float h[4] = {lp_lo<F16>(hv[it].x), lp_hi<F16>(hv[it].x), lp_lo<F16>(hv[it].y),
-                                lp_hi<F16>(hv[it].y)};
+            const uint2 hp = hv[pass][it];
+            const float h[4] = {lp_lo<F16>(hp.x), lp_hi<F16>(hp.x), lp_lo<F16>(hp.y), lp_hi<F16>(hp.y)};
             const float a[4] = {v.x * gelu_grad_f(h[0]), v.y * gelu_grad_f(h[1]),
                                 v.z * gelu_grad_f(h[2]), v.w * gelu_grad_f(h[3])};
             out_store((bf16_t *)p.out + (size_t)m * p.ldo + n,
@@ -545,8 +568,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
         }
         if (p.colsum) {
           lds_barrier();
-          if (tid < BN)
-            for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
+          if (tid < BN) csum += column_sum<C::WTM, C::LDC>(Cs, tid);
         }
         continue;
       }
@@ -563,8 +585,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
       }
       if (p.colsum) {
         lds_barrier();
-        if (tid < BN)
-          for (int rr = 0; rr < C::WTM; ++rr) csum += Cs[rr * C::LDC + tid];
+        if (tid < BN) csum += column_sum<C::WTM, C::LDC>(Cs, tid);
       }
     }
     if (p.colsum && tid < BN && n0 + tid < nv) unsafeAtomicAdd(&p.colsum[n0 + tid], csum);
@@ -1069,11 +1090,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmParams p) {
   }
   if (p.colsum) {
     lds_barrier();
-    if (tid < BN && n0 + tid < nv) {
-      float csum = 0.f;
-      for (int rr = 0; rr < BM; ++rr) csum += Cs[rr * C::LDC + tid];
-      unsafeAtomicAdd(&p.colsum[n0 + tid], csum);
-    }
+    if (tid < BN && n0 + tid < nv)
+      unsafeAtomicAdd(&p.colsum[n0 + tid], column_sum<BM, C::LDC>(Cs, tid));
   }
 }
 
