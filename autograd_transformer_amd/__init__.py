@@ -536,3 +536,33 @@ def tt_probe_hbm(ctx, buf, copy=False):
     nbytes = buf.numel() * buf.element_size()
     ctx.check(lib().tt_probe_hbm(ctx.handle, _ptr(buf), nbytes, 1 if copy else 0, _C.byref(out)))
     return out.value
+
+
+def tt_probe_lds(ctx, mfma=False):
+    """LDS fragment reads per clock per CU (bytes), alone or feeding MFMAs;
+    returns (bytes_per_clk, tflops)."""
+    b, t = _C.c_double(0.0), _C.c_double(0.0)
+    ctx.check(lib().tt_probe_lds(ctx.handle, 1 if mfma else 0, _C.byref(b), _C.byref(t)))
+    return b.value, t.value
+
+
+def tt_probe_lds_load(ctx, buf, resident=True):
+    """Direct-to-LDS global loads per clock per CU (bytes), from L2-resident
+    windows or streaming from HBM, over a device tensor."""
+    out = _C.c_double(0.0)
+    nbytes = buf.numel() * buf.element_size()
+    ctx.check(lib().tt_probe_lds_load(ctx.handle, _ptr(buf), nbytes, 1 if resident else 0,
+                                      _C.byref(out)))
+    return out.value
+
+
+ISSUE_PROBES = ["fma_1wave", "fma_2waves", "exp_1wave", "exp_2waves", "mfma_1wave", "mfma_2waves",
+                "mfma_beside_fma", "mfma_beside_exp"]
+
+
+def tt_probe_issue(ctx, which):
+    """Clocks per instruction of the two waves of a SIMD (see ISSUE_PROBES for
+    `which`); 0 for an idle second wave."""
+    a, b = _C.c_double(0.0), _C.c_double(0.0)
+    ctx.check(lib().tt_probe_issue(ctx.handle, which, _C.byref(a), _C.byref(b)))
+    return a.value, b.value

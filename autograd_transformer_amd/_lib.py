@@ -125,6 +125,9 @@ SIGS = {
     "tt_model_decode": (i32, [vp, vp, vp, i32, i32, vp, vp, vp]),
     "tt_probe_mfma": (i32, [vp, i32, i32, i32, P(C.c_double)]),
     "tt_probe_hbm": (i32, [vp, vp, sz, i32, P(C.c_double)]),
+    "tt_probe_lds": (i32, [vp, i32, P(C.c_double), P(C.c_double)]),
+    "tt_probe_lds_load": (i32, [vp, vp, sz, i32, P(C.c_double)]),
+    "tt_probe_issue": (i32, [vp, i32, P(C.c_double), P(C.c_double)]),
 }
 
 _lib = None

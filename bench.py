@@ -592,10 +592,106 @@ def probe_main(args):
     buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
     res["hbm_read_gbs"] = round(tt.tt_probe_hbm(ctx, buf, copy=False), 1)
     res["hbm_copy_gbs"] = round(tt.tt_probe_hbm(ctx, buf, copy=True), 1)
+    # per-CU ceilings in shader clocks
+    cu = {}
+    cu["lds_read_bytes_per_clk"] = round(tt.tt_probe_lds(ctx, mfma=False)[0], 1)
+    b, t = tt.tt_probe_lds(ctx, mfma=True)
+    cu["lds_read_feeding_mfma_bytes_per_clk"] = round(b, 1)
+    cu["lds_read_feeding_mfma_tflops"] = round(t, 1)
+    src = buf[: (1 << 29) // 4]   # 512 MiB of the probe buffer
+    cu["lds_load_l2_bytes_per_clk"] = round(tt.tt_probe_lds_load(ctx, src, resident=True), 1)
+    cu["lds_load_hbm_bytes_per_clk"] = round(tt.tt_probe_lds_load(ctx, src, resident=False), 1)
+    for i, name in enumerate(tt.ISSUE_PROBES):
+        cu[f"clk_per_instr_{name}"] = [round(v, 2) for v in tt.tt_probe_issue(ctx, i)]
+    res["per_cu"] = cu
     ctx.close()
     print(json.dumps({"probe": "roofline", "peak_vendor": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS,
                                                            "hbm_gbs": PEAK_HBM_GBS},
                       "measured": res}), flush=True)
+
+
+def step_products(L, C, NH, V, V_pad, T, B, F=None):
+    """Every matrix product of one training step as (M, N, K, count, layout):
+    'nt' = A [M,K] times B given as [N,K] (both reduced along their rows:
+    the forward and activation-gradient products), 'tn' = A given as [K,M]
+    times B [K,N] (both token-major: the weight gradients)."""
+    F = F or 4 * C
+    M = B * T
+    per_layer = [(M, 3 * C, C, "nt"), (M, C, C, "nt"), (M, F, C, "nt"), (M, C, F, "nt"),   # forward
+                 (M, F, C, "nt"), (M, C, F, "nt"), (M, C, C, "nt"), (M, C, 3 * C, "nt"),   # dX
+                 (C, 3 * C, M, "tn"), (C, C, M, "tn"), (C, F, M, "tn"), (F, C, M, "tn")]   # dW
+    out = [(m, n, k, L, lay) for m, n, k, lay in per_layer]
+    out += [(M, V_pad, C, 1, "nt"), (M, C, V_pad, 1, "nt"), (V_pad, C, M, 1, "tn")]  # LM head
+    return out
+
+
+def vendor_main(args, w):
+    """The vendor library on the step's products, for scale: hipBLASLt
+    (through torch.matmul; bf16 in and out, no epilogues) on every product of
+    the training step, summed per step, next to this library's GEMM kernels
+    in the same step (the profiled pass's kernels named gemm*, with their
+    fused bias / GELU / residual / column-sum epilogues)."""
+    import torch
+    import autograd_transformer_amd as tt
+    from autograd_transformer_amd import synthetic as syn
+    L, C, NH, V, V_pad, T, B = (w[k] for k in ("L", "C", "NH", "V", "V_pad", "T", "B"))
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    params = syn.gpt2_params(syn.ModelShape(L, C, NH, V, T), seed=3)
+    tok, tgt = syn.gpt2_tokens(B, T, V, seed=3)
+    ctx = tt.Context(arena_bytes=64 << 30 if L > 12 else 24 << 30, stream=stream)
+    model = tt.Model(ctx, L=L, C=C, NH=NH, V=V, T_max=T, B_max=B, mode="bf16", V_pad=V_pad)
+    model.load(params)
+    del params
+    tok_d, tgt_d = torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda()
+    loss = torch.zeros(1, device="cuda")
+    t = 1
+    for _ in range(args.warmup):
+        tt.tt_train_step(ctx, model, B, T, tok_d, tgt_d, 3e-4, 0.9, 0.95, 1e-8, 0.1, t, loss)
+        t += 1
+    ctx.sync()
+    ctx.profile(True)
+    for _ in range(args.steps):
+        tt.tt_train_step(ctx, model, B, T, tok_d, tgt_d, 3e-4, 0.9, 0.95, 1e-8, 0.1, t, loss)
+        t += 1
+    kernels = ctx.profile_report()
+    ctx.profile(False)
+    ctx.sync()
+    ours = sum(k["ms"] for k in kernels if k["name"].startswith("gemm")) / args.steps
+    ours_flops = sum(k["flops"] for k in kernels if k["name"].startswith("gemm")) / args.steps
+    model.close()
+    ctx.close()
+    rows, total = [], 0.0
+    for m, n, k, count, lay in step_products(L, C, NH, V, V_pad, T, B):
+        if lay == "nt":
+            a = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+            b = torch.randn(n, k, device="cuda").to(torch.bfloat16)
+            run = lambda: a @ b.t()
+        else:
+            a = torch.randn(k, m, device="cuda").to(torch.bfloat16)
+            b = torch.randn(k, n, device="cuda").to(torch.bfloat16)
+            run = lambda: a.t() @ b
+        for _ in range(3):
+            run()
+        reps = 20 if m * n * k < 2e10 else 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        total += ms * count
+        rows.append({"M": m, "N": n, "K": k, "per_step": count, "layout": lay,
+                     "us": round(ms * 1e3, 1), "tflops": round(2.0 * m * n * k / ms / 1e9, 1)})
+        del a, b
+    print(json.dumps({"comparison": "vendor GEMM library on the step's products",
+                      "workload": f"{args.workload} B={B} T={T}",
+                      "ours_gemm_ms_per_step": round(ours, 3),
+                      "ours_gemm_tflops": round(ours_flops / ours / 1e9, 1),
+                      "vendor_gemm_ms_per_step": round(total, 3),
+                      "vendor_gemm_tflops": round(ours_flops / total / 1e9, 1),
+                      "products": rows}), flush=True)
 
 
 def main():
@@ -614,6 +710,9 @@ def main():
                     help="measure the tiny classifier's step through the graph autograd")
     ap.add_argument("--probe", action="store_true",
                     help="only run the roofline probes (MFMA and HBM) and exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor GEMM library (torch.matmul) on the step's products "
+                         "next to this library's GEMM kernels, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -651,6 +750,9 @@ def main():
         lmhead_main(args)
         return
     w = WORKLOADS[args.workload]
+    if args.vendor_gemm:
+        vendor_main(args, w)
+        return
     if args.decode:
         decode_main(args, w)
         return

@@ -525,6 +525,25 @@ int tt_probe_mfma(tt_ctx *ctx, int waves_per_simd, int accumulators, int iters, 
  * its first half is copied over its second half).  Five passes after one
  * warm-up; *gbs [host] receives bytes read (+ written) per second / 1e9. */
 int tt_probe_hbm(tt_ctx *ctx, void *buf, size_t bytes, int copy, double *gbs);
+/* Per-CU ceilings, counted in shader clocks (clock64() around each wave's
+ * loop: independent of the clock the part runs at).  One workgroup of 8
+ * waves per CU (two per SIMD).
+ * tt_probe_lds: each wave reads 8 lane-linear 1 KB fragments per round from
+ * LDS (ds_read_b128) and, with mfma != 0, issues the 16 MFMAs of a 64 x 64
+ * tile on them.  *bytes_per_clk [host]: LDS bytes read per clock per CU;
+ * *tflops [host]: the MFMA rate (0 without mfma).
+ * tt_probe_lds_load: 16-byte direct-to-LDS loads (buffer_load ... lds), 16 in
+ * flight per wave, from a caller's device buffer (64 MiB .. 2 GiB, 16-byte
+ * aligned, read only): resident != 0 streams a 64 KB window per workgroup
+ * (L2 hits), else 4 MB windows (HBM).  *bytes_per_clk [host]: per CU.
+ * tt_probe_issue: 8 independent chains per wave; the first wave of each
+ * SIMD runs v_fma_f32 (which = 0, 1), v_exp_f32 (2, 3) or
+ * v_mfma_f32_16x16x32_bf16 (4 .. 7); the second wave is idle (0, 2, 4), runs
+ * the same (1, 3, 5), FMA (6) or exp (7).  *first, *second [host]: clocks
+ * per instruction of each (0 for an idle one). */
+int tt_probe_lds(tt_ctx *ctx, int mfma, double *bytes_per_clk, double *tflops);
+int tt_probe_lds_load(tt_ctx *ctx, void *buf, size_t bytes, int resident, double *bytes_per_clk);
+int tt_probe_issue(tt_ctx *ctx, int which, double *first, double *second);
 
 #ifdef __cplusplus
 }

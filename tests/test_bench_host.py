@@ -103,3 +103,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", ["gpt2-124m", "gpt2-350m"])
+def test_step_products_cover_the_step_flops(name):
+    """The vendor comparison's product list holds every GEMM of the step: its
+    FLOPs are the step's algorithmic FLOPs (at the padded vocabulary the
+    kernels run) less the two attention products per pass."""
+    w = bench.WORKLOADS[name]
+    prods = bench.step_products(**{k: w[k] for k in ("L", "C", "NH", "V", "V_pad", "T", "B")})
+    gemm = sum(2.0 * m * n * k * c for m, n, k, c, _ in prods)
+    attn = 3.0 * w["L"] * 2.0 * w["B"] * w["C"] * w["T"] * (w["T"] + 1)
+    full = bench.step_flops(**dict(w, V=w["V_pad"]))
+    assert gemm == pytest.approx(full - attn, rel=1e-12)
+    # 12 products per layer and three for the tied LM head
+    assert sum(p[3] for p in prods) == 12 * w["L"] + 3
