@@ -321,13 +321,16 @@ struct DOp {
   __device__ __forceinline__ static int swz_k(int r) { return (r >> 1) % CPR; }
   __device__ __forceinline__ static int rswz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
-  // Issue this wave's share of the tile's loads (chunk instructions w, w+NW, ...).
+  // Issue this wave's share of the tile's loads (chunk instructions w, w+NW,
+  // ...).  When the chunks do not divide evenly, the first CHUNKS % NW waves
+  // issue one more (the count stays uniform within a wave).
   template <int NW>
   __device__ __forceinline__ static void issue(bf16_t *tile, __amdgpu_buffer_rsrc_t rs, int ld,
                                                int r0, int k0, int R, int K, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < CHUNKS / NW; ++i) {
+    for (int i = 0; i < (CHUNKS + NW - 1) / NW; ++i) {
       const int ci = wave + i * NW;
+      if (CHUNKS % NW != 0 && ci >= CHUNKS) break;
       const int L = ci * 64 + lane;            // linear 16-byte slot in the tile
       uint32_t off;
       if constexpr (KM) {
@@ -439,12 +442,14 @@ struct Cfg3 {
   using OA = DOp<BM, BKV, A_KM>;
   using OB = DOp<BN, BKV, B_KM>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;
-  static constexpr int LPS = OA::CHUNKS / NW + OB::CHUNKS / NW;   // loads per stage per wave
+  // Loads per stage of the wave with the fewest (waves may differ by one per
+  // operand): the vmcnt waits count with it, which for the other waves waits
+  // for at most one load of a later stage besides the stage needed.
+  static constexpr int LPS = OA::CHUNKS / NW + OB::CHUNKS / NW;
   static constexpr int OPER_BYTES = NS * STAGE * 2;
   static constexpr int LDC = BN + 4;
   static constexpr int EPI_BYTES = WTM * LDC * 4;
   static constexpr int SMEM = OPER_BYTES > EPI_BYTES ? OPER_BYTES : EPI_BYTES;
-  static_assert(OA::CHUNKS % NW == 0 && OB::CHUNKS % NW == 0, "loads not divisible by waves");
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert((NS - 2) * LPS < 64, "vmcnt range");
   // workgroups per CU that the LDS allows (at most 2), as waves per SIMD
@@ -510,10 +515,13 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
     // items, over all passes, is issued before the first pass stages its
     // rows -- one memory round trip for the tile instead of one per pass
     // (or per item).
+    // (Only for wave tiles of at most 16 MFMA blocks: beside larger
+    // accumulator sets the prefetch array would not fit the registers.)
     constexpr int ITEMS = (C::WTM * TPR + NT - 1) / NT;
-    const bool gelu_bwd = p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out;
-    uint2 hv[WM][ITEMS];
-    if (gelu_bwd) {
+    constexpr bool GB_PREFETCH = FM * FN <= 16;
+    const bool gelu_bwd = GB_PREFETCH && p.epi == EPI_GELU_BWD && p.out_bf16 && p.vec_out;
+    uint2 hv[GB_PREFETCH ? WM : 1][GB_PREFETCH ? ITEMS : 1];
+    if constexpr (GB_PREFETCH) if (gelu_bwd) {
 #pragma unroll
       for (int pass = 0; pass < WM; ++pass)
 #pragma unroll
@@ -539,7 +547,7 @@ __device__ __forceinline__ void v3_epilogue(GemmParams &p, f32x4_t (&acc)[C::FM]
               Cs[(i * 16 + lg * 4 + r) * C::LDC + wn * C::WTN + j * 16 + lr] = acc[i][j][r];
       }
       lds_barrier();
-      if (gelu_bwd) {
+      if constexpr (GB_PREFETCH) if (gelu_bwd) {
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
           const int idx = tid + it * NT;
@@ -1285,6 +1293,12 @@ int tt_gemm_bf16(tt_ctx *ctx, const GemmArgs &g) {
     // the narrow products (N = 768: projections, down-projection, every dX
     // but the GELU-backward one, the LM-head dH): ping-pong tile
     if (g.N < 1536 && g.M > 128) return launch_pp<192, 2, 64>(ctx, g);
+    // Products whose 256 x 128 grid leaves a short second round (the qkv
+    // forward: 576 tiles on 512 slots, the last 64 running alone) take
+    // 256 x 288 tiles when those fill the GPU in exactly one round (one
+    // workgroup per CU): 48 against 54 us at M = 8192, N = 2304, K = 768.
+    if (g.K <= 1024 && g.M % 256 == 0 && g.N % 288 == 0 && (long)(g.M / 256) * (g.N / 288) == 256)
+      return launch3<256, 288, 32, 4, 2, 3>(ctx, g, 1);
     if (g.K >= 8192) return launch3<128, 192, 64, 2, 4, 3>(ctx, g, 1);
     if (tiles >= 512) {
       if (g.epi == EPI_GELU_BWD) return launch3<128, 192, 64, 2, 4, 2>(ctx, g, 1);
