@@ -1260,6 +1260,9 @@ bool tt_gemm_bf16_ok(const GemmArgs &g) {
 //      N < 1536 (the N = 768 products), M > 128: the ping-pong kernel,
 //        128 x 192, two 64-deep stages per group (gemm_pp_kernel)
 //    and otherwise:
+//      K <= 1024, exactly 256 tiles of 256 x 288 (the qkv forward at 8192
+//      tokens)                                  256 x 288, BK 32, 3 stages
+//                                               (one workgroup per CU)
 //      K >= 8192 (LM-head dH)                   128 x 192, BK 64, 3 stages
 //      >= 512 tiles of 256 x 128:  GELU-backward epilogue -> 128 x 192, BK 64,
 //                                  2 stages; others -> 256 x 128, BK 32, 3
